@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA decode on one MI355X.
+
+Workload (default): batch 64, 128 query heads, q_len 1, every sequence 4096 cached
+tokens, 576-wide bf16 latent rows (512 latent + 64 rope) in 64-token pages, block
+table a seeded page permutation, scale 192^-0.5; seeded N(0, 1) synthetic inputs.
+
+One step = the whole decode path on one batch: the split planner (mla_get_metadata),
+the split-KV decode kernel and the log-sum-exp combine.  Inputs are resident in HBM
+before timing starts.  Two KV pools with identical contents are alternated step by
+step, so no step can be served from the 256 MB memory-side cache left warm by the
+step before it.
+
+Prints one JSON line: throughput in TFLOP/s (algorithmic FLOPs: 2*(576+512) per
+visible key per query row), KV GB/s, roofline fractions, the decode kernel's own
+duration from HIP events, and the CPU oracle's rate on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+METRIC = "MLA decode TFLOP/s + KV GB/s (% roofline), 128 heads, B=64, seqlen 4096"
+DECODE_KERNEL = "mla_decode_bf16_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_h128_l4096_traffic.json")
+KERNEL_SOURCES = ["mla_decode_03_amd/csrc/mla_decode_bf16.hip", "mla_decode_03_amd/csrc/mla_device.h",
+                  "mla_decode_03_amd/csrc/mla_args.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_sizes(case):
+    """Algorithmic FLOPs and bytes of one decode of `case` (each visible key once)."""
+    import numpy as np
+    T, H = case.q_len, case.num_heads
+    flops = 0
+    for L in case.cache_seqlens.tolist():
+        for t in range(T):
+            n = (L - T + 1 + t) if (case.causal and T > 1) else L
+            flops += max(n, 0) * H * 2 * (576 + 512)
+    elem = 2 if case.dtype == "bf16" else 4
+    kv_bytes = int(np.sum(np.maximum(case.cache_seqlens, 0))) * 576 * elem
+    rows = case.batch * T * H
+    other = rows * 576 * elem + rows * 512 * elem + rows * 4 + case.block_table.size * 4 + case.batch * 4
+    return flops, kv_bytes, kv_bytes + other
+
+
+def traffic_from_profile():
+    """HBM bytes per decode launch from the committed counter profile, if it was taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, flops):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.decode_case(case)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "the whole workload once: all %d query rows x %d keys, float64 two-pass "
+                      "softmax on the host" % (case.batch * case.q_len * case.num_heads,
+                                               int(case.cache_seqlens.max()))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default: the headline one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--min-blocks", type=int, default=0)
+    ap.add_argument("--row-split", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode runs on a single MI355X and this build "
+              "has no multi-GPU path (asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mla_decode_03_amd as mla
+    from mla_inputs import CONFIGS, make_config
+
+    mla.lib()
+    dev = torch.device("cuda:0")
+    case = make_config(args.config)
+    flops, kv_bytes, total_bytes = workload_sizes(case)
+
+    if case.dtype == "bf16":
+        q = torch.from_numpy(case.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        kv_a = torch.from_numpy(case.kv_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(case.q).to(dev)
+        kv_a = torch.from_numpy(case.kv).to(dev)
+    kv_b = kv_a.clone()
+    bt = torch.from_numpy(case.block_table).to(dev)
+    lens = torch.from_numpy(case.cache_seqlens).to(dev)
+    B, T, H = case.batch, case.q_len, case.num_heads
+    out = torch.empty((B, T, H, 512), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    opts = None
+    if args.num_workgroups or args.min_blocks or args.row_split:
+        opts = mla.PlanOptions(num_workgroups=args.num_workgroups, min_blocks_per_wg=args.min_blocks,
+                               row_split=args.row_split)
+    split = case.dtype == "bf16"
+    dec = mla.Decoder(q, kv_a, bt, causal=case.causal, split=split, options=opts)
+    pools = (kv_a, kv_b)
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        kv = pools[i & 1]
+        if not split:
+            mla.decode(dec.problem, q, kv, bt, lens, case.scale, out, lse, None, None, stream)
+            return
+        plan = dec.plan_for(lens, stream)
+        if events is not None:
+            events[0].record(stream)
+        mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace, stream)
+        if events is not None:
+            events[1].record(stream)
+        mla.combine(dec.problem, out, lse, plan, dec.workspace, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` whole-path steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / args.steps
+
+    # the decode kernel alone, with HIP events on the stream it is launched on
+    kernel_ms = None
+    if split:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    t = ms_per_step * 1e-3
+    tflops = flops / t / 1e12
+    kv_gbs = kv_bytes / t / 1e9
+    frac_hbm = (total_bytes / t / 1e9) / HBM_PEAK_GBS
+    frac_mfma = tflops / MFMA_BF16_PEAK_TFLOPS
+
+    roofline = None
+    if kernel_ms is not None:
+        achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
+                    "kernel": DECODE_KERNEL, "kernel_ms": round(kernel_ms, 5),
+                    "algorithmic_bytes_per_launch": total_bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, flops)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[args.config]["name"], "batch": B, "heads": H, "q_len": T,
+                   "seqlen": int(case.cache_seqlens.max()), "page": 64, "d_qk": 576, "d_v": 512,
+                   "causal": case.causal, "kv_pools_alternated": 2,
+                   "plan": {"num_workgroups": dec.plan.grid_wg if dec.plan else None}},
+        "kv_gb_per_s": round(kv_gbs, 1),
+        "frac_hbm_total_bytes": round(frac_hbm, 4),
+        "frac_mfma_bf16": round(frac_mfma, 4),
+        "frac_roofline": round(max(frac_hbm, frac_mfma), 4),
+        "algorithmic": {"flop": flops, "kv_bytes": kv_bytes, "total_bytes": total_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * mla.h -- C ABI of libmla.so: MLA (multi-head latent attention) decoding over a
+ * paged latent KV cache on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The TileLang notes ("TileLang: bridging programmability and
+ * performance in modern neural kernels", section "A complete example: two-stage
+ * optimisation of FlashMLA") present MLA decoding as two chained GEMMs with a
+ * softmax between them: S = Q . KV^T kept in registers, down-cast, then
+ * O += S_cast . KV.  The pages do not write out the rest; this library fixes it
+ * as follows (the plainest reading, and the one the tests hold it to):
+ *
+ *   For sequence b, query position t < q_len and head h (row r = t*H + h):
+ *     L      = cache_seqlens[b]   (counts every cached token, the q_len new ones included)
+ *     n      = L                          if !causal or q_len == 1
+ *            = max(0, L - q_len + 1 + t)  if causal  (query t sees positions p <= L - q_len + t)
+ *     k_p    = kv_cache[block_table[b][p / 64]][p % 64][0:576]   for p < n
+ *     s_p    = scale * dot(q[b][t][h][0:576], k_p)
+ *     lse    = ln(sum_p exp(s_p))                                 (natural log)
+ *     out[d] = sum_p exp(s_p - lse) * k_p[d]        for d < 512   (V = first 512 dims)
+ *   A row with n == 0 gets out = 0 and lse = -inf.
+ *
+ * Sizes fixed by the library: 576-wide cache rows (512 latent + 64 rope), 512-wide
+ * values, 64-token pages.  q_len * num_heads (rows per sequence) must be <= 128.
+ *
+ * Layouts (all C-contiguous, row-major):
+ *   q            [batch, q_len, num_heads, 576]     dtype
+ *   kv_cache     [num_pages, 64, 576]               dtype
+ *   block_table  [batch, block_table_stride] int32; only the first ceil(L/64)
+ *                entries of row b are read
+ *   cache_seqlens[batch] int32
+ *   out          [batch, q_len, num_heads, 512]     dtype (bf16 out is rounded
+ *                to nearest even from the fp32 result)
+ *   lse          [batch, q_len, num_heads] float32
+ *
+ * Memory.  Every pointer argument except `problem`, `options`, `plan` and `num_cus` is
+ * DEVICE memory; the caller owns every buffer (the library allocates nothing and
+ * keeps no per-call state).  Device pointers must be 16-byte aligned (int32 arrays:
+ * 4-byte).  `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Asynchrony.  mla_get_metadata and mla_decode only enqueue work on `stream`;
+ * they never synchronise it, never copy to the host and never allocate, so they
+ * can be captured in a HIP graph.  A plan (metadata) is valid only for the
+ * cache_seqlens contents it was computed from and the problem it was made for.
+ *
+ * Errors.  Every call returns an mla_status_t.  Argument faults the host can see
+ * are reported before anything is enqueued.  Faults only the device can see
+ * (a block_table entry outside [0, num_pages), or L > 64 * max_blocks_per_seq)
+ * never cause an out-of-bounds access: the affected sequence's out and lse are
+ * written as NaN and a flag is raised in the metadata, which
+ * mla_plan_error() reads back (that call synchronises the stream).
+ * No call throws across the ABI; the library is reentrant and thread-safe.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_PAGE 64
+#define MLA_MAX_ROWS 128
+
+typedef enum {
+  MLA_DTYPE_F32 = 0,
+  MLA_DTYPE_BF16 = 1,
+} mla_dtype_t;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,         /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,        /* a size is out of range */
+  MLA_ERR_DTYPE = 3,        /* unknown dtype */
+  MLA_ERR_ALIGN = 4,        /* a pointer is not aligned as required */
+  MLA_ERR_WORKSPACE = 5,    /* metadata or workspace buffer too small */
+  MLA_ERR_UNSUPPORTED = 6,  /* valid request this build does not serve */
+  MLA_ERR_LAUNCH = 7,       /* the HIP runtime refused a launch */
+  MLA_ERR_DEVICE = 8,       /* device query failed */
+  MLA_ERR_BAD_INPUT = 9,    /* device-side data fault flagged (see mla_plan_error) */
+} mla_status_t;
+
+/* Host-side description of one decode problem. */
+typedef struct {
+  int32_t batch;               /* B >= 0 (0 = nothing to do) */
+  int32_t q_len;               /* T >= 1 new tokens per sequence */
+  int32_t num_heads;           /* H >= 1, with T * H <= 128 */
+  int32_t causal;              /* 0 or 1: mask within the T new tokens (only used when T > 1) */
+  int32_t num_pages;           /* pages in kv_cache (>= 1) */
+  int32_t block_table_stride;  /* int32 elements between block_table rows (>= max_blocks_per_seq) */
+  int32_t max_blocks_per_seq;  /* entries of a block_table row the library may read (>= 1) */
+  int32_t dtype;               /* mla_dtype_t of q, kv_cache and out */
+} mla_problem_t;
+
+/* Optional knobs of the split planner (NULL = defaults).  Zero fields take defaults. */
+typedef struct {
+  int32_t num_workgroups;      /* decode workgroups to spread the work over (default: one per CU) */
+  int32_t min_blocks_per_wg;   /* smallest share of 64-token blocks per workgroup (default 4) */
+  int32_t row_split;           /* split each sequence's rows over this many workgroups: 1, 2 or 4 (default 1) */
+} mla_plan_options_t;
+
+/* Human-readable name of a status code (static string). */
+MLA_API const char* mla_status_string(int32_t status);
+
+/* Compute units of the current HIP device (host call, no GPU work). */
+MLA_API int32_t mla_device_num_cus(int32_t* num_cus);
+
+/*
+ * Size in bytes of the metadata buffer mla_get_metadata needs for `problem`
+ * with `options` (NULL = defaults) on a device with `num_cus` CUs (<= 0: query
+ * the current device).  Host-only arithmetic; returns 0 for an invalid problem.
+ */
+MLA_API size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
+                          int32_t num_cus);
+
+/*
+ * Size in bytes of the workspace mla_decode needs with a plan made for the same
+ * problem/options/num_cus: room for the split partials (per split, every row's
+ * float32 output and log-sum-exp).  Host-only arithmetic.
+ */
+MLA_API size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
+                           int32_t num_cus);
+
+/*
+ * A split plan: the caller-owned device buffer the planner writes, plus the launch
+ * shape the host side needs (filled in by mla_get_metadata on the host, so
+ * mla_decode never reads device memory to launch).
+ */
+typedef struct {
+  void* metadata;              /* device buffer, >= mla_metadata_bytes (caller sets) */
+  size_t metadata_bytes;       /* its size (caller sets) */
+  int32_t grid_wg;             /* decode workgroups to launch (filled) */
+  int32_t row_split;           /* workgroups per sequence's rows (filled) */
+  int32_t rows_per_wg;         /* rows per workgroup (filled) */
+  int32_t max_partials;        /* partial slots the workspace must hold (filled) */
+  int32_t batch;               /* problem the plan was made for (filled) */
+  int32_t rows;                /* q_len * num_heads of that problem (filled) */
+} mla_plan_t;
+
+/*
+ * Plan the split-KV work.  Reads cache_seqlens on the device, writes the plan
+ * into plan->metadata: every sequence's 64-token blocks (times row_split) are
+ * laid end to end and cut into num_workgroups contiguous, equal (+-1 block)
+ * shares, so all CUs stream the same amount of KV; a sequence cut across k > 1
+ * workgroups gets k partial results that mla_decode merges by log-sum-exp.
+ * One single-workgroup kernel launch on `stream`; fills the host fields of *plan.
+ */
+MLA_API int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
+                         const mla_plan_options_t* options, int32_t num_cus,
+                         mla_plan_t* plan, void* stream);
+
+/*
+ * Decode.  Argument order follows the problem statement
+ * (q, kv_cache, block_table, cache_seqlens, scale, out, lse, ..., stream).
+ *   scale      multiplies every q . k (e.g. 192^-0.5)
+ *   plan       from mla_get_metadata for the same problem and cache_seqlens, or
+ *              NULL: one workgroup per sequence, no splits, no workspace needed
+ *   workspace  device buffer of >= mla_workspace_bytes (unused when plan is NULL)
+ * bf16 problems run the MFMA kernel (split-KV decode, then the LSE combine when
+ * the plan splits anything); float32 problems run a plain float32 kernel (plan
+ * ignored).
+ */
+MLA_API int32_t mla_decode(const mla_problem_t* problem,
+                   const void* q, const void* kv_cache,
+                   const int32_t* block_table, const int32_t* cache_seqlens,
+                   float scale, void* out, float* lse,
+                   const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * The two launches of mla_decode, for callers (and benchmarks) that want them apart.
+ * mla_decode_splits: the split-KV decode kernel alone -- writes out/lse of every
+ *   sequence the plan did not split, and the float32 partials (normalised output and
+ *   natural-log LSE per split) of the split ones into `workspace`.
+ * mla_combine: merges those partials by log-sum-exp into out/lse (sequences with no
+ *   cached tokens get out = 0, lse = -inf).  Same plan and workspace as the decode.
+ * Both require a plan and a bf16 problem; mla_decode(plan != NULL) == splits + combine.
+ */
+MLA_API int32_t mla_decode_splits(const mla_problem_t* problem,
+                                  const void* q, const void* kv_cache,
+                                  const int32_t* block_table, const int32_t* cache_seqlens,
+                                  float scale, void* out, float* lse,
+                                  const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+MLA_API int32_t mla_combine(const mla_problem_t* problem, void* out, float* lse,
+                            const mla_plan_t* plan, const void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Read back the device-side error flag of a plan after mla_decode ran with it:
+ * synchronises `stream`, returns MLA_OK or MLA_ERR_BAD_INPUT, and clears the flag.
+ */
+MLA_API int32_t mla_plan_error(const mla_plan_t* plan, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

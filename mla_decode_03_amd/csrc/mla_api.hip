@@ -1,0 +1,306 @@
+// Host side of libmla.so: argument checks, sizing, plan bookkeeping and launches.
+// Validation happens here in C++ before anything is enqueued (the DeepSeek-V4
+// TileLang note, section "Points from the V4 report", on moving launch and tensor
+// checks out of Python into compiled host code).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "mla.h"
+#include "mla_args.h"
+#include "mla_device.h"
+
+namespace {
+
+constexpr int kDefaultMinBlocks = 4;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_problem(const mla_problem_t* p) {
+  if (!p) return MLA_ERR_NULL;
+  if (p->dtype != MLA_DTYPE_F32 && p->dtype != MLA_DTYPE_BF16) return MLA_ERR_DTYPE;
+  if (p->batch < 0 || p->q_len < 1 || p->num_heads < 1) return MLA_ERR_SHAPE;
+  if ((int64_t)p->q_len * p->num_heads > MLA_MAX_ROWS) return MLA_ERR_SHAPE;
+  if (p->causal != 0 && p->causal != 1) return MLA_ERR_SHAPE;
+  if (p->num_pages < 1 || p->max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  if (p->block_table_stride < p->max_blocks_per_seq) return MLA_ERR_SHAPE;
+  // global block positions, page offsets and partial indices stay in int32 range
+  if ((int64_t)p->batch * p->max_blocks_per_seq * 4 > INT32_MAX) return MLA_ERR_SHAPE;
+  if ((int64_t)p->batch * p->block_table_stride > INT32_MAX) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+std::atomic<int32_t> g_cus_cache{0};
+
+int32_t resolve_cus(int32_t num_cus, int32_t* out) {
+  if (num_cus > 0) { *out = num_cus; return MLA_OK; }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MLA_ERR_DEVICE;
+  *out = cus;
+  return MLA_OK;
+}
+
+struct PlanShape {
+  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials;
+};
+
+int32_t plan_shape(const mla_problem_t* p, const mla_plan_options_t* o, int32_t num_cus, PlanShape* s) {
+  int32_t rc = check_problem(p);
+  if (rc != MLA_OK) return rc;
+  int32_t cus = 0;
+  rc = resolve_cus(num_cus, &cus);
+  if (rc != MLA_OK) return rc;
+  const int rows = p->q_len * p->num_heads;
+  int grid = (o && o->num_workgroups > 0) ? o->num_workgroups : cus;
+  int minb = (o && o->min_blocks_per_wg > 0) ? o->min_blocks_per_wg : kDefaultMinBlocks;
+  int rsplit = (o && o->row_split > 0) ? o->row_split : 1;
+  if (rsplit != 1 && rsplit != 2 && rsplit != 4) return MLA_ERR_UNSUPPORTED;
+  if (rows % rsplit != 0) return MLA_ERR_UNSUPPORTED;
+  if (grid > 65536) return MLA_ERR_SHAPE;
+  s->grid_wg = grid;
+  s->row_split = rsplit;
+  s->rows_per_wg = rows / rsplit;
+  s->min_blocks = minb;
+  const int64_t units = (int64_t)p->batch * rsplit;
+  // each workgroup range holds at most one partial segment at each end
+  s->max_partials = (int)(grid + (units < grid ? units : grid));
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "null pointer";
+    case MLA_ERR_SHAPE: return "size out of range";
+    case MLA_ERR_DTYPE: return "unknown dtype";
+    case MLA_ERR_ALIGN: return "misaligned pointer";
+    case MLA_ERR_WORKSPACE: return "metadata or workspace too small";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_DEVICE: return "device query failed";
+    case MLA_ERR_BAD_INPUT: return "device-side input fault (bad block_table entry or sequence length)";
+    default: return "unknown status";
+  }
+}
+
+int32_t mla_device_num_cus(int32_t* num_cus) {
+  if (!num_cus) return MLA_ERR_NULL;
+  int32_t c = g_cus_cache.load(std::memory_order_relaxed);
+  if (c <= 0) {
+    int32_t rc = resolve_cus(0, &c);
+    if (rc != MLA_OK) return rc;
+    g_cus_cache.store(c, std::memory_order_relaxed);
+  }
+  *num_cus = c;
+  return MLA_OK;
+}
+
+size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_options_t* options, int32_t num_cus) {
+  PlanShape s;
+  if (plan_shape(problem, options, num_cus, &s) != MLA_OK) return 0;
+  return mla::meta_words(problem->batch, s.row_split, s.grid_wg) * sizeof(int32_t);
+}
+
+size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options, int32_t num_cus) {
+  PlanShape s;
+  if (plan_shape(problem, options, num_cus, &s) != MLA_OK) return 0;
+  return (size_t)s.max_partials * s.rows_per_wg * (mla::kDv + 1) * sizeof(float);
+}
+
+int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
+                         const mla_plan_options_t* options, int32_t num_cus, mla_plan_t* plan,
+                         void* stream) {
+  if (!problem || !plan) return MLA_ERR_NULL;
+  PlanShape s;
+  int32_t rc = plan_shape(problem, options, num_cus, &s);
+  if (rc != MLA_OK) return rc;
+  if (!plan->metadata || (problem->batch > 0 && !cache_seqlens)) return MLA_ERR_NULL;
+  if (!aligned(plan->metadata, 16) || !aligned(cache_seqlens, 4)) return MLA_ERR_ALIGN;
+  const size_t need = mla::meta_words(problem->batch, s.row_split, s.grid_wg) * sizeof(int32_t);
+  if (plan->metadata_bytes < need) return MLA_ERR_WORKSPACE;
+  plan->grid_wg = s.grid_wg;
+  plan->row_split = s.row_split;
+  plan->rows_per_wg = s.rows_per_wg;
+  plan->max_partials = s.max_partials;
+  plan->batch = problem->batch;
+  plan->rows = problem->q_len * problem->num_heads;
+  if (mla_launch_plan(cache_seqlens, static_cast<int32_t*>(plan->metadata), problem->batch,
+                      plan->rows, s.row_split, s.grid_wg, s.min_blocks, problem->max_blocks_per_seq,
+                      s.max_partials, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+namespace {
+
+// Checks shared by every decode entry; fills the kernel argument block.
+int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                       const int32_t* block_table, const int32_t* cache_seqlens, float scale,
+                       void* out, float* lse, mla::DecodeArgs* a) {
+  int32_t rc = check_problem(problem);
+  if (rc != MLA_OK) return rc;
+  const mla_problem_t& p = *problem;
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !lse) return MLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
+    return MLA_ERR_ALIGN;
+  a->q = static_cast<const uint8_t*>(q);
+  a->kv = static_cast<const uint8_t*>(kv_cache);
+  a->block_table = block_table;
+  a->seqlens = cache_seqlens;
+  a->out = static_cast<uint16_t*>(out);
+  a->lse = lse;
+  a->scale_log2 = scale * mla::kLog2e;
+  a->batch = p.batch;
+  a->rows = p.q_len * p.num_heads;
+  a->q_len = p.q_len;
+  a->heads = p.num_heads;
+  a->causal = p.causal;
+  a->num_pages = p.num_pages;
+  a->bt_stride = p.block_table_stride;
+  a->max_blocks = p.max_blocks_per_seq;
+  a->meta = nullptr;
+  a->ws_o = nullptr;
+  a->ws_lse = nullptr;
+  a->rows_per_wg = a->rows;
+  a->row_split = 1;
+  return MLA_OK;
+}
+
+// Checks a plan and workspace against the problem; sets the plan fields of *a.
+int32_t attach_plan(const mla_problem_t& p, const mla_plan_t* plan, const void* workspace,
+                    size_t workspace_bytes, mla::DecodeArgs* a) {
+  if (!plan || !plan->metadata) return MLA_ERR_NULL;
+  const int rows = p.q_len * p.num_heads;
+  if (plan->batch != p.batch || plan->rows != rows || plan->grid_wg < 1 || plan->row_split < 1 ||
+      plan->rows_per_wg * plan->row_split != rows || plan->max_partials < 0)
+    return MLA_ERR_SHAPE;
+  if (!aligned(plan->metadata, 16)) return MLA_ERR_ALIGN;
+  const size_t ws_need = (size_t)plan->max_partials * plan->rows_per_wg * (mla::kDv + 1) * sizeof(float);
+  if (ws_need > 0 && !workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < ws_need) return MLA_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 16)) return MLA_ERR_ALIGN;
+  a->meta = static_cast<int32_t*>(plan->metadata);
+  a->ws_o = static_cast<float*>(const_cast<void*>(workspace));
+  a->ws_lse = a->ws_o + (size_t)plan->max_partials * plan->rows_per_wg * mla::kDv;
+  a->rows_per_wg = plan->rows_per_wg;
+  a->row_split = plan->row_split;
+  return MLA_OK;
+}
+
+int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
+  mla::CombineArgs c;
+  c.meta = a.meta;
+  c.ws_o = a.ws_o;
+  c.ws_lse = a.ws_lse;
+  c.out = a.out;
+  c.lse = a.lse;
+  c.batch = a.batch;
+  c.rows = a.rows;
+  c.rows_per_wg = a.rows_per_wg;
+  c.row_split = a.row_split;
+  return mla_launch_combine(&c, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int32_t mla_decode(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                   const int32_t* block_table, const int32_t* cache_seqlens, float scale, void* out,
+                   float* lse, const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int32_t rc = check_problem(problem);
+  if (rc != MLA_OK) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (problem->dtype == MLA_DTYPE_F32) {
+    mla::DecodeArgs d;
+    rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &d);
+    if (rc != MLA_OK) return rc;
+    mla::F32Args a;
+    a.q = static_cast<const float*>(q);
+    a.kv = static_cast<const float*>(kv_cache);
+    a.block_table = block_table;
+    a.seqlens = cache_seqlens;
+    a.out = static_cast<float*>(out);
+    a.lse = lse;
+    a.scale = scale;
+    a.batch = d.batch;
+    a.rows = d.rows;
+    a.q_len = d.q_len;
+    a.heads = d.heads;
+    a.causal = d.causal;
+    a.num_pages = d.num_pages;
+    a.bt_stride = d.bt_stride;
+    a.max_blocks = d.max_blocks;
+    return mla_launch_decode_f32(&a, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  }
+  mla::DecodeArgs a;
+  rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &a);
+  if (rc != MLA_OK) return rc;
+  if (!plan) return mla_launch_decode_bf16(&a, problem->batch, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
+  if (rc != MLA_OK) return rc;
+  if (mla_launch_decode_bf16(&a, plan->grid_wg, st) != hipSuccess) return MLA_ERR_LAUNCH;
+  return launch_combine(a, st);
+}
+
+int32_t mla_decode_splits(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                          const int32_t* block_table, const int32_t* cache_seqlens, float scale,
+                          void* out, float* lse, const mla_plan_t* plan, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int32_t rc = check_problem(problem);
+  if (rc != MLA_OK) return rc;
+  if (problem->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (problem->batch == 0) return MLA_OK;
+  mla::DecodeArgs a;
+  rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &a);
+  if (rc != MLA_OK) return rc;
+  rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
+  if (rc != MLA_OK) return rc;
+  return mla_launch_decode_bf16(&a, plan->grid_wg, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int32_t mla_combine(const mla_problem_t* problem, void* out, float* lse, const mla_plan_t* plan,
+                    const void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc = check_problem(problem);
+  if (rc != MLA_OK) return rc;
+  if (problem->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (problem->batch == 0) return MLA_OK;
+  if (!out || !lse) return MLA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_ALIGN;
+  mla::DecodeArgs a{};
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.batch = problem->batch;
+  a.rows = problem->q_len * problem->num_heads;
+  rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
+  if (rc != MLA_OK) return rc;
+  return launch_combine(a, static_cast<hipStream_t>(stream));
+}
+
+int32_t mla_plan_error(const mla_plan_t* plan, void* stream) {
+  if (!plan || !plan->metadata) return MLA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t flag = 0;
+  int32_t* dflag = static_cast<int32_t*>(plan->metadata) + mla::kHdrError;
+  if (hipStreamSynchronize(st) != hipSuccess) return MLA_ERR_DEVICE;
+  if (hipMemcpy(&flag, dflag, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_DEVICE;
+  if (flag) {
+    const int32_t zero = 0;
+    if (hipMemcpy(dflag, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return MLA_ERR_DEVICE;
+    return MLA_ERR_BAD_INPUT;
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

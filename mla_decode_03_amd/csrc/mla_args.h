@@ -1,0 +1,55 @@
+// Kernel argument blocks and launcher entry points shared by the host API and the
+// kernel translation units of libmla.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeArgs {
+  const uint8_t* q;            // bf16 [B, R, 576]
+  const uint8_t* kv;           // bf16 [num_pages, 64, 576]
+  const int32_t* block_table;  // [B, bt_stride]
+  const int32_t* seqlens;      // [B]
+  uint16_t* out;               // bf16 [B, R, 512]
+  float* lse;                  // [B, R]
+  int32_t* meta;               // plan, or nullptr (one workgroup per sequence)
+  float* ws_o;                 // partials [slots, rows_per_wg, 512]
+  float* ws_lse;               // partials [slots, rows_per_wg]
+  float scale_log2;            // scale * log2(e)
+  int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
+  int rows_per_wg, row_split;
+};
+
+struct CombineArgs {
+  const int32_t* meta;
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* out;    // bf16 [B, R, 512]
+  float* lse;       // [B, R]
+  int batch, rows, rows_per_wg, row_split;
+};
+
+struct F32Args {
+  const float* q;              // [B, R, 576]
+  const float* kv;             // [num_pages, 64, 576]
+  const int32_t* block_table;  // [B, bt_stride]
+  const int32_t* seqlens;      // [B]
+  float* out;                  // [B, R, 512]
+  float* lse;                  // [B, R]
+  float scale;
+  int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
+};
+
+}  // namespace mla
+
+// Internal launchers: not part of the exported ABI.
+#define MLA_INTERNAL __attribute__((visibility("hidden")))
+
+extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32_t* meta, int batch, int rows,
+                                      int row_split, int grid_wg, int min_blocks, int max_blocks,
+                                      int max_partials, hipStream_t stream);
+extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream);
+extern "C" MLA_INTERNAL hipError_t mla_launch_combine(const mla::CombineArgs* args, hipStream_t stream);
+extern "C" MLA_INTERNAL hipError_t mla_launch_decode_f32(const mla::F32Args* args, hipStream_t stream);

@@ -1,0 +1,76 @@
+// Log-sum-exp merge of split-KV partials (the second kernel of a split decode).
+//
+// A unit (rows of one sequence) cut across k > 1 workgroups left k partial results
+// (o_s = normalised output over its key range, lse_s = natural-log sum of exp over
+// it).  Over the union of the disjoint ranges:
+//     lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s
+//     out = sum_s exp(lse_s - lse) * o_s
+// A partial with lse_s = -inf weighs 0; a NaN partial (a poisoned segment) makes the row NaN.  Units with no blocks at all get out = 0,
+// lse = -inf.  Units decoded by one workgroup were written directly and are skipped.
+// Memory-bound: 8 rows per workgroup, 32 threads per row, 16 output dims per thread.
+#include "mla_args.h"
+#include "mla_device.h"
+
+namespace mla {
+
+
+constexpr int kCombineRows = 8;
+
+__global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
+  MetaView v = meta_view(const_cast<int32_t*>(a.meta), a.batch, a.row_split);
+  const int chunks = (a.rows_per_wg + kCombineRows - 1) / kCombineRows;
+  const int u = blockIdx.x / chunks;
+  const int rl = (blockIdx.x % chunks) * kCombineRows + (threadIdx.x >> 5);
+  if (u >= a.batch * a.row_split || rl >= a.rows_per_wg) return;
+  const int ns = v.num_splits[u];
+  if (ns == 1) return;
+  const int b = u / a.row_split, g = u % a.row_split;
+  const int r = g * a.rows_per_wg + rl;
+  const int t = threadIdx.x & 31;
+  uint16_t* orow = a.out + ((size_t)b * a.rows + r) * kDv + 16 * t;
+  if (ns == 0) {
+    *(u32x4*)orow = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(orow + 8) = u32x4{0u, 0u, 0u, 0u};
+    if (t == 0) a.lse[(size_t)b * a.rows + r] = -INFINITY;
+    return;
+  }
+  const int s0 = v.part_off[u];
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[(size_t)(s0 + s) * a.rows_per_wg + rl]);
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float tot = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const size_t prow = (size_t)(s0 + s) * a.rows_per_wg + rl;
+    const float wgt = expf(a.ws_lse[prow] - Ms);
+    tot += wgt;
+    const f32x4* src = (const f32x4*)(a.ws_o + prow * kDv + 16 * t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 x = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[4 * i + j] += wgt * x[j];
+    }
+  }
+  const bool empty = !(tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / tot;
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    packed[i] = f32_to_bf16_rne(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
+  *(u32x4*)orow = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  *(u32x4*)(orow + 8) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+  if (t == 0) a.lse[(size_t)b * a.rows + r] = empty ? -INFINITY : Ms + logf(tot);
+}
+
+}  // namespace mla
+
+extern "C" MLA_INTERNAL hipError_t mla_launch_combine(const mla::CombineArgs* args, hipStream_t stream) {
+  const int chunks = (args->rows_per_wg + mla::kCombineRows - 1) / mla::kCombineRows;
+  const int grid = args->batch * args->row_split * chunks;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla::mla_combine_kernel, dim3(grid), dim3(256), 0, stream, *args);
+  return hipGetLastError();
+}

@@ -1,0 +1,94 @@
+// Device-side helpers shared by the libmla kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+namespace mla {
+
+constexpr int kDqk = 576;                 // cache row: 512 latent + 64 rope
+constexpr int kDv = 512;                  // value width (first 512 dims of a row)
+constexpr int kPage = 64;                 // tokens per page = tokens per KV block
+constexpr int kRowBytes = kDqk * 2;       // one bf16 cache row: 1152 B = 72 chunks of 16 B
+constexpr int kChunksPerRow = kRowBytes / 16;
+constexpr int kBlockBytes = kPage * kRowBytes;   // 73728 B per bf16 page
+constexpr int kLoadsPerBlock = kBlockBytes / 1024;  // 72 wave-wide 16 B/lane loads
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- plan (metadata) layout, int32 words --------------------------------------------
+// header
+constexpr int kMetaMagic = 0x4D4C4150;    // 'MLAP'
+enum MetaHdr {
+  kHdrMagic = 0,
+  kHdrBatch = 1,
+  kHdrRows = 2,          // rows per sequence R = q_len * heads
+  kHdrRowSplit = 3,      // workgroups sharing one sequence's rows
+  kHdrRowsPerWg = 4,
+  kHdrNumWg = 5,         // workgroups that have work (device-computed)
+  kHdrGridWg = 6,        // workgroups launched (host-known upper bound)
+  kHdrTotal = 7,         // total 64-token blocks over all units
+  kHdrNumPartials = 8,   // partial slots used
+  kHdrError = 9,         // device-side input fault flag
+  kHdrMaxPartials = 10,  // partial slot capacity of the workspace
+  kHdrMaxBlocks = 11,    // max_blocks_per_seq the plan was made for
+  kHdrWords = 16,
+};
+// arrays follow the header: cu_blocks[B+1], num_splits[U], first_wg[U], part_off[U],
+// wg_begin[grid+1], with U = B * row_split units (unit u = b * row_split + g).
+struct MetaView {
+  int32_t* hdr;
+  int32_t* cu_blocks;
+  int32_t* num_splits;
+  int32_t* first_wg;
+  int32_t* part_off;
+  int32_t* wg_begin;
+};
+__host__ __device__ inline size_t meta_words(int batch, int row_split, int grid_wg) {
+  const size_t units = (size_t)batch * row_split;
+  return kHdrWords + (size_t)(batch + 1) + 3 * units + (size_t)grid_wg + 1;
+}
+__host__ __device__ inline MetaView meta_view(int32_t* base, int batch, int row_split) {
+  MetaView v;
+  const size_t units = (size_t)batch * row_split;
+  v.hdr = base;
+  v.cu_blocks = base + kHdrWords;
+  v.num_splits = v.cu_blocks + batch + 1;
+  v.first_wg = v.num_splits + units;
+  v.part_off = v.first_wg + units;
+  v.wg_begin = v.part_off + units;
+  return v;
+}
+
+// ---- small device utilities ---------------------------------------------------------
+// Read-only kernel inputs (block tables, sequence lengths, the plan) are read through the
+// constant address space so uniform reads become scalar loads.
+#define MLA_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, size_t i) {
+  return ((const MLA_CONST T*)p)[i];
+}
+// Index of this wave in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ inline float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace mla

@@ -1,0 +1,123 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every symbol the
+header declares (and nothing else), and every host-checkable argument fault returns
+its status code before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_decode_03_amd as m
+from mla_decode_03_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def _exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    return sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+
+
+def test_library_exports_exactly_the_header():
+    declared = _declared()
+    assert declared == sorted(_abi.EXPORTS)
+    assert _exported() == declared
+    L = m.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings():
+    for code in range(10):
+        assert _abi.status_string(code)
+    assert _abi.status_string(0) == "ok"
+    assert "unknown" in _abi.status_string(99)
+
+
+def _problem(**kw):
+    base = dict(batch=4, q_len=1, num_heads=128, causal=0, num_pages=64, block_table_stride=16,
+                max_blocks_per_seq=16, dtype=m.DTYPE_BF16)
+    base.update(kw)
+    return m.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=129), _abi.MLA_ERR_SHAPE),
+    (dict(q_len=2, num_heads=65), _abi.MLA_ERR_SHAPE),
+    (dict(q_len=0), _abi.MLA_ERR_SHAPE),
+    (dict(batch=-1), _abi.MLA_ERR_SHAPE),
+    (dict(num_pages=0), _abi.MLA_ERR_SHAPE),
+    (dict(block_table_stride=8), _abi.MLA_ERR_SHAPE),
+    (dict(causal=2), _abi.MLA_ERR_SHAPE),
+    (dict(dtype=7), _abi.MLA_ERR_DTYPE),
+])
+def test_decode_rejects_bad_problem(kw, code):
+    p = _problem(**kw)
+    fake = ctypes.c_void_p(0x10000)
+    rc = m.lib().mla_decode(ctypes.byref(p), fake, fake, fake, fake, 1.0, fake, fake, None, None, 0, None)
+    assert rc == code
+    assert m.metadata_bytes(p, None, 256) == 0 and m.workspace_bytes(p, None, 256) == 0
+
+
+def test_decode_rejects_null_and_misaligned():
+    p = _problem()
+    a = ctypes.c_void_p(0x10000)
+    L = m.lib()
+    assert L.mla_decode(None, a, a, a, a, 1.0, a, a, None, None, 0, None) == _abi.MLA_ERR_NULL
+    assert L.mla_decode(ctypes.byref(p), None, a, a, a, 1.0, a, a, None, None, 0, None) == _abi.MLA_ERR_NULL
+    assert L.mla_decode(ctypes.byref(p), a, a, a, a, 1.0, a, None, None, None, 0, None) == _abi.MLA_ERR_NULL
+    odd = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+    assert L.mla_decode(ctypes.byref(p), odd, a, a, a, 1.0, a, a, None, None, 0, None) == _abi.MLA_ERR_ALIGN
+    assert L.mla_decode(ctypes.byref(p), a, a, ctypes.c_void_p(0x10002), a, 1.0, a, a, None, None, 0,
+                        None) == _abi.MLA_ERR_ALIGN
+    # batch 0 is a no-op, even with null buffers
+    p0 = _problem(batch=0)
+    assert L.mla_decode(ctypes.byref(p0), None, None, None, None, 1.0, None, None, None, None, 0, None) == 0
+
+
+def test_plan_sizes_and_workspace_checks():
+    p = _problem()
+    mb = m.metadata_bytes(p, None, 256)
+    wb = m.workspace_bytes(p, None, 256)
+    # header + cu_blocks[B+1] + 3 per unit + wg_begin[grid+1] int32 words
+    assert mb == 4 * (16 + 5 + 3 * 4 + 257)
+    # partial slots: grid + min(grid, units), each rows_per_wg * (512 + 1) floats
+    assert wb == (256 + 4) * 128 * 513 * 4
+    opts = m.PlanOptions(num_workgroups=8, min_blocks_per_wg=1, row_split=2)
+    assert m.workspace_bytes(p, opts, 256) == (8 + 8) * 64 * 513 * 4
+    assert m.workspace_bytes(p, m.PlanOptions(row_split=3), 256) == 0  # unsupported split
+    L = m.lib()
+    a = ctypes.c_void_p(0x10000)
+    # metadata buffer too small: refused before any launch
+    plan = _abi.CPlan(metadata=0x10000, metadata_bytes=mb - 4)
+    assert L.mla_get_metadata(ctypes.byref(p), a, None, 256, ctypes.byref(plan), None) == _abi.MLA_ERR_WORKSPACE
+    plan = _abi.CPlan(metadata=None, metadata_bytes=mb)
+    assert L.mla_get_metadata(ctypes.byref(p), a, None, 256, ctypes.byref(plan), None) == _abi.MLA_ERR_NULL
+    plan = _abi.CPlan(metadata=0x10004, metadata_bytes=mb)
+    assert L.mla_get_metadata(ctypes.byref(p), a, None, 256, ctypes.byref(plan), None) == _abi.MLA_ERR_ALIGN
+    # a plan for another problem, or an undersized workspace, is refused by mla_decode
+    good = _abi.CPlan(metadata=0x10000, metadata_bytes=mb, grid_wg=256, row_split=1, rows_per_wg=128,
+                      max_partials=260, batch=4, rows=128)
+    assert L.mla_decode(ctypes.byref(p), a, a, a, a, 1.0, a, a, ctypes.byref(good), a, wb - 1,
+                        None) == _abi.MLA_ERR_WORKSPACE
+    assert L.mla_decode(ctypes.byref(p), a, a, a, a, 1.0, a, a, ctypes.byref(good), None, wb,
+                        None) == _abi.MLA_ERR_NULL
+    other = _abi.CPlan(metadata=0x10000, metadata_bytes=mb, grid_wg=256, row_split=1, rows_per_wg=128,
+                       max_partials=260, batch=5, rows=128)
+    assert L.mla_decode(ctypes.byref(p), a, a, a, a, 1.0, a, a, ctypes.byref(other), a, wb,
+                        None) == _abi.MLA_ERR_SHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "_LIB_PATH", str(tmp_path / "libmla.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _abi.lib()

@@ -1,0 +1,191 @@
+"""Parity of the HIP decode path (through the C ABI) against the float64 oracle."""
+import numpy as np
+import pytest
+
+from gpu_util import ATOL, compare, oracle_rows, run, sample_rows, say, to_device
+from mla_inputs import make_case, make_config, poison_unused
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_decode_03_amd as mla
+    mla.lib()
+
+
+def _case(B, T, H, lens, seed, causal=False, dtype="bf16", extra_pages=0):
+    return make_case(batch=B, q_len=T, num_heads=H, seqlens=lens, dtype=dtype, causal=causal,
+                     seed=seed, extra_pages=extra_pages)
+
+
+def test_config0_fp32_full():
+    case = make_config(0)
+    say("config0 fp32", case.name)
+    ref_o, ref_l = oracle_rows(case)
+    o, l, _ = run(case)
+    s = compare(o, l, ref_o, ref_l, "config0")
+    assert s["max_abs"] < 1e-4  # fp32 path: far inside the bf16 tolerance
+
+
+SMALL = [
+    # (B, T, H, lens, causal): token counts crossing page edges; every row/wave layout
+    (2, 1, 128, [1, 70], False),
+    (3, 1, 128, [63, 64, 65], False),
+    (2, 1, 128, [4095, 4097], False),
+    (4, 2, 16, [2, 65, 100, 128], True),
+    (3, 2, 16, [1, 3, 64], True),
+    (3, 1, 64, [200, 1, 129], False),
+    (2, 1, 16, [300, 5], False),
+    (2, 1, 48, [130, 77], False),
+    (2, 1, 100, [150, 40], False),
+    (2, 2, 64, [66, 130], True),
+    (3, 1, 128, [0, 50, 0], False),
+]
+
+
+@pytest.mark.parametrize("mode", ["plan", "forced_splits", "unsplit"])
+@pytest.mark.parametrize("B,T,H,lens,causal", SMALL)
+def test_small_parity(B, T, H, lens, causal, mode):
+    import mla_decode_03_amd as mla
+    case = _case(B, T, H, lens, seed=B * 100 + T * 10 + H + len(mode), causal=causal)
+    say("small", B, T, H, lens, causal, mode)
+    ref_o, ref_l = oracle_rows(case)
+    kw = {}
+    if mode == "forced_splits":
+        kw = dict(options=mla.PlanOptions(num_workgroups=7, min_blocks_per_wg=1))
+    elif mode == "unsplit":
+        kw = dict(split=False)
+    o, l, _ = run(case, **kw)
+    compare(o, l, ref_o, ref_l, "small %s" % mode)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_full_config_sampled(idx):
+    """Full-size workloads, default plan (the launch configuration the benchmark times),
+    checked on sampled rows the oracle computes one by one."""
+    case = make_config(idx)
+    say("config", idx, case.name, "pages", case.num_pages)
+    o, l, _ = run(case)
+    rows = sample_rows(case)
+    ref_o, ref_l = oracle_rows(case, rows=rows)
+    compare(o[rows], l[rows], ref_o, ref_l, "config%d sampled %d rows" % (idx, rows.size))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def test_split_counts_agree():
+    """Different split plans (1 .. many workgroups per sequence) differ only by fp32
+    rounding; each also meets the oracle tolerance."""
+    import mla_decode_03_amd as mla
+    case = _case(2, 1, 128, [3000, 1500], seed=7)
+    t = to_device(case)
+    ref_o, ref_l = oracle_rows(case)
+    res = []
+    for nwg in (1, 2, 7, 64, 256):
+        say("splits nwg", nwg)
+        o, l, _ = run(case, tensors=t, options=mla.PlanOptions(num_workgroups=nwg, min_blocks_per_wg=1))
+        compare(o, l, ref_o, ref_l, "nwg=%d" % nwg)
+        res.append((o, l))
+    o0, l0 = res[0]
+    for o, l in res[1:]:
+        assert np.max(np.abs(l - l0)) < 1e-4
+        assert np.max(np.abs(o - o0) / (np.abs(o0) + 1e-3)) < 2 ** -7  # one bf16 rounding apart
+
+
+@pytest.mark.parametrize("rs", [2, 4])
+def test_row_split(rs):
+    import mla_decode_03_amd as mla
+    case = _case(3, 1, 128, [700, 64, 1], seed=11 + rs)
+    say("row_split", rs)
+    ref_o, ref_l = oracle_rows(case)
+    o, l, _ = run(case, options=mla.PlanOptions(num_workgroups=24, min_blocks_per_wg=1, row_split=rs))
+    compare(o, l, ref_o, ref_l, "row_split=%d" % rs)
+
+
+def test_page_permutation_is_bit_exact_and_deterministic():
+    import torch
+    case = _case(3, 1, 128, [500, 130, 64], seed=21)
+    q, kv, bt, lens = to_device(case)
+    o1, l1, dec = run(case, tensors=(q, kv, bt, lens))
+    o1b, l1b, _ = run(case, tensors=(q, kv, bt, lens), decoder=dec)
+    assert np.array_equal(o1, o1b) and np.array_equal(l1, l1b)       # run-to-run identical
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(case.num_pages)).cuda()
+    kv2 = torch.empty_like(kv)
+    kv2[perm] = kv
+    bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0).long()].int(), bt)
+    o2, l2, _ = run(case, tensors=(q, kv2, bt2, lens), decoder=dec)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_poisoned_unused_slots_never_leak():
+    case = _case(3, 2, 16, [70, 129, 2], seed=31, causal=True, extra_pages=3)
+    poison_unused(case)
+    say("poison")
+    ref_o, ref_l = oracle_rows(case)
+    for split in (True, False):
+        o, l, _ = run(case, split=split)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(l[np.isfinite(ref_l)]))
+        compare(o, l, ref_o, ref_l, "poison split=%s" % split)
+
+
+def test_device_plan_matches_mirror():
+    import torch
+    import mla_decode_03_amd as mla
+    from plan_mirror import make_plan, to_words
+    rng = np.random.default_rng(3)
+    lens = [int(x) for x in rng.integers(0, 5000, size=37)]
+    case = _case(37, 1, 128, lens, seed=41)
+    q, kv, bt, lt = to_device(case)
+    for opts in (mla.PlanOptions(num_workgroups=256, min_blocks_per_wg=4),
+                 mla.PlanOptions(num_workgroups=50, min_blocks_per_wg=1, row_split=2)):
+        dec = mla.Decoder(q, kv, bt, options=opts, num_cus=256)
+        plan = dec.plan_for(lt)
+        torch.cuda.synchronize()
+        words = plan.metadata.view(torch.int32).cpu().numpy()
+        ref = make_plan(lens, row_split=opts.row_split or 1, grid_wg=opts.num_workgroups,
+                        min_blocks=opts.min_blocks_per_wg)
+        hdr, arrays = to_words(ref, opts.num_workgroups, 128, plan.max_partials,
+                               case.block_table.shape[1])
+        assert list(words[:12]) == hdr
+        assert list(words[16:16 + len(arrays)]) == arrays
+
+
+def test_bad_page_is_flagged_and_poisoned():
+    import mla_decode_03_amd as mla
+    case = _case(3, 1, 128, [200, 300, 100], seed=51)
+    case.block_table[1, 2] = case.num_pages + 1000      # out of the pool
+    say("bad page")
+    q, kv, bt, lens = to_device(case)
+    o, l, dec = run(case, tensors=(q, kv, bt, lens))
+    assert dec.plan.error() == mla._abi.MLA_ERR_BAD_INPUT
+    assert dec.plan.error() == 0                          # the flag was cleared
+    R = 128
+    assert np.all(np.isnan(o[R:2 * R])) and np.all(np.isnan(l[R:2 * R]))
+    good = np.r_[0:R, 2 * R:3 * R]
+    case.block_table[1, 2] = 0
+    ref_o, ref_l = oracle_rows(case, rows=good)
+    compare(o[good], l[good], ref_o, ref_l, "other sequences")
+
+
+def test_tolerance_is_not_vacuous():
+    """The elementwise bound alone is loose at long lengths; the relative-L2 gate is what
+    catches a wrong kernel.  A plausible bug (V taken from the wrong 512 columns) must fail."""
+    case = _case(1, 1, 16, [4096], seed=61)
+    ref_o, ref_l = oracle_rows(case)
+    o, l, _ = run(case)
+    compare(o, l, ref_o, ref_l, "baseline")
+    case2 = _case(1, 1, 16, [4096], seed=61)
+    case2.kv[..., :512] = case2.kv[..., 64:576]          # the mistake, made in the oracle input
+    case2.kv_bits = None
+    bad_o, _ = oracle_rows(_case_f32(case2))
+    with pytest.raises(AssertionError):
+        compare(o, l, bad_o, ref_l, "wrong-V oracle")
+    assert ATOL > 0
+
+
+def _case_f32(case):
+    case.dtype = "f32"
+    return case

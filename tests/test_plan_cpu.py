@@ -1,0 +1,69 @@
+"""Properties of the split partition rule (CPU, on the mirror in plan_mirror.py)."""
+import numpy as np
+import pytest
+
+from plan_mirror import make_plan, segments
+
+
+def _check(plan, seqlens, rs, max_partials):
+    nblk = [(max(L, 0) + 63) // 64 for L in seqlens]
+    segs = segments(plan)
+    # every unit's blocks are covered exactly once
+    cover = {}
+    for (w, b, g, lo, hi, slot) in segs:
+        assert 0 <= lo < hi <= nblk[b]
+        cover.setdefault((b, g), []).append((lo, hi, w, slot))
+    for b, nb in enumerate(nblk):
+        for g in range(rs):
+            if nb == 0:
+                assert (b, g) not in cover
+                continue
+            parts = sorted(cover[(b, g)])
+            assert parts[0][0] == 0 and parts[-1][1] == nb
+            for (l0, h0, _, _), (l1, _, _, _) in zip(parts, parts[1:]):
+                assert h0 == l1
+            u = b * rs + g
+            assert plan["num_splits"][u] == len(parts)
+            slots = [p[3] for p in parts]
+            if len(parts) == 1:
+                assert slots == [-1]
+            else:
+                assert slots == list(range(plan["part_off"][u], plan["part_off"][u] + len(parts)))
+    # shares are balanced to within one block
+    shares = [plan["wg_begin"][w + 1] - plan["wg_begin"][w] for w in range(plan["num_wg"])]
+    if shares:
+        assert max(shares) - min(shares) <= 1
+        assert sum(shares) == plan["total"]
+    # partial slots are unique and fit the workspace bound
+    used = [s for (*_, s) in segs if s >= 0]
+    assert len(used) == len(set(used)) == plan["num_partials"] <= max_partials
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_plans(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    seqlens = [int(x) for x in rng.integers(0, 3000, size=B)]
+    rs = [1, 2, 4][seed % 3]
+    grid = int(rng.integers(1, 300))
+    minb = int(rng.integers(1, 9))
+    plan = make_plan(seqlens, row_split=rs, grid_wg=grid, min_blocks=minb)
+    _check(plan, seqlens, rs, grid + min(grid, B * rs))
+
+
+def test_headline_shape_splits_each_sequence_in_four():
+    plan = make_plan([4096] * 64, grid_wg=256, min_blocks=4)
+    assert plan["num_wg"] == 256 and set(plan["num_splits"]) == {4}
+    assert plan["num_partials"] == 256
+    _check(plan, [4096] * 64, 1, 512)
+
+
+def test_small_problem_is_not_over_split_and_empty_batch():
+    # 2 + 4 blocks with at least 4 per workgroup: two workgroups; the contiguous cut at
+    # block 3 splits the second sequence in two
+    plan = make_plan([100, 200], grid_wg=256, min_blocks=4)
+    assert plan["num_wg"] == 2 and plan["num_splits"] == [1, 2] and plan["num_partials"] == 2
+    plan = make_plan([100, 200], grid_wg=256, min_blocks=8)
+    assert plan["num_wg"] == 1 and plan["num_splits"] == [1, 1] and plan["num_partials"] == 0
+    plan = make_plan([0, 0], grid_wg=8)
+    assert plan["num_wg"] == 0 and plan["num_splits"] == [0, 0] and segments(plan) == []
