@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
       for (int j = 0; j < 4; ++j) acc[4 * i + j] += wgt * x[j];
     }
   }
-  const bool empty = !(tot > 0.f);
+  const bool empty = tot == 0.f;  // NaN (a poisoned split) propagates
   const float inv = empty ? 0.f : 1.f / tot;
   uint32_t packed[8];
 #pragma unroll

@@ -504,7 +504,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     const int r = rbase + 16 * nt + li;
     if (r >= row_end) continue;
     const float ls = st.lsum[nt];
-    const bool empty = !(ls > 0.f);
+    const bool empty = ls == 0.f;   // no visible key; NaN propagates
     const float nanv = __builtin_nanf("");
     const float scale_o = poison ? nanv : (empty ? 0.f : 1.f / ls);
     const float lse_v = poison ? nanv : (empty ? -INFINITY : (st.m[nt] + __log2f(ls)) * kLn2);

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
       for (int i = 0; i < 8; ++i) o[i] = fmaf(wk, vrow[l + 64 * i], o[i]);
     }
   }
-  const bool empty = !(lsum > 0.f);
+  const bool empty = lsum == 0.f;  // no visible key; NaN propagates
   const float inv = poison ? __builtin_nanf("") : (empty ? 0.f : 1.f / lsum);
   float* orow = a.out + ((size_t)b * a.rows + r) * kDv;
 #pragma unroll

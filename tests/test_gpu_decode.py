@@ -77,8 +77,10 @@ def test_full_config_sampled(idx):
 
 
 def test_split_counts_agree():
-    """Different split plans (1 .. many workgroups per sequence) differ only by fp32
-    rounding; each also meets the oracle tolerance."""
+    """Different split plans (1 .. many workgroups per sequence) each meet the oracle
+    tolerance and agree with each other to the bf16 rounding of P: every split fixes its
+    own reference max, so the rounding errors of P (2^-9 relative) land differently;
+    the outputs then differ by about 2^-9 * |v| / sqrt(effective keys), ~1e-4 here."""
     import mla_decode_03_amd as mla
     case = _case(2, 1, 128, [3000, 1500], seed=7)
     t = to_device(case)
@@ -92,7 +94,10 @@ def test_split_counts_agree():
     o0, l0 = res[0]
     for o, l in res[1:]:
         assert np.max(np.abs(l - l0)) < 1e-4
-        assert np.max(np.abs(o - o0) / (np.abs(o0) + 1e-3)) < 2 ** -7  # one bf16 rounding apart
+        # a bf16 ulp of the output (2^-8..2^-7 relative) plus the P-rounding noise
+        assert np.all(np.abs(o - o0) <= 2 ** -7 * np.abs(o0) + 2e-3)
+        # two independent roundings (output and P, ~2e-3 relative L2 each vs the oracle)
+        assert np.linalg.norm(o - o0) / np.linalg.norm(o0) < 5e-3
 
 
 @pytest.mark.parametrize("rs", [2, 4])
