@@ -125,7 +125,8 @@ MLA_API size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_o
 /*
  * Size in bytes of the workspace mla_decode needs with a plan made for the same
  * problem/options/num_cus: room for the split partials (per split, every row's
- * float32 output and log-sum-exp).  Host-only arithmetic.
+ * normalised output as bf16 and its float32 log-sum-exp: 1028 bytes per row and
+ * partial slot).  Host-only arithmetic.
  */
 MLA_API size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
                            int32_t num_cus);
@@ -179,8 +180,9 @@ MLA_API int32_t mla_decode(const mla_problem_t* problem,
 /*
  * The two launches of mla_decode, for callers (and benchmarks) that want them apart.
  * mla_decode_splits: the split-KV decode kernel alone -- writes out/lse of every
- *   sequence the plan did not split, and the float32 partials (normalised output and
- *   natural-log LSE per split) of the split ones into `workspace`.
+ *   sequence the plan did not split, and the partials of the split ones into
+ *   `workspace` (per split: normalised output rounded to bf16, natural-log LSE in
+ *   float32).
  * mla_combine: merges those partials by log-sum-exp into out/lse (sequences with no
  *   cached tokens get out = 0, lse = -inf).  Same plan and workspace as the decode.
  * Both require a plan and a bf16 problem; mla_decode(plan != NULL) == splits + combine.

@@ -18,6 +18,11 @@ constexpr int kDefaultMinBlocks = 4;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Split partials: bf16 normalised outputs [slots, rows, 512], then fp32 LSE [slots, rows].
+size_t partial_bytes(int64_t slots, int64_t rows_per_wg) {
+  return (size_t)slots * rows_per_wg * (mla::kDv * sizeof(uint16_t) + sizeof(float));
+}
+
 int32_t check_problem(const mla_problem_t* p) {
   if (!p) return MLA_ERR_NULL;
   if (p->dtype != MLA_DTYPE_F32 && p->dtype != MLA_DTYPE_BF16) return MLA_ERR_DTYPE;
@@ -113,7 +118,7 @@ size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_options_t
 size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options, int32_t num_cus) {
   PlanShape s;
   if (plan_shape(problem, options, num_cus, &s) != MLA_OK) return 0;
-  return (size_t)s.max_partials * s.rows_per_wg * (mla::kDv + 1) * sizeof(float);
+  return partial_bytes(s.max_partials, s.rows_per_wg);
 }
 
 int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
@@ -185,13 +190,13 @@ int32_t attach_plan(const mla_problem_t& p, const mla_plan_t* plan, const void* 
       plan->rows_per_wg * plan->row_split != rows || plan->max_partials < 0)
     return MLA_ERR_SHAPE;
   if (!aligned(plan->metadata, 16)) return MLA_ERR_ALIGN;
-  const size_t ws_need = (size_t)plan->max_partials * plan->rows_per_wg * (mla::kDv + 1) * sizeof(float);
+  const size_t ws_need = partial_bytes(plan->max_partials, plan->rows_per_wg);
   if (ws_need > 0 && !workspace) return MLA_ERR_NULL;
   if (workspace_bytes < ws_need) return MLA_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 16)) return MLA_ERR_ALIGN;
   a->meta = static_cast<int32_t*>(plan->metadata);
-  a->ws_o = static_cast<float*>(const_cast<void*>(workspace));
-  a->ws_lse = a->ws_o + (size_t)plan->max_partials * plan->rows_per_wg * mla::kDv;
+  a->ws_o = static_cast<uint16_t*>(const_cast<void*>(workspace));
+  a->ws_lse = reinterpret_cast<float*>(a->ws_o + (size_t)plan->max_partials * plan->rows_per_wg * mla::kDv);
   a->rows_per_wg = plan->rows_per_wg;
   a->row_split = plan->row_split;
   return MLA_OK;

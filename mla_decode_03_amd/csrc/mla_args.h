@@ -15,8 +15,8 @@ struct DecodeArgs {
   uint16_t* out;               // bf16 [B, R, 512]
   float* lse;                  // [B, R]
   int32_t* meta;               // plan, or nullptr (one workgroup per sequence)
-  float* ws_o;                 // partials [slots, rows_per_wg, 512]
-  float* ws_lse;               // partials [slots, rows_per_wg]
+  uint16_t* ws_o;              // partial outputs, bf16 [slots, rows_per_wg, 512]
+  float* ws_lse;               // partial log-sum-exp [slots, rows_per_wg]
   float scale_log2;            // scale * log2(e)
   int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
   int rows_per_wg, row_split;
@@ -24,7 +24,7 @@ struct DecodeArgs {
 
 struct CombineArgs {
   const int32_t* meta;
-  const float* ws_o;
+  const uint16_t* ws_o;        // bf16 partial outputs
   const float* ws_lse;
   uint16_t* out;    // bf16 [B, R, 512]
   float* lse;       // [B, R]

@@ -2,7 +2,7 @@
 //
 // A unit (rows of one sequence) cut across k > 1 workgroups left k partial results
 // (o_s = normalised output over its key range, lse_s = natural-log sum of exp over
-// it).  Over the union of the disjoint ranges:
+// it; o_s stored as bf16).  Over the union of the disjoint ranges:
 //     lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s
 //     out = sum_s exp(lse_s - lse) * o_s
 // A partial with lse_s = -inf weighs 0; a NaN partial (a poisoned segment) makes the row NaN.  Units with no blocks at all get out = 0,
@@ -46,12 +46,15 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
     const size_t prow = (size_t)(s0 + s) * a.rows_per_wg + rl;
     const float wgt = expf(a.ws_lse[prow] - Ms);
     tot += wgt;
-    const f32x4* src = (const f32x4*)(a.ws_o + prow * kDv + 16 * t);
+    const u32x4* src = (const u32x4*)(a.ws_o + prow * kDv + 16 * t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 x = src[i];
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 x = src[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[4 * i + j] += wgt * x[j];
+      for (int j = 0; j < 4; ++j) {
+        acc[8 * i + 2 * j] += wgt * __uint_as_float(x[j] << 16);
+        acc[8 * i + 2 * j + 1] += wgt * __uint_as_float(x[j] & 0xffff0000u);
+      }
     }
   }
   const bool empty = tot == 0.f;  // NaN (a poisoned split) propagates

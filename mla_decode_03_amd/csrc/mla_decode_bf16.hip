@@ -1,45 +1,56 @@
 // Split-KV MLA decode on bf16 MFMA for gfx950 (CDNA4).
 //
-// One workgroup = 4 waves on one CU walks a contiguous range of 64-token KV blocks
-// (its share from the split planner; NULL plan = one whole sequence).  Per block:
+// One workgroup = 4 waves on one CU walks a contiguous range of 64-token KV pages (its
+// share from the split planner; NULL plan = one whole sequence), 32 tokens at a time:
 //
-//   S^T = K . Q^T          MFMA 16x16x32 bf16, K tile from LDS, Q fragments in VGPRs
+//   S^T = K . Q^T          MFMA 16x16x32 bf16, K from LDS, Q fragments held in VGPRs
 //   online softmax         per row, exp2 with the scale folded into log2(e)
-//   O^T += V^T . P^T       MFMA 16x16x32 bf16, V read from the same LDS tile with the
-//                          gfx950 transposing LDS read, P straight from registers
+//   O^T += V^T . P^T       MFMA 16x16x32 bf16, V read from the same LDS page with the
+//                          gfx950 transposing LDS read
 //
 // This is the two-GEMM structure of the TileLang notes' FlashMLA example ("TileLang:
 // bridging programmability and performance in modern neural kernels", section "A
-// complete example: two-stage optimisation of FlashMLA": Q and KV tiles staged on
-// chip, S kept in registers, down-cast, second GEMM), and the exp2 / log2(e) form of
-// the online softmax shown in the DeepSeek-V4 TileLang note (section "The essence of
-// TileLang's design").  Placement is re-derived for gfx950: the 128x576 Q tile
-// (147 KB) and two 73.7 KB KV pages cannot share the 160 KB LDS, so Q lives in VGPRs,
-// O (128x512 fp32, 256 regs per wave) in the accumulation registers (AGPRs), and LDS
-// holds only the double-buffered KV stream, fed by global_load_lds (no VGPR staging).
-// S is computed transposed (tokens x rows) so that its accumulator layout is already
-// the B operand of the second MFMA: no shuffle between the GEMMs.  O is never rescaled
-// inside the loop (so its accumulators never leave the AGPRs): each row fixes its
-// reference max at its first visible keys and accumulates exp2(x - m_ref) <= 2^16; if a
-// later score exceeds m_ref + 16 (log2 units), the segment is decoded again with m_ref
-// = the row's true running max, which no score can exceed.
+// complete example: two-stage optimisation of FlashMLA": Q and KV tiles staged on chip,
+// S kept in registers, down-cast, second GEMM), and the exp2 / log2(e) form of the
+// online softmax shown in the DeepSeek-V4 TileLang note (section "The essence of
+// TileLang's design").  Placement is re-derived for gfx950: the 128x576 Q tile (147 KB)
+// and two 73.7 KB pages cannot share the 160 KB LDS, so Q lives in VGPRs (32 rows x 576
+// per wave), O (fp32) in the accumulation registers, and LDS holds the double-buffered
+// KV stream fed by global_load_lds (no VGPR staging).  S is computed transposed (tokens
+// x rows) so that its accumulator layout is already the B operand of the second MFMA.
 //
-// Waves split the rows (TG = 1: 32 rows each, all 64 tokens), or rows and tokens
-// (TG = 2, 4) when a sequence has <= 64 / <= 32 rows; token groups merge their
-// softmax states through LDS at the end of a segment.
+// Two work splits over the 4 waves:
+//  * wide (more than 64 rows, e.g. 128 heads): each wave scores its own 32 rows, writes
+//    its bf16 P fragments to LDS, and then accumulates O for ALL rows over its quarter of
+//    the 512 value columns.  Each page's V is then read from LDS once instead of four
+//    times, which keeps the P.V phase off the LDS-bandwidth limit.
+//  * narrow (<= 64 rows): waves split rows and tokens (TG token groups); each wave keeps
+//    O for its 32 rows and the token groups merge their states through LDS at the end.
+// O is never rescaled inside the loop: each row fixes its reference max at its first
+// visible keys and accumulates exp2(x - m_ref) <= 2^kRefSlack; if a later score exceeds
+// that, the segment is decoded again with m_ref = the row's true running max (exact).
 #include "mla_args.h"
 #include "mla_device.h"
 
 namespace mla {
 
-// ---- LDS layout of one KV page buffer (73728 B) -------------------------------------
+// ---- LDS layout ---------------------------------------------------------------------
+// Two page buffers of 73728 B each:
 //   [0, 65536)      value/latent part: token t, 16-byte chunk c < 64 at t*1024 + (c ^ swz(t))*16
 //   [65536, 73728)  rope part:         token t, chunk 64 + c   at 65536 + t*128 + (c ^ swz(t))*16
+// then (wide split only) a 16 KB P buffer: [K step 0..3][row tile 0..3][lane][8 x bf16].
 // swz maps any 8 consecutive tokens to 8 distinct values (conflict-free K reads: 8 lanes
 // read 8 tokens at one chunk) and any 4 consecutive tokens to distinct swz >> 1
 // (conflict-free transposing V reads: 4 tokens x 2 adjacent chunks per 16 lanes).
 constexpr int kRopeOff = 65536;
+constexpr int kPBufOff = 2 * kBlockBytes;          // 147456
+constexpr int kPBufBytes = 16384;                 // wide split: P of one page
+constexpr int kLdsBytes = kPBufOff + kPBufBytes;   // 163840 = all of it
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+constexpr float kRefSlack = 16.0f;  // scores may exceed the reference max by 2^16
+constexpr int kPrefK = 2;           // K-fragment prefetch distance (32-dim steps)
+constexpr int kPrefV = 4;           // V-fragment prefetch distance (16-wide value tiles)
 
 // One wave-wide 16 B/lane global->LDS copy: lane i's 16 bytes from base + voff land at
 // LDS address lds + 16*i.  Issued as assembly so the compiler does not treat it as an
@@ -55,27 +66,39 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, MLA_LD
 // (16 value rows + 2 x 8 rope rows).  Tokens >= valid (the tail of a sequence's last
 // page) copy token 0 instead: their scores are masked to -inf, so the finite stand-in
 // rows contribute exactly 0 and never leak NaN or garbage.  w must be wave-uniform.
+// A page's global->LDS copy, issued piecewise: each wave issues 18 one-KB copies, 16 of
+// value rows (token 16w + i) and 2 of rope rows (8 tokens each).  Tokens at or past
+// `valid` re-read token 0 of the page (never used; keeps every read inside the page).
+struct PageCopy {
+  const uint8_t* base;    // page start in the pool (uniform)
+  int valid;              // tokens of the page in the sequence
+  MLA_LDS uint8_t* buf;   // page buffer
+};
+__device__ __forceinline__ void issue_copy(const PageCopy& c, int i, int w, int l) {
+  if (i < 16) {
+    const int t = 16 * w + i;
+    const int te = (t < c.valid) ? t : 0;                   // uniform
+    dma16(c.base + te * kRowBytes, (uint32_t)(l ^ swz(i)) << 4, c.buf + t * 1024);
+  } else {
+    const int k = 2 * w + (i - 16);
+    const int t = 8 * k + (l >> 3);
+    const int te = (t < c.valid) ? t : 0;
+    dma16(c.base, (uint32_t)(te * kRowBytes + ((64 + ((l & 7) ^ swz(l >> 3))) << 4)),
+          c.buf + kRopeOff + k * 1024);
+  }
+}
 __device__ __forceinline__ void issue_page(const uint8_t* __restrict__ kv, int page, int valid,
                                            MLA_LDS uint8_t* buf, int w, int l) {
-  const uint8_t* base = kv + (size_t)page * kBlockBytes;   // uniform
+  const PageCopy c{kv + (size_t)page * kBlockBytes, valid, buf};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = 16 * w + i;
-    const int te = (t < valid) ? t : 0;                     // uniform
-    dma16(base + te * kRowBytes, (uint32_t)(l ^ swz(i)) << 4, buf + t * 1024);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int k = 2 * w + i;
-    const int t = 8 * k + (l >> 3);
-    const int te = (t < valid) ? t : 0;
-    dma16(base, (uint32_t)(te * kRowBytes + ((64 + ((l & 7) ^ swz(l >> 3))) << 4)),
-          buf + kRopeOff + k * 1024);
-  }
+  for (int i = 0; i < 18; ++i) issue_copy(c, i, w, l);
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS uint8_t* p) {
   return *(const MLA_LDS bf16x8*)p;
+}
+__device__ __forceinline__ void lds_write_b128(MLA_LDS uint8_t* p, const bf16x8& v) {
+  *(MLA_LDS bf16x8*)p = v;
 }
 __device__ __forceinline__ bf16x4 lds_read_tr(const MLA_LDS uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
@@ -92,56 +115,35 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
   return r;
 }
 
+// Workgroup-wide OR through 4 words of caller-provided LDS that no wave touches
+// between the two barriers (the wide split uses every byte of LDS, so the OR cannot
+// reserve its own).
+__device__ __forceinline__ bool wg_or(bool f, MLA_LDS int* scratch) {
+  const int w = wave_id();
+  const int wf = __builtin_amdgcn_ballot_w64(f) != 0;
+  if ((threadIdx.x & 63) == 0) scratch[w] = wf;
+  __syncthreads();
+  const bool r = (scratch[0] | scratch[1] | scratch[2] | scratch[3]) != 0;
+  __syncthreads();  // every wave has read before the words are reused
+  return r;
+}
+
 // Keep an O tile in AGPRs across a point where vector ALU code touched it.
 __device__ __forceinline__ void pin_agpr(f32x4& t) { asm volatile("" : "+a"(t)); }
 
-// Per-wave softmax state and accumulators: rows rbase + 16*nt + (lane % 16), nt < 2.
-struct WaveState {
-  f32x4 o[32][2];   // O^T tiles [dv tile][row tile]; lane holds dv 16*dt + 4*(lane/16) + j
-  float m[2];       // reference max of x = s * scale * log2(e); o and lsum are relative to it
+// Softmax state of the rows a wave scores: rows rbase + 16*nt + (lane % 16), nt < 2.
+struct RowState {
+  float m[2];       // reference max of x = s * scale * log2(e); O and lsum are relative to it
   float lsum[2];    // sum of exp2(x - m)
   float mtrue[2];   // running max of every x seen (for the restart pass)
   bool over;        // some x exceeded m + kRefSlack: the pass must be redone
 };
 
-constexpr float kRefSlack = 16.0f;          // scores may exceed the reference max by 2^16
-constexpr int kPrefK = 1;                   // K-fragment prefetch distance (32-dim steps)
-constexpr int kPrefV = 1;                   // V-fragment prefetch distance (16-dim tiles)
-constexpr int kStateSlotFloats = (256 + 4) * 64;
-
-__device__ __forceinline__ void store_state(const WaveState& st, MLA_LDS float* slot, int l) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) slot[((dt * 2 + nt) * 4 + j) * 64 + l] = st.o[dt][nt][j];
-    slot[256 * 64 + nt * 64 + l] = st.m[nt];
-    slot[256 * 64 + 128 + nt * 64 + l] = st.lsum[nt];
-  }
-}
-__device__ __forceinline__ void merge_state(WaveState& st, const MLA_LDS float* slot, int l) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float mb = slot[256 * 64 + nt * 64 + l];
-    const float lb = slot[256 * 64 + 128 + nt * 64 + l];
-    const float mn = fmaxf(st.m[nt], mb);
-    const float ms = (mn == -INFINITY) ? 0.f : mn;
-    const float fa = __builtin_amdgcn_exp2f(st.m[nt] - ms), fb = __builtin_amdgcn_exp2f(mb - ms);
-    st.lsum[nt] = st.lsum[nt] * fa + lb * fb;
-    st.m[nt] = mn;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        st.o[dt][nt][j] = st.o[dt][nt][j] * fa + slot[((dt * 2 + nt) * 4 + j) * 64 + l] * fb;
-      pin_agpr(st.o[dt][nt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
-// One K step (32 dims) of S^T for NMT token tiles x 2 row tiles, VGPR accumulators.
+// ---- MFMA steps, written out so the register classes can be pinned -------------------
+// S accumulators live in VGPRs, O in AGPRs.  Chains accumulate into exactly the same
+// registers (no wait states needed between them); a first step takes C = 0; "s_nop 1"
+// covers a vector-ALU write of an operand just before (2 wait states); a step that ends
+// a chain read later by vector ALU code appends 21 wait states.
 template <int NMT>
 __device__ __forceinline__ void mfma_s_step(f32x4 (&s)[NMT][2], const bf16x8 (&ka)[NMT],
                                             const bf16x8& q0, const bf16x8& q1, int kk) {
@@ -200,10 +202,7 @@ __device__ __forceinline__ void mfma_s_step(f32x4 (&s)[NMT][2], const bf16x8 (&k
   }
 }
 
-// One 16-wide dv tile of O^T += V^T . P^T for both row tiles, accumulators pinned to
-// AGPRs.  "s_nop 1" covers a VALU write of an operand right before (2 wait states);
-// `last` appends 21 wait states so later VALU reads of O (rescale, epilogue) see the
-// final results.
+// Narrow split: one 16-wide value tile for the wave's 2 row tiles.
 __device__ __forceinline__ void mfma_pv32(f32x4& o0, f32x4& o1, const bf16x8& va, const bf16x8& p0,
                                           const bf16x8& p1, bool last) {
   if (!last)
@@ -242,30 +241,91 @@ __device__ __forceinline__ void mfma_pv16(f32x4& o0, f32x4& o1, const s16x4& va,
         : "+a"(o0), "+a"(o1)
         : "v"(va), "v"(p0), "v"(p1));
 }
+// Wide split (32x32x16 tiles).  S^T step: two 32-token tiles x the wave's 32 rows, one
+// 16-dim K step; accumulators in VGPRs.
+__device__ __forceinline__ void mfma32_s_step(f32x16& s0, f32x16& s1, const bf16x8& k0, const bf16x8& k1,
+                                              const bf16x8& q, int kk) {
+  if (kk == 0)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %3, %4, 0"
+        : "=&v"(s0), "=&v"(s1)
+        : "v"(k0), "v"(k1), "v"(q));
+  else if (kk < 35)
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+        : "+v"(s0), "+v"(s1)
+        : "v"(k0), "v"(k1), "v"(q));
+  else
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %1\n\t"
+        "s_nop 15\n\t"
+        "s_nop 4"
+        : "+v"(s0), "+v"(s1)
+        : "v"(k0), "v"(k1), "v"(q));
+}
+// O^T step: one 32-wide value tile x all 4 row tiles (128 rows), one 16-token K step;
+// accumulators in AGPRs.
+__device__ __forceinline__ void mfma32_pv_step(f32x16 (&o)[4], const bf16x8& va, const bf16x8 (&p)[4],
+                                               bool last) {
+  if (!last)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3"
+        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
+        : "v"(va), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+  else
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3\n\t"
+        "s_nop 15\n\t"
+        "s_nop 4"
+        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
+        : "v"(va), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+}
 
 // Lane constants for LDS reads.
 struct LaneOffsets {
-  int k_v;      // K read, value part: token li row + chunk bits
+  int k_v;      // K read, value part: token li row
   int kx;       // K read chunk xor: chunk (4*kk + lq) ^ swz(li) == (4*kk) ^ kx
   int k_r;      // K read, rope part
   int v_base;   // V read: token 4*lq + li/4, byte 8*(li&1)
-  int vy[4];    // V read chunk offsets for dv tile dt with dt % 4 == d
+  int vy[4];    // V read chunk offsets for value tile dt with dt % 4 == d
 };
+__device__ __forceinline__ LaneOffsets lane_offsets(int l) {
+  const int lq = l >> 4, li = l & 15;
+  LaneOffsets lo;
+  lo.kx = lq ^ swz(li);
+  lo.k_v = li * 1024;
+  lo.k_r = kRopeOff + li * 128;
+  const int vg = (((li >> 2) & 3) << 1) | (lq & 1);   // swz of token 4*lq + li/4
+  lo.v_base = (4 * lq + (li >> 2)) * 1024 + 8 * (li & 1);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) lo.vy[d] = ((2 * d + ((li & 3) >> 1)) ^ vg) << 4;
+  return lo;
+}
 
-// One sub-block of NMT 16-token tiles starting at token tokA of the LDS page `cur`:
-// scores, lazy online softmax, and the P.V update.
+// V^T fragment (16 value columns x 32 tokens from tokA) as the A operand: two transposing
+// reads, tokens tokA + {4*lq .. +3} and tokA + 16 + {4*lq .. +3} for column 16*dt + li.
+__device__ __forceinline__ bf16x8 load_v32(const MLA_LDS uint8_t* cur, const LaneOffsets& lo, int tokA,
+                                           int dt) {
+  const MLA_LDS uint8_t* vp = cur + lo.v_base + tokA * 1024 + (dt >> 2) * 128 + lo.vy[dt & 3];
+  return cat8(lds_read_tr(vp), lds_read_tr(vp + 16 * 1024));
+}
+
+// S^T for NMT 16-token tiles starting at token tokA, all 576 dims (K from LDS).
 template <int NMT>
-__device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][18],
-                                          const MLA_LDS uint8_t* cur, int tokA, const LaneOffsets& lo,
-                                          bool need_mask, int pos0, const int (&nvis)[2],
-                                          float scale_log2, int l) {
-  const int lq = l >> 4;
-  // ---- S^T = K . Q^T over all 576 dims ---------------------------------------------
-  // The S accumulators are kept in VGPRs (the AGPRs hold O): these MFMAs are written
-  // out so the register class can be pinned.  Chains accumulate into exactly the same
-  // registers (no wait states needed); the first step takes C = 0; the last step ends
-  // with 21 wait states so VALU reads of S see the final MFMA results.
-  f32x4 s[NMT][2];
+__device__ __forceinline__ void s_phase(f32x4 (&s)[NMT][2], const bf16x8 (&qf)[2][18],
+                                        const MLA_LDS uint8_t* cur, int tokA, const LaneOffsets& lo) {
   auto load_k = [&](int kk, bf16x8(&ka)[NMT]) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -277,8 +337,7 @@ __device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][1
     }
   };
   // K fragments are fetched kPrefK steps ahead through a small ring; the scheduling
-  // fences keep the compiler from hoisting further (each fragment costs 4 VGPRs and Q
-  // already holds 144).
+  // fences keep the compiler from hoisting further (Q already holds 144 VGPRs).
   bf16x8 kring[kPrefK + 1][NMT];
 #pragma unroll
   for (int kk = 0; kk < kPrefK; ++kk) load_k(kk, kring[kk]);
@@ -288,8 +347,15 @@ __device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][1
     mfma_s_step<NMT>(s, kring[kk % (kPrefK + 1)], qf[0][kk], qf[1][kk], kk);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
 
-  // ---- softmax: lane owns rows li and 16 + li; its 4*NMT values per row --------------
+// Softmax of the scores in s (lane owns rows li and 16 + li, 4*NMT keys each): masks
+// keys at positions >= nvis, updates the row state, returns P as bf16 B operands.
+template <int NMT>
+__device__ __forceinline__ void softmax_p(RowState& st, f32x4 (&s)[NMT][2], bf16x4 (&pb)[NMT][2],
+                                          bool need_mask, int pos0, const int (&nvis)[2],
+                                          float scale_log2, int l) {
+  const int lq = l >> 4;
   float mx[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -312,7 +378,6 @@ __device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][1
     if (st.m[nt] == -INFINITY) st.m[nt] = mx[nt];     // nothing accumulated yet: exact
     st.over |= mx[nt] > st.m[nt] + kRefSlack;
   }
-  bf16x4 pb[NMT][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float msub = (st.m[nt] == -INFINITY) ? 0.f : st.m[nt];
@@ -331,25 +396,366 @@ __device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][1
     rs += __shfl_xor(rs, 32, 64);
     st.lsum[nt] += rs;
   }
+}
 
-  // ---- O^T += V^T . P^T (V = first 512 dims of the same tokens) ---------------------
-  const MLA_LDS uint8_t* vrow = cur + lo.v_base + tokA * 1024;
+// Per-segment setup shared by both splits.
+struct SegmentSetup {
+  int Lc;          // sequence length (0 if it is out of range)
+  bool bad_len;
+  int nvis[2];     // visible keys of this lane's two scored rows
+  int nmin;        // fewest visible keys over the workgroup's rows
+};
+__device__ __forceinline__ SegmentSetup segment_setup(const DecodeArgs& a, int b, int row0, int rbase,
+                                                      int li) {
+  SegmentSetup s;
+  const int L = ld_const(a.seqlens, b);
+  s.bad_len = (L < 0) || ((int64_t)L > (int64_t)kPage * a.max_blocks);
+  s.Lc = s.bad_len ? 0 : L;
+  const int R = a.rows;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = min(rbase + 16 * nt + li, R - 1);
+    int n = s.Lc;
+    if (a.causal && a.q_len > 1) n = s.Lc - a.q_len + 1 + r / a.heads;
+    s.nvis[nt] = max(n, 0);
+  }
+  s.nmin = s.Lc;
+  if (a.causal && a.q_len > 1) s.nmin = max(s.Lc - a.q_len + 1 + row0 / a.heads, 0);
+  return s;
+}
+
+// Q fragments (B operand of S^T = K Q^T): lane holds q[row][32*kk + 8*lq .. +8] for
+// rows rbase + 16*nt + li; rows >= row_end read as zero.
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int rbase, int row0, int row_end,
+                                       int l, bf16x8 (&qf)[2][18]) {
+  const int lq = l >> 4, li = l & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = rbase + 16 * nt + li;
+    const bool ok = r < row_end;
+    const bf16x8* src = (const bf16x8*)(a.q + ((size_t)b * a.rows + (ok ? r : row0)) * kRowBytes) + lq;
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const bf16x8 v = src[4 * kk];
+      qf[nt][kk] = ok ? v : bf16x8{};
+    }
+  }
+}
+
+__device__ __forceinline__ void issue_block(const DecodeArgs& a, int b, int j, int Lc, MLA_LDS uint8_t* buf,
+                                            int w, int l, bool& bad_page) {
+  const int page = ld_const(a.block_table, (size_t)b * a.bt_stride + j);
+  const bool bad = page < 0 || page >= a.num_pages;
+  bad_page |= bad;
+  issue_page(a.kv, bad ? 0 : page, bad ? 1 : min(kPage, Lc - j * kPage), buf, w, l);
+}
+// Page j's copy description, checking the page index (a bad index reads page 0 and
+// poisons the segment).
+__device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int b, int j, int Lc, MLA_LDS uint8_t* buf,
+                                              bool& bad_page) {
+  const int page = ld_const(a.block_table, (size_t)b * a.bt_stride + j);
+  const bool bad = page < 0 || page >= a.num_pages;
+  bad_page |= bad;
+  return PageCopy{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, bad ? 1 : min(kPage, Lc - j * kPage), buf};
+}
+
+// ===== wide split: more than 64 rows per workgroup =====================================
+// 32x32x16 MFMA tiles.  Wave w scores rows row0 + 32w .. +31 (one row tile) over the
+// page's two 32-token tiles, publishes P (bf16) through LDS, and accumulates O^T for
+// value columns 128w .. 128w + 127 of all four row tiles:
+//   o[dt][rt] lane l, index 4i + j:  column 128w + 32dt + 8i + 4(l/32) + j,  row row0 + 32rt + l%32.
+// P buffer (16 KB after the two page buffers): [K step ks 0..3][row tile 0..3][lane][8 bf16],
+// the B operand of O^T += V^T . P^T for tokens 16ks .. 16ks + 15.
+struct WideLane {
+  int k_base;   // K read: token (l % 32) of the value part
+  int k_rbase;  // K read: token (l % 32) of the rope part
+  int ky[4];    // K read chunk offsets for dims 16kk + 8(l/32): ((2(kk&3) + l/32) ^ swz) * 16
+  int v_base;   // V read: token 4(l/32) + (l%16)/4, byte 8(l&1)
+  int vy[2];    // V read chunk offsets for value tiles with dt even / odd
+};
+__device__ __forceinline__ WideLane wide_lane(int l, int w) {
+  WideLane o;
+  const int g = l >> 5, q = l >> 4, jj = l & 15;
+  const int sk = swz(l & 7);
+  o.k_base = (l & 31) * 1024;
+  o.k_rbase = kRopeOff + (l & 31) * 128;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o.ky[m] = ((2 * m + g) ^ sk) << 4;
+  const int vgz = ((jj >> 2) << 1) | g;               // swz of token 4g + jj/4 (+ multiples of 8)
+  o.v_base = (4 * g + (jj >> 2)) * 1024 + 8 * (jj & 1) + 256 * w;   // + 128 * (2w) for the slice
+#pragma unroll
+  for (int e = 0; e < 2; ++e) o.vy[e] = ((4 * e + 2 * (q & 1) + ((jj & 3) >> 1)) ^ vgz) << 4;
+  return o;
+}
+
+__device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
+                                                    int row0, int blk_lo, int blk_hi, int slot) {
+  const int w = wave_id(), l = threadIdx.x & 63;
+  const int g = l >> 5, lr = l & 31;
+  const int R = a.rows;
+  const int row_end = min(row0 + a.rows_per_wg, R);
+  const int myrow = row0 + 32 * w + lr;
+
+  const int L = ld_const(a.seqlens, b);
+  const bool bad_len = (L < 0) || ((int64_t)L > (int64_t)kPage * a.max_blocks);
+  const int Lc = bad_len ? 0 : L;
+  int nvis = Lc;
+  if (a.causal && a.q_len > 1) nvis = Lc - a.q_len + 1 + min(myrow, R - 1) / a.heads;
+  nvis = max(nvis, 0);
+  int nmin = Lc;  // fewest visible keys over the workgroup's rows: masking starts there
+  if (a.causal && a.q_len > 1) nmin = max(Lc - a.q_len + 1 + row0 / a.heads, 0);
+
+  // Q fragments (B operand of S^T = K Q^T): dims 16kk + 8g .. +8 of row myrow
+  bf16x8 qf[36];
+  {
+    const bool ok = myrow < row_end;
+    const bf16x8* src = (const bf16x8*)(a.q + ((size_t)b * R + (ok ? myrow : row0)) * kRowBytes) + g;
+#pragma unroll
+    for (int kk = 0; kk < 36; ++kk) {
+      const bf16x8 v = src[2 * kk];
+      qf[kk] = ok ? v : bf16x8{};
+    }
+  }
+  const WideLane wl = wide_lane(l, w);
+  MLA_LDS uint8_t* pbuf = lds + kPBufOff;
+
+  f32x16 o[4][4];
+  float m_ref = -INFINITY, mtrue = -INFINITY, lsum = 0.f;
+  bool over = false, bad_page = false;
+  float mref_init = -INFINITY;
+  for (int pass = 0; pass < 2; ++pass) {
+    m_ref = mref_init;
+    mtrue = -INFINITY;
+    lsum = 0.f;
+    over = false;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        o[dt][rt] = f32x16{};
+        asm volatile("" : "+a"(o[dt][rt]));
+      }
+
+    __syncthreads();  // LDS free (a previous segment or pass may still be reading it)
+    if (blk_lo < blk_hi) issue_block(a, b, blk_lo, Lc, lds, w, l, bad_page);
+    for (int j = blk_lo; j < blk_hi; ++j) {
+      const int it = j - blk_lo;
+      const MLA_LDS uint8_t* cur = lds + (it & 1) * kBlockBytes;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of page j have landed
+      __syncthreads();                // ... and every wave's; page j-1 (and its P) consumed
+      // Page j+1 streams into the other buffer while this page is computed: its 18 copies
+      // per wave are spread over the MFMA loops below (9 in S, 1 after softmax, 8 in P.V),
+      // so no wave stalls for long on a full memory queue with its matrix unit idle.
+      const bool pre = j + 1 < blk_hi;
+      PageCopy nxt{};
+      if (pre) nxt = page_copy(a, b, j + 1, Lc, lds + ((it + 1) & 1) * kBlockBytes, bad_page);
+
+      // ---- S^T: 2 token tiles x 32 rows x 576 dims ----------------------------------
+      f32x16 s0, s1;
+      {
+        auto load_k = [&](int kk, bf16x8& k0, bf16x8& k1) {
+          if (kk < 32) {
+            const MLA_LDS uint8_t* p = cur + wl.k_base + (kk >> 2) * 128 + wl.ky[kk & 3];
+            k0 = lds_read_b128(p);
+            k1 = lds_read_b128(p + 32 * 1024);
+          } else {
+            const MLA_LDS uint8_t* p = cur + wl.k_rbase + wl.ky[kk & 3];
+            k0 = lds_read_b128(p);
+            k1 = lds_read_b128(p + 32 * 128);
+          }
+        };
+        bf16x8 kr0[kPrefK + 1], kr1[kPrefK + 1];
+#pragma unroll
+        for (int kk = 0; kk < kPrefK; ++kk) load_k(kk, kr0[kk], kr1[kk]);
+#pragma unroll
+        for (int kk = 0; kk < 36; ++kk) {
+          if (pre && (kk & 3) == 1) issue_copy(nxt, kk >> 2, w, l);
+          if (kk + kPrefK < 36)
+            load_k(kk + kPrefK, kr0[(kk + kPrefK) % (kPrefK + 1)], kr1[(kk + kPrefK) % (kPrefK + 1)]);
+          mfma32_s_step(s0, s1, kr0[kk % (kPrefK + 1)], kr1[kk % (kPrefK + 1)], qf[kk], kk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- softmax of the wave's row myrow over the page's 64 keys -------------------
+      const bool need_mask = j * kPage + kPage > nmin;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t0 = 8 * (e >> 2) + 4 * g + (e & 3);          // token of s0[e] in the page
+        float x0 = s0[e] * a.scale_log2, x1 = s1[e] * a.scale_log2;
+        if (need_mask) {
+          x0 = (j * kPage + t0 < nvis) ? x0 : -INFINITY;
+          x1 = (j * kPage + 32 + t0 < nvis) ? x1 : -INFINITY;
+        }
+        s0[e] = x0;
+        s1[e] = x1;
+        mx = fmaxf(mx, fmaxf(x0, x1));
+      }
+      mx = wave_max_xor(mx, 32);
+      mtrue = fmaxf(mtrue, mx);
+      if (m_ref == -INFINITY) m_ref = mx;        // nothing accumulated yet: exact
+      over |= mx > m_ref + kRefSlack;
+      const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float rs = 0.f;
+      f32x16 p0, p1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p0[e] = __builtin_amdgcn_exp2f(s0[e] - msub);
+        p1[e] = __builtin_amdgcn_exp2f(s1[e] - msub);
+        rs += p0[e] + p1[e];
+      }
+      rs += __shfl_xor(rs, 32, 64);
+      lsum += rs;
+      // B operands per 16-token K step: ks -> tile ks/2, C indices 8(ks&1) .. +7
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x16& pt = (ks < 2) ? p0 : p1;
+        const int base = 8 * (ks & 1);
+        f32x4 lo4 = {pt[base + 0], pt[base + 1], pt[base + 2], pt[base + 3]};
+        f32x4 hi4 = {pt[base + 4], pt[base + 5], pt[base + 6], pt[base + 7]};
+        lds_write_b128(pbuf + ((ks * 4 + w) * 64 + l) * 16, cat8(to_bf16x4(lo4), to_bf16x4(hi4)));
+      }
+      if (pre) issue_copy(nxt, 17, w, l);
+      __syncthreads();  // every wave's P visible
+
+      // ---- O^T += V^T . P^T over the wave's 128 value columns, all 128 rows ----------
+      auto load_v = [&](int t) {   // t = 4 ks + dt
+        const int ks = t >> 2, dt = t & 3;
+        const MLA_LDS uint8_t* vp = cur + wl.v_base + ks * 16 * 1024 + (dt >> 1) * 128 + wl.vy[dt & 1];
+        return cat8(lds_read_tr(vp), lds_read_tr(vp + 8 * 1024));
+      };
+      bf16x8 vring[kPrefV + 1];
+#pragma unroll
+      for (int t = 0; t < kPrefV; ++t) vring[t] = load_v(t);
+      bf16x8 pf[4];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int ks = t >> 2, dt = t & 3;
+        if (dt == 0) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) pf[rt] = lds_read_b128(pbuf + ((ks * 4 + rt) * 64 + l) * 16);
+        }
+        if (pre && (t & 1) == 0) issue_copy(nxt, 9 + (t >> 1), w, l);
+        if (t + kPrefV < 16) vring[(t + kPrefV) % (kPrefV + 1)] = load_v(t + kPrefV);
+        mfma32_pv_step(o[dt], vring[t % (kPrefV + 1)], pf, t == 15);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the page buffers and P buffer are idle until the next pass starts
+    if (!wg_or(over, (MLA_LDS int*)pbuf)) break;
+    mref_init = mtrue;
+  }
+
+  // ---- epilogue: every wave needs the row statistics of all 128 rows ---------------------
+  const bool poison = bad_len || wg_or(bad_page, (MLA_LDS int*)pbuf);
+  if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
+  MLA_LDS float* stats = (MLA_LDS float*)pbuf;   // [row][m, lsum]
+  if (g == 0) {
+    stats[2 * (32 * w + lr)] = m_ref;
+    stats[2 * (32 * w + lr) + 1] = lsum;
+  }
+  __syncthreads();
+  const float nanv = __builtin_nanf("");
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = row0 + 32 * rt + lr;
+    if (r >= row_end) continue;
+    const float mr = stats[2 * (32 * rt + lr)];
+    const float ls = stats[2 * (32 * rt + lr) + 1];
+    const bool empty = ls == 0.f;   // no visible key; NaN propagates
+    const float scale_o = poison ? nanv : (empty ? 0.f : 1.f / ls);
+    const float lse_v = poison ? nanv : (empty ? -INFINITY : (mr + __log2f(ls)) * kLn2);
+    if (slot < 0) {
+      uint16_t* orow = a.out + ((size_t)b * R + r) * kDv + 128 * w + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& t = o[dt][rt];
+          const uint32_t lo2 = f32_to_bf16_rne(t[4 * i] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 1] * scale_o) << 16);
+          const uint32_t hi2 = f32_to_bf16_rne(t[4 * i + 2] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 3] * scale_o) << 16);
+          *(u32x2*)(orow + 32 * dt + 8 * i) = u32x2{lo2, hi2};
+        }
+      if (w == 0 && g == 0) a.lse[(size_t)b * R + r] = lse_v;
+    } else {
+      uint16_t* prow = a.ws_o + ((size_t)slot * a.rows_per_wg + (r - row0)) * kDv + 128 * w + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& t = o[dt][rt];
+          const uint32_t lo2 = f32_to_bf16_rne(t[4 * i] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 1] * scale_o) << 16);
+          const uint32_t hi2 = f32_to_bf16_rne(t[4 * i + 2] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 3] * scale_o) << 16);
+          *(u32x2*)(prow + 32 * dt + 8 * i) = u32x2{lo2, hi2};
+        }
+      if (w == 0 && g == 0) a.ws_lse[(size_t)slot * a.rows_per_wg + (r - row0)] = lse_v;
+    }
+  }
+}
+
+// ===== narrow split: at most 64 rows per workgroup =====================================
+// TG token groups x (4 / TG) row groups of 32 rows; each wave keeps O^T for its rows,
+// o[dt][nt] = columns 16dt + 4*(lane/16) + j of row rbase + 16nt + lane%16.
+struct NarrowState {
+  f32x4 o[32][2];
+  RowState r;
+};
+constexpr int kStateSlotFloats = (256 + 4) * 64;
+
+__device__ __forceinline__ void store_state(const NarrowState& st, MLA_LDS float* slot, int l) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) slot[((dt * 2 + nt) * 4 + j) * 64 + l] = st.o[dt][nt][j];
+    slot[256 * 64 + nt * 64 + l] = st.r.m[nt];
+    slot[256 * 64 + 128 + nt * 64 + l] = st.r.lsum[nt];
+  }
+}
+__device__ __forceinline__ void merge_state(NarrowState& st, const MLA_LDS float* slot, int l) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float mb = slot[256 * 64 + nt * 64 + l];
+    const float lb = slot[256 * 64 + 128 + nt * 64 + l];
+    const float mn = fmaxf(st.r.m[nt], mb);
+    const float ms = (mn == -INFINITY) ? 0.f : mn;
+    const float fa = __builtin_amdgcn_exp2f(st.r.m[nt] - ms), fb = __builtin_amdgcn_exp2f(mb - ms);
+    st.r.lsum[nt] = st.r.lsum[nt] * fa + lb * fb;
+    st.r.m[nt] = mn;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        st.o[dt][nt][j] = st.o[dt][nt][j] * fa + slot[((dt * 2 + nt) * 4 + j) * 64 + l] * fb;
+      pin_agpr(st.o[dt][nt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// One sub-block of NMT 16-token tiles at token tokA: scores, softmax, P.V for own rows.
+template <int NMT>
+__device__ __forceinline__ void narrow_sub_block(NarrowState& st, const bf16x8 (&qf)[2][18],
+                                                 const MLA_LDS uint8_t* cur, int tokA, const LaneOffsets& lo,
+                                                 bool need_mask, int pos0, const int (&nvis)[2],
+                                                 float scale_log2, int l) {
+  f32x4 s[NMT][2];
+  s_phase<NMT>(s, qf, cur, tokA, lo);
+  bf16x4 pb[NMT][2];
+  softmax_p<NMT>(st.r, s, pb, need_mask, pos0, nvis, scale_log2, l);
   if constexpr (NMT == 2) {
     bf16x8 pk[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) pk[nt] = cat8(pb[0][nt], pb[1][nt]);
-    auto load_v = [&](int dt) {
-      const MLA_LDS uint8_t* vp = vrow + (dt >> 2) * 128 + lo.vy[dt & 3];
-      return cat8(lds_read_tr(vp), lds_read_tr(vp + 16 * 1024));
-    };
     bf16x8 vring[kPrefV + 1];
 #pragma unroll
-    for (int dt = 0; dt < kPrefV; ++dt) vring[dt] = load_v(dt);
+    for (int dt = 0; dt < kPrefV; ++dt) vring[dt] = load_v32(cur, lo, tokA, dt);
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      if (dt + kPrefV < 32) vring[(dt + kPrefV) % (kPrefV + 1)] = load_v(dt + kPrefV);
-      const bf16x8 va = vring[dt % (kPrefV + 1)];
-      mfma_pv32(st.o[dt][0], st.o[dt][1], va, pk[0], pk[1], dt == 31);
+      if (dt + kPrefV < 32) vring[(dt + kPrefV) % (kPrefV + 1)] = load_v32(cur, lo, tokA, dt + kPrefV);
+      mfma_pv32(st.o[dt][0], st.o[dt][1], vring[dt % (kPrefV + 1)], pk[0], pk[1], dt == 31);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -357,7 +763,7 @@ __device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][1
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) pk[nt] = __builtin_bit_cast(s16x4, pb[0][nt]);
     auto load_v = [&](int dt) {
-      const MLA_LDS uint8_t* vp = vrow + (dt >> 2) * 128 + lo.vy[dt & 3];
+      const MLA_LDS uint8_t* vp = cur + lo.v_base + tokA * 1024 + (dt >> 2) * 128 + lo.vy[dt & 3];
       return __builtin_bit_cast(s16x4, lds_read_tr(vp));
     };
     s16x4 vring[kPrefV + 1];
@@ -366,124 +772,73 @@ __device__ __forceinline__ void sub_block(WaveState& st, const bf16x8 (&qf)[2][1
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
       if (dt + kPrefV < 32) vring[(dt + kPrefV) % (kPrefV + 1)] = load_v(dt + kPrefV);
-      const s16x4 va = vring[dt % (kPrefV + 1)];
-      mfma_pv16(st.o[dt][0], st.o[dt][1], va, pk[0], pk[1], dt == 31);
+      mfma_pv16(st.o[dt][0], st.o[dt][1], vring[dt % (kPrefV + 1)], pk[0], pk[1], dt == 31);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// One segment: rows [row0, row0 + rows_per_wg) of sequence b, blocks [blk_lo, blk_hi).
-// slot < 0: write out/lse directly; else write normalised partials to that slot.
 template <int TG>
-__device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
-                                               int row0, int blk_lo, int blk_hi, int slot) {
+__device__ __forceinline__ void decode_segment_narrow(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
+                                                      int row0, int blk_lo, int blk_hi, int slot) {
   constexpr int RG = 4 / TG;       // waves along rows
-  constexpr int WTOK = 64 / TG;    // tokens per wave per block
+  constexpr int WTOK = 64 / TG;    // tokens per wave per page
   const int w = wave_id(), l = threadIdx.x & 63;
   const int rg = w % RG, tg = w / RG;
   const int lq = l >> 4, li = l & 15;
   const int R = a.rows;
   const int row_end = min(row0 + a.rows_per_wg, R);
   const int rbase = row0 + 32 * rg;
+  const SegmentSetup ss = segment_setup(a, b, row0, rbase, li);
 
-  const int L = ld_const(a.seqlens, b);
-  const bool bad_len = (L < 0) || ((int64_t)L > (int64_t)kPage * a.max_blocks);
-  const int Lc = bad_len ? 0 : L;
-
-  int nvis[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = min(rbase + 16 * nt + li, R - 1);
-    int n = Lc;
-    if (a.causal && a.q_len > 1) n = Lc - a.q_len + 1 + r / a.heads;
-    nvis[nt] = max(n, 0);
-  }
-  // fewest visible keys over the workgroup's rows: masking starts at that position
-  int nmin = Lc;
-  if (a.causal && a.q_len > 1) nmin = max(Lc - a.q_len + 1 + row0 / a.heads, 0);
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][32*kk + 8*lq .. +8]
   bf16x8 qf[2][18];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = rbase + 16 * nt + li;
-    const bool ok = r < row_end;
-    const bf16x8* src = (const bf16x8*)(a.q + ((size_t)b * R + (ok ? r : row0)) * kRowBytes) + lq;
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      const bf16x8 v = src[4 * kk];
-      qf[nt][kk] = ok ? v : bf16x8{};
-    }
-  }
-
-  LaneOffsets lo;
-  lo.kx = lq ^ swz(li);
-  lo.k_v = li * 1024;
-  lo.k_r = kRopeOff + li * 128;
-  const int vg = (((li >> 2) & 3) << 1) | (lq & 1);   // swz of token 4*lq + li/4
-  lo.v_base = (4 * lq + (li >> 2)) * 1024 + 8 * (li & 1);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) lo.vy[d] = ((2 * d + ((li & 3) >> 1)) ^ vg) << 4;
+  load_q(a, b, rbase, row0, row_end, l, qf);
+  const LaneOffsets lo = lane_offsets(l);
   const int tok0 = WTOK * tg;
 
-  WaveState st;
+  NarrowState st;
   bool bad_page = false;
   float mref_init[2] = {-INFINITY, -INFINITY};
-  // Pass 0 fixes each row's reference max at its first visible keys.  Pass 1 runs only
-  // if some score outgrew that reference by more than 2^kRefSlack, and starts from the
-  // true running max seen in pass 0, which no score of the segment can exceed.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      st.m[nt] = mref_init[nt];
-      st.mtrue[nt] = -INFINITY;
-      st.lsum[nt] = 0.f;
+      st.r.m[nt] = mref_init[nt];
+      st.r.mtrue[nt] = -INFINITY;
+      st.r.lsum[nt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
         st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         pin_agpr(st.o[dt][nt]);
       }
     }
-    st.over = false;
+    st.r.over = false;
 
-    __syncthreads();  // LDS free (a previous segment or pass may still be reading it)
-    if (blk_lo < blk_hi) {
-      const int page = ld_const(a.block_table, (size_t)b * a.bt_stride + blk_lo);
-      const bool bad = page < 0 || page >= a.num_pages;
-      bad_page |= bad;
-      issue_page(a.kv, bad ? 0 : page, bad ? 1 : min(kPage, Lc - blk_lo * kPage), lds, w, l);
-    }
+    __syncthreads();
+    if (blk_lo < blk_hi) issue_block(a, b, blk_lo, ss.Lc, lds, w, l, bad_page);
     for (int j = blk_lo; j < blk_hi; ++j) {
       const int it = j - blk_lo;
       const MLA_LDS uint8_t* cur = lds + (it & 1) * kBlockBytes;
-      MLA_LDS uint8_t* nxt = lds + ((it + 1) & 1) * kBlockBytes;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block j have landed
-      __syncthreads();                // ... and every wave's; block j-1 fully consumed
-      if (j + 1 < blk_hi) {
-        const int page = ld_const(a.block_table, (size_t)b * a.bt_stride + j + 1);
-        const bool bad = page < 0 || page >= a.num_pages;
-        bad_page |= bad;
-        issue_page(a.kv, bad ? 0 : page, bad ? 1 : min(kPage, Lc - (j + 1) * kPage), nxt, w, l);
-      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (j + 1 < blk_hi) issue_block(a, b, j + 1, ss.Lc, lds + ((it + 1) & 1) * kBlockBytes, w, l, bad_page);
       if constexpr (WTOK >= 32) {
 #pragma unroll
         for (int sb = 0; sb < WTOK / 32; ++sb) {
           const int tokA = tok0 + 32 * sb;
           const int pos0 = j * kPage + tokA;
-          sub_block<2>(st, qf, cur, tokA, lo, pos0 + 32 > nmin, pos0, nvis, a.scale_log2, l);
+          narrow_sub_block<2>(st, qf, cur, tokA, lo, pos0 + 32 > ss.nmin, pos0, ss.nvis, a.scale_log2, l);
         }
       } else {
         const int pos0 = j * kPage + tok0;
-        sub_block<1>(st, qf, cur, tok0, lo, pos0 + 16 > nmin, pos0, nvis, a.scale_log2, l);
+        narrow_sub_block<1>(st, qf, cur, tok0, lo, pos0 + 16 > ss.nmin, pos0, ss.nvis, a.scale_log2, l);
       }
     }
-    if (!__syncthreads_or(st.over ? 1 : 0)) break;
+    if (!__syncthreads_or(st.r.over ? 1 : 0)) break;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) mref_init[nt] = st.mtrue[nt];
+    for (int nt = 0; nt < 2; ++nt) mref_init[nt] = st.r.mtrue[nt];
   }
 
-  // ---- merge token groups through LDS (the KV buffers are free once all waves pass) --
+  // merge token groups through LDS (the page buffers are free once all waves pass)
   if constexpr (TG > 1) {
     MLA_LDS float* slots = (MLA_LDS float*)lds;
 #pragma unroll
@@ -495,41 +850,47 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     }
   }
 
-  // ---- epilogue -----------------------------------------------------------------------
-  const bool poison = bad_len || __syncthreads_or(bad_page ? 1 : 0);
+  const bool poison = ss.bad_len || __syncthreads_or(bad_page ? 1 : 0);
   if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
   if (tg != 0) return;
+  const float nanv = __builtin_nanf("");
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int r = rbase + 16 * nt + li;
     if (r >= row_end) continue;
-    const float ls = st.lsum[nt];
+    const float ls = st.r.lsum[nt];
     const bool empty = ls == 0.f;   // no visible key; NaN propagates
-    const float nanv = __builtin_nanf("");
     const float scale_o = poison ? nanv : (empty ? 0.f : 1.f / ls);
-    const float lse_v = poison ? nanv : (empty ? -INFINITY : (st.m[nt] + __log2f(ls)) * kLn2);
+    const float lse_v = poison ? nanv : (empty ? -INFINITY : (st.r.m[nt] + __log2f(ls)) * kLn2);
     if (slot < 0) {
       uint16_t* orow = a.out + ((size_t)b * R + r) * kDv + 4 * lq;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
-        const f32x4 o = st.o[dt][nt] * scale_o;
-        const uint32_t lo2 = f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-        const uint32_t hi2 = f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+        const f32x4 v = st.o[dt][nt] * scale_o;
+        const uint32_t lo2 = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi2 = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
         *(u32x2*)(orow + 16 * dt) = u32x2{lo2, hi2};
       }
       if (lq == 0) a.lse[(size_t)b * R + r] = lse_v;
     } else {
-      float* prow = a.ws_o + ((size_t)slot * a.rows_per_wg + (r - row0)) * kDv + 4 * lq;
+      uint16_t* prow = a.ws_o + ((size_t)slot * a.rows_per_wg + (r - row0)) * kDv + 4 * lq;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) *(f32x4*)(prow + 16 * dt) = st.o[dt][nt] * scale_o;
+      for (int dt = 0; dt < 32; ++dt) {
+        const f32x4 v = st.o[dt][nt] * scale_o;
+        const uint32_t lo2 = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi2 = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *(u32x2*)(prow + 16 * dt) = u32x2{lo2, hi2};
+      }
       if (lq == 0) a.ws_lse[(size_t)slot * a.rows_per_wg + (r - row0)] = lse_v;
     }
   }
 }
 
+// ===== kernel ==========================================================================
+// TG = 1: wide split (rows_per_wg > 64); TG = 2, 4: narrow split.
 template <int TG>
 __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[2 * kBlockBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[TG == 1 ? kLdsBytes : 2 * kBlockBytes];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)lds_raw;
   const bool planned = a.meta != nullptr;
   MetaView v = meta_view(a.meta, a.batch, a.row_split);
@@ -572,7 +933,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
       slot = -1;
       pos = end;
     }
-    decode_segment<TG>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    if constexpr (TG == 1)
+      decode_segment_wide(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    else
+      decode_segment_narrow<TG>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
   }
 }
 

@@ -90,9 +90,9 @@ def test_plan_sizes_and_workspace_checks():
     # header + cu_blocks[B+1] + 3 per unit + wg_begin[grid+1] int32 words
     assert mb == 4 * (16 + 5 + 3 * 4 + 257)
     # partial slots: grid + min(grid, units), each rows_per_wg * (512 + 1) floats
-    assert wb == (256 + 4) * 128 * 513 * 4
+    assert wb == (256 + 4) * 128 * (512 * 2 + 4)   # bf16 partial rows + fp32 LSE
     opts = m.PlanOptions(num_workgroups=8, min_blocks_per_wg=1, row_split=2)
-    assert m.workspace_bytes(p, opts, 256) == (8 + 8) * 64 * 513 * 4
+    assert m.workspace_bytes(p, opts, 256) == (8 + 8) * 64 * (512 * 2 + 4)
     assert m.workspace_bytes(p, m.PlanOptions(row_split=3), 256) == 0  # unsupported split
     L = m.lib()
     a = ctypes.c_void_p(0x10000)
