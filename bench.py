@@ -89,8 +89,8 @@ def cpu_baseline(case, flops):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default: the headline one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--num-workgroups", type=int, default=0)

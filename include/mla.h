@@ -79,7 +79,7 @@ typedef enum {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL = 1,         /* a required pointer is NULL */
-  MLA_ERR_SHAPE = 2,        /* a size is out of range */
+  MLA_ERR_SHAPE = 2,        /* a size (or the scale) is out of range */
   MLA_ERR_DTYPE = 3,        /* unknown dtype */
   MLA_ERR_ALIGN = 4,        /* a pointer is not aligned as required */
   MLA_ERR_WORKSPACE = 5,    /* metadata or workspace buffer too small */
@@ -162,7 +162,8 @@ MLA_API int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* ca
 /*
  * Decode.  Argument order follows the problem statement
  * (q, kv_cache, block_table, cache_seqlens, scale, out, lse, ..., stream).
- *   scale      multiplies every q . k (e.g. 192^-0.5)
+ *   scale      multiplies every q . k (e.g. 192^-0.5); must be positive and finite
+ *              (MLA_ERR_SHAPE otherwise)
  *   plan       from mla_get_metadata for the same problem and cache_seqlens, or
  *              NULL: one workgroup per sequence, no splits, no workspace needed
  *   workspace  device buffer of >= mla_workspace_bytes (unused when plan is NULL)

@@ -165,6 +165,8 @@ int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* 
   a->out = static_cast<uint16_t*>(out);
   a->lse = lse;
   a->scale_log2 = scale * mla::kLog2e;
+  // the kernels take the row max on unscaled scores: the scale must be positive
+  if (!(scale > 0.f) || !(a->scale_log2 <= 3.0e38f)) return MLA_ERR_SHAPE;
   a->batch = p.batch;
   a->rows = p.q_len * p.num_heads;
   a->q_len = p.q_len;

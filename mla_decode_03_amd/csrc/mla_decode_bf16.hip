@@ -449,11 +449,10 @@ __device__ __forceinline__ void issue_block(const DecodeArgs& a, int b, int j, i
   bad_page |= bad;
   issue_page(a.kv, bad ? 0 : page, bad ? 1 : min(kPage, Lc - j * kPage), buf, w, l);
 }
-// Page j's copy description, checking the page index (a bad index reads page 0 and
-// poisons the segment).
-__device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int b, int j, int Lc, MLA_LDS uint8_t* buf,
+// Copy description of page j (pool index `page`), checking the index (a bad index reads
+// page 0 and poisons the segment).
+__device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int j, int Lc, MLA_LDS uint8_t* buf,
                                               bool& bad_page) {
-  const int page = ld_const(a.block_table, (size_t)b * a.bt_stride + j);
   const bool bad = page < 0 || page >= a.num_pages;
   bad_page |= bad;
   return PageCopy{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, bad ? 1 : min(kPage, Lc - j * kPage), buf};
@@ -466,26 +465,74 @@ __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int b, int j,
 //   o[dt][rt] lane l, index 4i + j:  column 128w + 32dt + 8i + 4(l/32) + j,  row row0 + 32rt + l%32.
 // P buffer (16 KB after the two page buffers): [K step ks 0..3][row tile 0..3][lane][8 bf16],
 // the B operand of O^T += V^T . P^T for tokens 16ks .. 16ks + 15.
+// The wide split stores a page as 9 column blocks (dims 64c .. 64c + 63 of all 64
+// tokens, 8 KB each, the rope block last): token t, 16-byte chunk p of block c at
+// c*8192 + t*128 + (p ^ swz(t))*16.  The score loop walks the dims in block order, so it
+// can start on a page once its first blocks have landed.
+constexpr int kColBlock = 8192;
 struct WideLane {
-  int k_base;   // K read: token (l % 32) of the value part
-  int k_rbase;  // K read: token (l % 32) of the rope part
+  int k_base;   // K read: token (l % 32)
   int ky[4];    // K read chunk offsets for dims 16kk + 8(l/32): ((2(kk&3) + l/32) ^ swz) * 16
-  int v_base;   // V read: token 4(l/32) + (l%16)/4, byte 8(l&1)
+  int v_base;   // V read: token 4(l/32) + (l%16)/4, byte 8(l&1), the wave's first block
   int vy[2];    // V read chunk offsets for value tiles with dt even / odd
 };
 __device__ __forceinline__ WideLane wide_lane(int l, int w) {
   WideLane o;
   const int g = l >> 5, q = l >> 4, jj = l & 15;
   const int sk = swz(l & 7);
-  o.k_base = (l & 31) * 1024;
-  o.k_rbase = kRopeOff + (l & 31) * 128;
+  o.k_base = (l & 31) * 128;
 #pragma unroll
   for (int m = 0; m < 4; ++m) o.ky[m] = ((2 * m + g) ^ sk) << 4;
   const int vgz = ((jj >> 2) << 1) | g;               // swz of token 4g + jj/4 (+ multiples of 8)
-  o.v_base = (4 * g + (jj >> 2)) * 1024 + 8 * (jj & 1) + 256 * w;   // + 128 * (2w) for the slice
+  o.v_base = (4 * g + (jj >> 2)) * 128 + 8 * (jj & 1) + 2 * w * kColBlock;
 #pragma unroll
   for (int e = 0; e < 2; ++e) o.vy[e] = ((4 * e + 2 * (q & 1) + ((jj & 3) >> 1)) ^ vgz) << 4;
   return o;
+}
+// Copy i (0..17) of this wave's share of a page in the column-block layout: block i/2,
+// tokens 8k .. 8k + 7 with k = 2w + (i & 1); lane l brings chunk (l&7) ^ swz(t) of token
+// t = 8k + l/8.  Copies go out in block order, two per wave per block.
+__device__ __forceinline__ void issue_col_copy(const PageCopy& c, int i, int w, int l) {
+  const int cb = i >> 1, k = 2 * w + (i & 1);
+  const int t = 8 * k + (l >> 3);
+  const int te = (t < c.valid) ? t : 0;
+  dma16(c.base, (uint32_t)(te * kRowBytes + cb * 128 + (((l & 7) ^ swz(t)) << 4)),
+        c.buf + cb * kColBlock + k * 1024);
+}
+// Where the next page's 18 copies (per wave, in copy order) go inside one page's
+// compute.  Score loop: the block-group waits cut the 36 steps into 5 windows; each
+// window carries 2 copies per wave, wave w issuing its copies w steps after the window's
+// copy slots, so the four waves do not queue their copies behind each other at the
+// same step (every wave still issues the same copies before each wait, which keeps the
+// wait counts compile-time).  Then kCopySm after the softmax and the rest spread over
+// the 16 P.V steps.
+constexpr int kCopyS = 10, kCopySm = 2;
+constexpr int kCopyPV = 18 - kCopyS - kCopySm;
+static_assert(kCopyPV >= 0 && kCopyPV <= 16, "copy schedule");
+constexpr int win_start(int W) { return W == 0 ? 0 : 8 * W - kPrefK; }
+constexpr int win_end(int W) { return W == 4 ? 36 : 8 * (W + 1) - kPrefK; }
+constexpr int win_of(int kk) { return kk < win_start(1) ? 0 : kk < win_start(2) ? 1 : kk < win_start(3) ? 2 : kk < win_start(4) ? 3 : 4; }
+constexpr int win_slot1(int W) { return win_end(W) - win_start(W) - 4; }   // second slot's offset
+static_assert(win_slot1(0) >= 1 && win_slot1(4) >= 1, "windows too short to stagger");
+// Copies this wave issued in the score loop before step kk (kk a window start).
+constexpr int s_copies_before(int kk) { return 2 * win_of(kk); }
+// This page's copies issued after block group G (blocks 2G, 2G+1; G = 4: the rope block).
+constexpr int copies_after_group(int G) { return G < 4 ? 14 - 4 * G : 0; }
+// Wait until this wave's copies of the current page up to a block group have landed,
+// then meet the other waves (their copies of those blocks have landed too).  N = copies
+// this wave issued after that group (they may still be in flight; loads complete in
+// order): the page's later groups plus the next page's copies issued so far.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+  __syncthreads();
+}
+template <int G>
+__device__ __forceinline__ void wait_group(bool pre) {
+  constexpr int kk = 8 * G - kPrefK;   // the step that first loads block 2G
+  if (pre) wait_vm_barrier<copies_after_group(G) + s_copies_before(kk)>();
+  else wait_vm_barrier<copies_after_group(G)>();
 }
 
 __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
@@ -537,62 +584,76 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       }
 
     __syncthreads();  // LDS free (a previous segment or pass may still be reading it)
-    if (blk_lo < blk_hi) issue_block(a, b, blk_lo, Lc, lds, w, l, bad_page);
+    const int* bt_row = a.block_table + (size_t)b * a.bt_stride;
+    if (blk_lo < blk_hi) {
+      const PageCopy first = page_copy(a, ld_const(bt_row, blk_lo), blk_lo, Lc, lds, bad_page);
+#pragma unroll
+      for (int i = 0; i < 18; ++i) issue_col_copy(first, i, w, l);
+    }
+    int pg_ahead = (blk_lo + 1 < blk_hi) ? ld_const(bt_row, blk_lo + 1) : 0;   // page j+1's index
     for (int j = blk_lo; j < blk_hi; ++j) {
       const int it = j - blk_lo;
       const MLA_LDS uint8_t* cur = lds + (it & 1) * kBlockBytes;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of page j have landed
-      __syncthreads();                // ... and every wave's; page j-1 (and its P) consumed
+      // blocks 0-1 of page j have landed (all waves); page j-1 and its P are consumed
+      wait_vm_barrier<14>();
       // Page j+1 streams into the other buffer while this page is computed: its 18 copies
-      // per wave are spread over the MFMA loops below (9 in S, 1 after softmax, 8 in P.V),
-      // so no wave stalls for long on a full memory queue with its matrix unit idle.
+      // per wave go out in block order, spread over the MFMA loops below (the copy
+      // schedule above; the waits in S count on it),
+      // so no wave stalls for long on a full memory queue with its matrix unit idle, and
+      // the later blocks of page j are waited for only where S reaches them.
       const bool pre = j + 1 < blk_hi;
       PageCopy nxt{};
-      if (pre) nxt = page_copy(a, b, j + 1, Lc, lds + ((it + 1) & 1) * kBlockBytes, bad_page);
+      if (pre) nxt = page_copy(a, pg_ahead, j + 1, Lc, lds + ((it + 1) & 1) * kBlockBytes, bad_page);
+      pg_ahead = (j + 2 < blk_hi) ? ld_const(bt_row, j + 2) : 0;   // read a page ahead
 
       // ---- S^T: 2 token tiles x 32 rows x 576 dims ----------------------------------
       f32x16 s0, s1;
       {
         auto load_k = [&](int kk, bf16x8& k0, bf16x8& k1) {
-          if (kk < 32) {
-            const MLA_LDS uint8_t* p = cur + wl.k_base + (kk >> 2) * 128 + wl.ky[kk & 3];
-            k0 = lds_read_b128(p);
-            k1 = lds_read_b128(p + 32 * 1024);
-          } else {
-            const MLA_LDS uint8_t* p = cur + wl.k_rbase + wl.ky[kk & 3];
-            k0 = lds_read_b128(p);
-            k1 = lds_read_b128(p + 32 * 128);
-          }
+          const MLA_LDS uint8_t* p = cur + (kk >> 2) * kColBlock + wl.k_base + wl.ky[kk & 3];
+          k0 = lds_read_b128(p);
+          k1 = lds_read_b128(p + 32 * 128);
         };
         bf16x8 kr0[kPrefK + 1], kr1[kPrefK + 1];
 #pragma unroll
         for (int kk = 0; kk < kPrefK; ++kk) load_k(kk, kr0[kk], kr1[kk]);
 #pragma unroll
         for (int kk = 0; kk < 36; ++kk) {
-          if (pre && (kk & 3) == 1) issue_copy(nxt, kk >> 2, w, l);
-          if (kk + kPrefK < 36)
-            load_k(kk + kPrefK, kr0[(kk + kPrefK) % (kPrefK + 1)], kr1[(kk + kPrefK) % (kPrefK + 1)]);
+          // before the first read of blocks 2G, 2G+1: wait for them
+          const int kl = kk + kPrefK;
+          if (kl == 8) wait_group<1>(pre);
+          if (kl == 16) wait_group<2>(pre);
+          if (kl == 24) wait_group<3>(pre);
+          if (kl == 32) wait_group<4>(pre);
+          if (pre) {
+            const int W = win_of(kk), d = kk - win_start(W);
+            if (d < 4 && w == d) issue_col_copy(nxt, 2 * W, w, l);
+            if (d >= win_slot1(W) && d < win_slot1(W) + 4 && w == d - win_slot1(W)) issue_col_copy(nxt, 2 * W + 1, w, l);
+          }
+          if (kl < 36)
+            load_k(kl, kr0[kl % (kPrefK + 1)], kr1[kl % (kPrefK + 1)]);
           mfma32_s_step(s0, s1, kr0[kk % (kPrefK + 1)], kr1[kk % (kPrefK + 1)], qf[kk], kk);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
       // ---- softmax of the wave's row myrow over the page's 64 keys -------------------
-      const bool need_mask = j * kPage + kPage > nmin;
-      float mx = -INFINITY;
+      // Scores stay unscaled (scale > 0 commutes with max); the scale is folded into the
+      // exponent's FMA below.  Only a sequence's last pages (or causal rows) mask.
+      if (j * kPage + kPage > nmin) {
+        asm volatile("");   // keep this a branch: the full pages skip it
+        const int lim = nvis - j * kPage;                        // visible tokens of the page
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t0 = 8 * (e >> 2) + 4 * g + (e & 3);          // token of s0[e] in the page
-        float x0 = s0[e] * a.scale_log2, x1 = s1[e] * a.scale_log2;
-        if (need_mask) {
-          x0 = (j * kPage + t0 < nvis) ? x0 : -INFINITY;
-          x1 = (j * kPage + 32 + t0 < nvis) ? x1 : -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int t0 = 8 * (e >> 2) + 4 * g + (e & 3);          // token of s0[e] in the page
+          s0[e] = (t0 < lim) ? s0[e] : -INFINITY;
+          s1[e] = (t0 + 32 < lim) ? s1[e] : -INFINITY;
         }
-        s0[e] = x0;
-        s1[e] = x1;
-        mx = fmaxf(mx, fmaxf(x0, x1));
       }
-      mx = wave_max_xor(mx, 32);
+      float mr = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mr = fmaxf(mr, fmaxf(s0[e], s1[e]));
+      const float mx = wave_max_xor(mr, 32) * a.scale_log2;
       mtrue = fmaxf(mtrue, mx);
       if (m_ref == -INFINITY) m_ref = mx;        // nothing accumulated yet: exact
       over |= mx > m_ref + kRefSlack;
@@ -601,8 +662,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       f32x16 p0, p1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p0[e] = __builtin_amdgcn_exp2f(s0[e] - msub);
-        p1[e] = __builtin_amdgcn_exp2f(s1[e] - msub);
+        p0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], a.scale_log2, -msub));
+        p1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], a.scale_log2, -msub));
         rs += p0[e] + p1[e];
       }
       rs += __shfl_xor(rs, 32, 64);
@@ -616,14 +677,17 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         f32x4 hi4 = {pt[base + 4], pt[base + 5], pt[base + 6], pt[base + 7]};
         lds_write_b128(pbuf + ((ks * 4 + w) * 64 + l) * 16, cat8(to_bf16x4(lo4), to_bf16x4(hi4)));
       }
-      if (pre) issue_copy(nxt, 17, w, l);
+      if (pre) {
+#pragma unroll
+        for (int i = 0; i < kCopySm; ++i) issue_col_copy(nxt, kCopyS + i, w, l);
+      }
       __syncthreads();  // every wave's P visible
 
       // ---- O^T += V^T . P^T over the wave's 128 value columns, all 128 rows ----------
       auto load_v = [&](int t) {   // t = 4 ks + dt
         const int ks = t >> 2, dt = t & 3;
-        const MLA_LDS uint8_t* vp = cur + wl.v_base + ks * 16 * 1024 + (dt >> 1) * 128 + wl.vy[dt & 1];
-        return cat8(lds_read_tr(vp), lds_read_tr(vp + 8 * 1024));
+        const MLA_LDS uint8_t* vp = cur + wl.v_base + ks * 16 * 128 + (dt >> 1) * kColBlock + wl.vy[dt & 1];
+        return cat8(lds_read_tr(vp), lds_read_tr(vp + 8 * 128));
       };
       bf16x8 vring[kPrefV + 1];
 #pragma unroll
@@ -636,7 +700,11 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) pf[rt] = lds_read_b128(pbuf + ((ks * 4 + rt) * 64 + l) * 16);
         }
-        if (pre && (t & 1) == 0) issue_copy(nxt, 9 + (t >> 1), w, l);
+        if (pre) {
+#pragma unroll
+          for (int i = 0; i < kCopyPV; ++i)
+            if (i * 16 / kCopyPV == t) issue_col_copy(nxt, kCopyS + kCopySm + i, w, l);
+        }
         if (t + kPrefV < 16) vring[(t + kPrefV) % (kPrefV + 1)] = load_v(t + kPrefV);
         mfma32_pv_step(o[dt], vring[t % (kPrefV + 1)], pf, t == 15);
         __builtin_amdgcn_sched_barrier(0);

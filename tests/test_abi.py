@@ -114,6 +114,10 @@ def test_plan_sizes_and_workspace_checks():
                        max_partials=260, batch=5, rows=128)
     assert L.mla_decode(ctypes.byref(p), a, a, a, a, 1.0, a, a, ctypes.byref(other), a, wb,
                         None) == _abi.MLA_ERR_SHAPE
+    # the scale must be positive and finite (checked before any launch)
+    for bad in (0.0, -0.5, float("inf"), float("nan"), 3e38):
+        assert L.mla_decode(ctypes.byref(p), a, a, a, a, bad, a, a, ctypes.byref(good), a, wb,
+                            None) == _abi.MLA_ERR_SHAPE, bad
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
