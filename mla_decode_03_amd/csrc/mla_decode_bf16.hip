@@ -467,36 +467,45 @@ __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int
 // the B operand of O^T += V^T . P^T for tokens 16ks .. 16ks + 15.
 // The wide split stores a page as 9 column blocks (dims 64c .. 64c + 63 of all 64
 // tokens, 8 KB each, the rope block last): token t, 16-byte chunk p of block c at
-// c*8192 + t*128 + (p ^ swz(t))*16.  The score loop walks the dims in block order, so it
+// c*8192 + t*128 + (p ^ cswz(t))*16.  The score loop walks the dims in block order, so it
 // can start on a page once its first blocks have landed.
 constexpr int kColBlock = 8192;
+// Chunk swizzle of the column-block layout.  gfx950 LDS serves 256 bytes per cycle, so a
+// 16-lane quarter of a 128-bit read is conflict-free when its 16 slots are distinct
+// modulo 256 B.  K reads (16 consecutive tokens, one chunk; rows 128 B apart, so the
+// token's low bit picks the 128-B half) need cswz(2i) and cswz(2i+1) to be permutations
+// of 0..7; the transposing V reads (4 consecutive tokens x one aligned group of 4 chunks)
+// need cswz(t) ^ cswz(t+2) to flip bit 2.  Both hold for:
+__device__ __forceinline__ int cswz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 struct WideLane {
   int k_base;   // K read: token (l % 32)
   int ky[4];    // K read chunk offsets for dims 16kk + 8(l/32): ((2(kk&3) + l/32) ^ swz) * 16
   int v_base;   // V read: token 4(l/32) + (l%16)/4, byte 8(l&1), the wave's first block
-  int vy[2];    // V read chunk offsets for value tiles with dt even / odd
+  int vy[2][2]; // V read chunk offsets [dt odd][second read: token + 8]
 };
 __device__ __forceinline__ WideLane wide_lane(int l, int w) {
   WideLane o;
   const int g = l >> 5, q = l >> 4, jj = l & 15;
-  const int sk = swz(l & 7);
+  const int sk = cswz(l & 31);                        // tokens l%32 and l%32 + 32 alike
   o.k_base = (l & 31) * 128;
 #pragma unroll
   for (int m = 0; m < 4; ++m) o.ky[m] = ((2 * m + g) ^ sk) << 4;
-  const int vgz = ((jj >> 2) << 1) | g;               // swz of token 4g + jj/4 (+ multiples of 8)
-  o.v_base = (4 * g + (jj >> 2)) * 128 + 8 * (jj & 1) + 2 * w * kColBlock;
+  const int tv = 4 * g + (jj >> 2);                   // V token (+ 16 ks; + 8 for the second read)
+  o.v_base = tv * 128 + 8 * (jj & 1) + 2 * w * kColBlock;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) o.vy[e] = ((4 * e + 2 * (q & 1) + ((jj & 3) >> 1)) ^ vgz) << 4;
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) o.vy[e][r] = ((4 * e + 2 * (q & 1) + ((jj & 3) >> 1)) ^ cswz(tv + 8 * r)) << 4;
   return o;
 }
 // Copy i (0..17) of this wave's share of a page in the column-block layout: block i/2,
-// tokens 8k .. 8k + 7 with k = 2w + (i & 1); lane l brings chunk (l&7) ^ swz(t) of token
+// tokens 8k .. 8k + 7 with k = 2w + (i & 1); lane l brings chunk (l&7) ^ cswz(t) of token
 // t = 8k + l/8.  Copies go out in block order, two per wave per block.
 __device__ __forceinline__ void issue_col_copy(const PageCopy& c, int i, int w, int l) {
   const int cb = i >> 1, k = 2 * w + (i & 1);
   const int t = 8 * k + (l >> 3);
   const int te = (t < c.valid) ? t : 0;
-  dma16(c.base, (uint32_t)(te * kRowBytes + cb * 128 + (((l & 7) ^ swz(t)) << 4)),
+  dma16(c.base, (uint32_t)(te * kRowBytes + cb * 128 + (((l & 7) ^ cswz(t)) << 4)),
         c.buf + cb * kColBlock + k * 1024);
 }
 // Where the next page's 18 copies (per wave, in copy order) go inside one page's
@@ -686,8 +695,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       // ---- O^T += V^T . P^T over the wave's 128 value columns, all 128 rows ----------
       auto load_v = [&](int t) {   // t = 4 ks + dt
         const int ks = t >> 2, dt = t & 3;
-        const MLA_LDS uint8_t* vp = cur + wl.v_base + ks * 16 * 128 + (dt >> 1) * kColBlock + wl.vy[dt & 1];
-        return cat8(lds_read_tr(vp), lds_read_tr(vp + 8 * 128));
+        const MLA_LDS uint8_t* vp = cur + wl.v_base + ks * 16 * 128 + (dt >> 1) * kColBlock;
+        return cat8(lds_read_tr(vp + wl.vy[dt & 1][0]), lds_read_tr(vp + 8 * 128 + wl.vy[dt & 1][1]));
       };
       bf16x8 vring[kPrefV + 1];
 #pragma unroll
