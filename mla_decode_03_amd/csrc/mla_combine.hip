@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    packed[i] = f32_to_bf16_rne(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
+    packed[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   *(u32x4*)orow = u32x4{packed[0], packed[1], packed[2], packed[3]};
   *(u32x4*)(orow + 8) = u32x4{packed[4], packed[5], packed[6], packed[7]};
   if (t == 0) a.lse[(size_t)b * a.rows + r] = empty ? -INFINITY : Ms + logf(tot);

@@ -561,14 +561,30 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   int nmin = Lc;  // fewest visible keys over the workgroup's rows: masking starts there
   if (a.causal && a.q_len > 1) nmin = max(Lc - a.q_len + 1 + row0 / a.heads, 0);
 
-  // Q fragments (B operand of S^T = K Q^T): dims 16kk + 8g .. +8 of row myrow
+  // Q fragments (B operand of S^T = K Q^T): dims 16kk + 8g .. +8 of row myrow.  The
+  // workgroup's rows are contiguous in q, so they come in as (up to) two 64-row "pages"
+  // through the page buffers, with the KV pages' column-block copies (whole 128-byte
+  // lines per copy); each wave then reads its 32 rows' fragments.
   bf16x8 qf[36];
   {
+    const int nq = row_end - row0;
+    __syncthreads();   // LDS free (a previous segment may still be reading it)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (64 * h < nq) {
+        const PageCopy qc{a.q + ((size_t)b * R + row0 + 64 * h) * kRowBytes, min(64, nq - 64 * h),
+                          lds + h * kBlockBytes};
+#pragma unroll
+        for (int i = 0; i < 18; ++i) issue_col_copy(qc, i, w, l);
+      }
+    wait_vm_barrier<0>();
+    const int rr = (32 * w + lr) & 63;                        // row within its 64-row half
+    const MLA_LDS uint8_t* qb = lds + (w >> 1) * kBlockBytes + rr * 128;
+    const int sq = cswz(rr);
     const bool ok = myrow < row_end;
-    const bf16x8* src = (const bf16x8*)(a.q + ((size_t)b * R + (ok ? myrow : row0)) * kRowBytes) + g;
 #pragma unroll
     for (int kk = 0; kk < 36; ++kk) {
-      const bf16x8 v = src[2 * kk];
+      const bf16x8 v = lds_read_b128(qb + (kk >> 2) * kColBlock + (((2 * (kk & 3) + g) ^ sq) << 4));
       qf[kk] = ok ? v : bf16x8{};
     }
   }
@@ -734,40 +750,43 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   }
   __syncthreads();
   const float nanv = __builtin_nanf("");
+  // O (normalised, bf16) goes through LDS so that every store writes a whole 1 KB row:
+  // row rr of the workgroup at rr*1024, 16-byte chunk c (values 8c .. 8c+7) at
+  // (c ^ (rr & 15))*16.  The page buffers are idle now.
+  MLA_LDS uint8_t* ob = lds;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const int r = row0 + 32 * rt + lr;
-    if (r >= row_end) continue;
-    const float mr = stats[2 * (32 * rt + lr)];
-    const float ls = stats[2 * (32 * rt + lr) + 1];
+    const int rr = 32 * rt + lr;
+    const float ls = stats[2 * rr + 1];
     const bool empty = ls == 0.f;   // no visible key; NaN propagates
     const float scale_o = poison ? nanv : (empty ? 0.f : 1.f / ls);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x16& t = o[dt][rt];
+        const uint32_t lo2 = pack_bf16x2(t[4 * i] * scale_o, t[4 * i + 1] * scale_o);
+        const uint32_t hi2 = pack_bf16x2(t[4 * i + 2] * scale_o, t[4 * i + 3] * scale_o);
+        const int c = 16 * w + 4 * dt + i;
+        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g) = u32x2{lo2, hi2};
+      }
+  }
+  __syncthreads();
+  for (int k = 0; k < 32; ++k) {                  // the wave's rows 32w .. 32w+31
+    const int rr = 32 * w + k;
+    if (row0 + rr >= row_end) break;              // uniform
+    const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l ^ (rr & 15)) << 4));
+    uint16_t* dst = (slot < 0) ? a.out + ((size_t)b * R + row0 + rr) * kDv
+                               : a.ws_o + ((size_t)slot * a.rows_per_wg + rr) * kDv;
+    *(u32x4*)(dst + 8 * l) = v;
+  }
+  if (threadIdx.x < 128 && row0 + (int)threadIdx.x < row_end) {
+    const int rr = threadIdx.x;
+    const float mr = stats[2 * rr], ls = stats[2 * rr + 1];
+    const bool empty = ls == 0.f;
     const float lse_v = poison ? nanv : (empty ? -INFINITY : (mr + __log2f(ls)) * kLn2);
-    if (slot < 0) {
-      uint16_t* orow = a.out + ((size_t)b * R + r) * kDv + 128 * w + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x16& t = o[dt][rt];
-          const uint32_t lo2 = f32_to_bf16_rne(t[4 * i] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 1] * scale_o) << 16);
-          const uint32_t hi2 = f32_to_bf16_rne(t[4 * i + 2] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 3] * scale_o) << 16);
-          *(u32x2*)(orow + 32 * dt + 8 * i) = u32x2{lo2, hi2};
-        }
-      if (w == 0 && g == 0) a.lse[(size_t)b * R + r] = lse_v;
-    } else {
-      uint16_t* prow = a.ws_o + ((size_t)slot * a.rows_per_wg + (r - row0)) * kDv + 128 * w + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x16& t = o[dt][rt];
-          const uint32_t lo2 = f32_to_bf16_rne(t[4 * i] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 1] * scale_o) << 16);
-          const uint32_t hi2 = f32_to_bf16_rne(t[4 * i + 2] * scale_o) | ((uint32_t)f32_to_bf16_rne(t[4 * i + 3] * scale_o) << 16);
-          *(u32x2*)(prow + 32 * dt + 8 * i) = u32x2{lo2, hi2};
-        }
-      if (w == 0 && g == 0) a.ws_lse[(size_t)slot * a.rows_per_wg + (r - row0)] = lse_v;
-    }
+    if (slot < 0) a.lse[(size_t)b * R + row0 + rr] = lse_v;
+    else a.ws_lse[(size_t)slot * a.rows_per_wg + rr] = lse_v;
   }
 }
 
@@ -944,8 +963,8 @@ __device__ __forceinline__ void decode_segment_narrow(const DecodeArgs& a, MLA_L
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
         const f32x4 v = st.o[dt][nt] * scale_o;
-        const uint32_t lo2 = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        const uint32_t hi2 = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        const uint32_t lo2 = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi2 = pack_bf16x2(v[2], v[3]);
         *(u32x2*)(orow + 16 * dt) = u32x2{lo2, hi2};
       }
       if (lq == 0) a.lse[(size_t)b * R + r] = lse_v;
@@ -954,8 +973,8 @@ __device__ __forceinline__ void decode_segment_narrow(const DecodeArgs& a, MLA_L
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
         const f32x4 v = st.o[dt][nt] * scale_o;
-        const uint32_t lo2 = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        const uint32_t hi2 = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        const uint32_t lo2 = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi2 = pack_bf16x2(v[2], v[3]);
         *(u32x2*)(prow + 16 * dt) = u32x2{lo2, hi2};
       }
       if (lq == 0) a.ws_lse[(size_t)slot * a.rows_per_wg + (r - row0)] = lse_v;

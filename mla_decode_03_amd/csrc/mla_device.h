@@ -85,11 +85,12 @@ __device__ inline float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats -> a packed bf16 pair (lo in bits 0-15), round to nearest even, NaN kept
+// NaN: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 }  // namespace mla
