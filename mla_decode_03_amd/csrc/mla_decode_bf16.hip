@@ -510,21 +510,27 @@ __device__ __forceinline__ void issue_col_copy(const PageCopy& c, int i, int w, 
 }
 // Where the next page's 18 copies (per wave, in copy order) go inside one page's
 // compute.  Score loop: the block-group waits cut the 36 steps into 5 windows; each
-// window carries 2 copies per wave, wave w issuing its copies w steps after the window's
+// window carries up to 2 copies per wave, wave w issuing its copies w steps after the window's
 // copy slots, so the four waves do not queue their copies behind each other at the
 // same step (every wave still issues the same copies before each wait, which keeps the
 // wait counts compile-time).  Then kCopySm after the softmax and the rest spread over
 // the 16 P.V steps.
-constexpr int kCopyS = 10, kCopySm = 2;
-constexpr int kCopyPV = 18 - kCopyS - kCopySm;
-static_assert(kCopyPV >= 0 && kCopyPV <= 16, "copy schedule");
 constexpr int win_start(int W) { return W == 0 ? 0 : 8 * W - kPrefK; }
 constexpr int win_end(int W) { return W == 4 ? 36 : 8 * (W + 1) - kPrefK; }
 constexpr int win_of(int kk) { return kk < win_start(1) ? 0 : kk < win_start(2) ? 1 : kk < win_start(3) ? 2 : kk < win_start(4) ? 3 : 4; }
-constexpr int win_slot1(int W) { return win_end(W) - win_start(W) - 4; }   // second slot's offset
-static_assert(win_slot1(0) >= 1 && win_slot1(4) >= 1, "windows too short to stagger");
+constexpr int win_len(int W) { return win_end(W) - win_start(W); }
+// copies per window: wave w issues slot 0 at step start+w and slot 1 at step end-4+w
+constexpr int win_copies(int W) { return win_len(W) >= 6 ? 2 : win_len(W) >= 4 ? 1 : 0; }
+// windows 1-3 are 8 steps long (2 copies each)
+constexpr int copies_before_win(int W) {
+  return W == 0 ? 0 : W <= 4 ? win_copies(0) + 2 * (W - 1) : win_copies(0) + 6 + win_copies(4);
+}
+constexpr int kCopyS = copies_before_win(5), kCopySm = 2;
+constexpr int kCopyPV = 18 - kCopyS - kCopySm;
+static_assert(kCopyPV >= 0 && kCopyPV <= 16, "copy schedule");
+static_assert(win_len(1) == 8 && win_len(2) == 8 && win_len(3) == 8, "copy schedule");
 // Copies this wave issued in the score loop before step kk (kk a window start).
-constexpr int s_copies_before(int kk) { return 2 * win_of(kk); }
+constexpr int s_copies_before(int kk) { return copies_before_win(win_of(kk)); }
 // This page's copies issued after block group G (blocks 2G, 2G+1; G = 4: the rope block).
 constexpr int copies_after_group(int G) { return G < 4 ? 14 - 4 * G : 0; }
 // Wait until this wave's copies of the current page up to a block group have landed,
@@ -650,14 +656,16 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
           if (kl == 16) wait_group<2>(pre);
           if (kl == 24) wait_group<3>(pre);
           if (kl == 32) wait_group<4>(pre);
-          if (pre) {
-            const int W = win_of(kk), d = kk - win_start(W);
-            if (d < 4 && w == d) issue_col_copy(nxt, 2 * W, w, l);
-            if (d >= win_slot1(W) && d < win_slot1(W) + 4 && w == d - win_slot1(W)) issue_col_copy(nxt, 2 * W + 1, w, l);
-          }
           if (kl < 36)
             load_k(kl, kr0[kl % (kPrefK + 1)], kr1[kl % (kPrefK + 1)]);
           mfma32_s_step(s0, s1, kr0[kk % (kPrefK + 1)], kr1[kk % (kPrefK + 1)], qf[kk], kk);
+          // a copy issued behind the step's MFMAs stalls (on a full memory queue) while
+          // they run rather than ahead of them
+          if (pre) {
+            const int W = win_of(kk), d = kk - win_start(W), d1 = d - (win_len(W) - 4);
+            if (win_copies(W) >= 1 && d < 4 && w == d) issue_col_copy(nxt, copies_before_win(W), w, l);
+            if (win_copies(W) == 2 && d1 >= 0 && d1 < 4 && w == d1) issue_col_copy(nxt, copies_before_win(W) + 1, w, l);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -717,21 +725,23 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       bf16x8 vring[kPrefV + 1];
 #pragma unroll
       for (int t = 0; t < kPrefV; ++t) vring[t] = load_v(t);
-      bf16x8 pf[4];
+      bf16x8 pf[2][4];   // P fragments of K step ks (all 4 row tiles), read one step ahead
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) pf[0][rt] = lds_read_b128(pbuf + (rt * 64 + l) * 16);
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int ks = t >> 2, dt = t & 3;
-        if (dt == 0) {
+        if (dt == 0 && ks < 3) {
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) pf[rt] = lds_read_b128(pbuf + ((ks * 4 + rt) * 64 + l) * 16);
+          for (int rt = 0; rt < 4; ++rt) pf[(ks + 1) & 1][rt] = lds_read_b128(pbuf + (((ks + 1) * 4 + rt) * 64 + l) * 16);
         }
+        if (t + kPrefV < 16) vring[(t + kPrefV) % (kPrefV + 1)] = load_v(t + kPrefV);
+        mfma32_pv_step(o[dt], vring[t % (kPrefV + 1)], pf[ks & 1], t == 15);
         if (pre) {
 #pragma unroll
           for (int i = 0; i < kCopyPV; ++i)
             if (i * 16 / kCopyPV == t) issue_col_copy(nxt, kCopyS + kCopySm + i, w, l);
         }
-        if (t + kPrefV < 16) vring[(t + kPrefV) % (kPrefV + 1)] = load_v(t + kPrefV);
-        mfma32_pv_step(o[dt], vring[t % (kPrefV + 1)], pf, t == 15);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
