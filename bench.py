@@ -18,7 +18,6 @@ duration from HIP events, and the CPU oracle's rate on the host as a reported ba
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,16 +32,6 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/cl
 METRIC = "MLA decode TFLOP/s + KV GB/s (% roofline), 128 heads, B=64, seqlen 4096"
 DECODE_KERNEL = "mla_decode_bf16_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_h128_l4096_traffic.json")
-KERNEL_SOURCES = ["mla_decode_03_amd/csrc/mla_decode_bf16.hip", "mla_decode_03_amd/csrc/mla_device.h",
-                  "mla_decode_03_amd/csrc/mla_args.h"]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def workload_sizes(case):
@@ -69,6 +58,7 @@ def traffic_from_profile():
             rec = json.load(f)
     except (OSError, ValueError):
         return None
+    from mla_decode_03_amd.profiling import kernel_source_hash
     if rec.get("kernel_source_sha") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -96,6 +86,9 @@ def main():
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--min-blocks", type=int, default=0)
     ap.add_argument("--row-split", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="after timing, copy BYTES device to device 3 times (the reference "
+                         "dispatch that scales the HBM byte counters of a profiled run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -189,6 +182,14 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                     "kernel": DECODE_KERNEL, "kernel_ms": round(kernel_ms, 5),
                     "algorithmic_bytes_per_launch": total_bytes}
+
+    if args.calibrate_copy > 0:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
