@@ -1,12 +1,12 @@
 // Split-KV MLA decode on bf16 MFMA for gfx950 (CDNA4).
 //
 // One workgroup = 4 waves on one CU walks a contiguous range of 64-token KV pages (its
-// share from the split planner; NULL plan = one whole sequence), 32 tokens at a time:
+// share from the split planner; NULL plan = one whole sequence), a page at a time:
 //
-//   S^T = K . Q^T          MFMA 16x16x32 bf16, K from LDS, Q fragments held in VGPRs
+//   S^T = K . Q^T          bf16 MFMA, K from LDS, Q fragments held in VGPRs
 //   online softmax         per row, exp2 with the scale folded into log2(e)
-//   O^T += V^T . P^T       MFMA 16x16x32 bf16, V read from the same LDS page with the
-//                          gfx950 transposing LDS read
+//   O^T += V^T . P^T       bf16 MFMA, V read from the same LDS page with the gfx950
+//                          transposing LDS read, O in the accumulation registers
 //
 // This is the two-GEMM structure of the TileLang notes' FlashMLA example ("TileLang:
 // bridging programmability and performance in modern neural kernels", section "A
@@ -14,18 +14,20 @@
 // S kept in registers, down-cast, second GEMM), and the exp2 / log2(e) form of the
 // online softmax shown in the DeepSeek-V4 TileLang note (section "The essence of
 // TileLang's design").  Placement is re-derived for gfx950: the 128x576 Q tile (147 KB)
-// and two 73.7 KB pages cannot share the 160 KB LDS, so Q lives in VGPRs (32 rows x 576
-// per wave), O (fp32) in the accumulation registers, and LDS holds the double-buffered
-// KV stream fed by global_load_lds (no VGPR staging).  S is computed transposed (tokens
-// x rows) so that its accumulator layout is already the B operand of the second MFMA.
+// and two 73.7 KB pages cannot share the 160 KB LDS, so Q passes through LDS once and
+// then lives in VGPRs (32 rows x 576 per wave), O (fp32) in the accumulation registers,
+// and LDS holds the double-buffered KV stream fed by global_load_lds (no VGPR staging).
+// S is computed transposed (tokens x rows): one query row per lane for the softmax, and
+// the accumulator's token order is the B operand order of the second MFMA.
 //
 // Two work splits over the 4 waves:
-//  * wide (more than 64 rows, e.g. 128 heads): each wave scores its own 32 rows, writes
-//    its bf16 P fragments to LDS, and then accumulates O for ALL rows over its quarter of
-//    the 512 value columns.  Each page's V is then read from LDS once instead of four
-//    times, which keeps the P.V phase off the LDS-bandwidth limit.
-//  * narrow (<= 64 rows): waves split rows and tokens (TG token groups); each wave keeps
-//    O for its 32 rows and the token groups merge their states through LDS at the end.
+//  * wide (more than 64 rows, e.g. 128 heads), on 32x32x16 MFMA tiles: each wave scores
+//    its own 32 rows, writes its bf16 P fragments to LDS, and then accumulates O for ALL
+//    rows over its quarter of the 512 value columns (each page's V is read from LDS
+//    once, not four times).  Pages stream in as column blocks (see the wide split).
+//  * narrow (<= 64 rows), on 16x16x32 MFMA tiles: waves split rows and tokens (TG token
+//    groups); each wave keeps O for its rows and the token groups merge their states
+//    through LDS at the end.
 // O is never rescaled inside the loop: each row fixes its reference max at its first
 // visible keys and accumulates exp2(x - m_ref) <= 2^kRefSlack; if a later score exceeds
 // that, the segment is decoded again with m_ref = the row's true running max (exact).
@@ -35,10 +37,11 @@
 namespace mla {
 
 // ---- LDS layout ---------------------------------------------------------------------
-// Two page buffers of 73728 B each:
+// Two page buffers of 73728 B each.  Narrow split (token rows):
 //   [0, 65536)      value/latent part: token t, 16-byte chunk c < 64 at t*1024 + (c ^ swz(t))*16
 //   [65536, 73728)  rope part:         token t, chunk 64 + c   at 65536 + t*128 + (c ^ swz(t))*16
-// then (wide split only) a 16 KB P buffer: [K step 0..3][row tile 0..3][lane][8 x bf16].
+// (the wide split uses column blocks instead, defined with it), then (wide split only) a
+// 16 KB P buffer: [K step 0..3][row tile 0..3][lane][8 x bf16].
 // swz maps any 8 consecutive tokens to 8 distinct values (conflict-free K reads: 8 lanes
 // read 8 tokens at one chunk) and any 4 consecutive tokens to distinct swz >> 1
 // (conflict-free transposing V reads: 4 tokens x 2 adjacent chunks per 16 lanes).
