@@ -35,26 +35,49 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
     return;
   }
   const int s0 = v.part_off[u];
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[(size_t)(s0 + s) * a.rows_per_wg + rl]);
-  const float Ms = (M == -INFINITY) ? 0.f : M;
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  float tot = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t prow = (size_t)(s0 + s) * a.rows_per_wg + rl;
-    const float wgt = expf(a.ws_lse[prow] - Ms);
+  float tot = 0.f, Ms = 0.f;
+  // o_s rows of this thread: 16 bf16 = two 16-byte loads per split
+  auto part = [&](int sidx) { return (const u32x4*)(a.ws_o + ((size_t)(s0 + sidx) * a.rows_per_wg + rl) * kDv + 16 * t); };
+  auto accumulate = [&](float wgt, u32x4 x0, u32x4 x1) {
     tot += wgt;
-    const u32x4* src = (const u32x4*)(a.ws_o + prow * kDv + 16 * t);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u32x4 x = src[i];
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += wgt * __uint_as_float(x0[j] << 16);
+      acc[2 * j + 1] += wgt * __uint_as_float(x0[j] & 0xffff0000u);
+      acc[8 + 2 * j] += wgt * __uint_as_float(x1[j] << 16);
+      acc[8 + 2 * j + 1] += wgt * __uint_as_float(x1[j] & 0xffff0000u);
+    }
+  };
+  if (ns <= 4) {
+    // the common case: every load of the row issued before any is used
+    float ls[4];
+    u32x4 x[4][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[8 * i + 2 * j] += wgt * __uint_as_float(x[j] << 16);
-        acc[8 * i + 2 * j + 1] += wgt * __uint_as_float(x[j] & 0xffff0000u);
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      if (sidx < ns) {
+        ls[sidx] = a.ws_lse[(size_t)(s0 + sidx) * a.rows_per_wg + rl];
+        x[sidx][0] = part(sidx)[0];
+        x[sidx][1] = part(sidx)[1];
       }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx)
+      if (sidx < ns) M = fmaxf(M, ls[sidx]);
+    Ms = (M == -INFINITY) ? 0.f : M;
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx)
+      if (sidx < ns) accumulate(expf(ls[sidx] - Ms), x[sidx][0], x[sidx][1]);
+  } else {
+    float M = -INFINITY;
+    for (int sidx = 0; sidx < ns; ++sidx) M = fmaxf(M, a.ws_lse[(size_t)(s0 + sidx) * a.rows_per_wg + rl]);
+    Ms = (M == -INFINITY) ? 0.f : M;
+    for (int sidx = 0; sidx < ns; ++sidx) {
+      const float wgt = expf(a.ws_lse[(size_t)(s0 + sidx) * a.rows_per_wg + rl] - Ms);
+      accumulate(wgt, part(sidx)[0], part(sidx)[1]);
     }
   }
   const bool empty = tot == 0.f;  // NaN (a poisoned split) propagates

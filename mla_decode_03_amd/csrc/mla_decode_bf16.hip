@@ -20,14 +20,11 @@
 // S is computed transposed (tokens x rows): one query row per lane for the softmax, and
 // the accumulator's token order is the B operand order of the second MFMA.
 //
-// Two work splits over the 4 waves:
-//  * wide (more than 64 rows, e.g. 128 heads), on 32x32x16 MFMA tiles: each wave scores
-//    its own 32 rows, writes its bf16 P fragments to LDS, and then accumulates O for ALL
-//    rows over its quarter of the 512 value columns (each page's V is read from LDS
-//    once, not four times).  Pages stream in as column blocks (see the wide split).
-//  * narrow (<= 64 rows), on 16x16x32 MFMA tiles: waves split rows and tokens (TG token
-//    groups); each wave keeps O for its rows and the token groups merge their states
-//    through LDS at the end.
+// Work split over the 4 waves: each wave scores its own 32 rows (one row tile; waves
+// beyond the workgroup's row tiles score nothing), writes its bf16 P fragments to LDS,
+// and then accumulates O for ALL rows over its quarter of the 512 value columns (each
+// page's V is read from LDS once, not four times).  Everything runs on 32x32x16 MFMA
+// tiles; pages stream in as column blocks (see the copies below).
 // O is never rescaled inside the loop: each row fixes its reference max at its first
 // visible keys and accumulates exp2(x - m_ref) <= 2^kRefSlack; if a later score exceeds
 // that, the segment is decoded again with m_ref = the row's true running max (exact).
@@ -37,19 +34,11 @@
 namespace mla {
 
 // ---- LDS layout ---------------------------------------------------------------------
-// Two page buffers of 73728 B each.  Narrow split (token rows):
-//   [0, 65536)      value/latent part: token t, 16-byte chunk c < 64 at t*1024 + (c ^ swz(t))*16
-//   [65536, 73728)  rope part:         token t, chunk 64 + c   at 65536 + t*128 + (c ^ swz(t))*16
-// (the wide split uses column blocks instead, defined with it), then (wide split only) a
-// 16 KB P buffer: [K step 0..3][row tile 0..3][lane][8 x bf16].
-// swz maps any 8 consecutive tokens to 8 distinct values (conflict-free K reads: 8 lanes
-// read 8 tokens at one chunk) and any 4 consecutive tokens to distinct swz >> 1
-// (conflict-free transposing V reads: 4 tokens x 2 adjacent chunks per 16 lanes).
-constexpr int kRopeOff = 65536;
+// Two page buffers of 73728 B each (column-block layout, defined with the copies below),
+// then a 16 KB P buffer: [K step 0..3][row tile 0..3][lane][8 x bf16].
 constexpr int kPBufOff = 2 * kBlockBytes;          // 147456
-constexpr int kPBufBytes = 16384;                 // wide split: P of one page
+constexpr int kPBufBytes = 16384;                 // P of one page
 constexpr int kLdsBytes = kPBufOff + kPBufBytes;   // 163840 = all of it
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
 constexpr float kRefSlack = 16.0f;  // scores may exceed the reference max by 2^16
 constexpr int kPrefK = 2;           // K-fragment prefetch distance (32-dim steps)
@@ -77,25 +66,6 @@ struct PageCopy {
   int valid;              // tokens of the page in the sequence
   MLA_LDS uint8_t* buf;   // page buffer
 };
-__device__ __forceinline__ void issue_copy(const PageCopy& c, int i, int w, int l) {
-  if (i < 16) {
-    const int t = 16 * w + i;
-    const int te = (t < c.valid) ? t : 0;                   // uniform
-    dma16(c.base + te * kRowBytes, (uint32_t)(l ^ swz(i)) << 4, c.buf + t * 1024);
-  } else {
-    const int k = 2 * w + (i - 16);
-    const int t = 8 * k + (l >> 3);
-    const int te = (t < c.valid) ? t : 0;
-    dma16(c.base, (uint32_t)(te * kRowBytes + ((64 + ((l & 7) ^ swz(l >> 3))) << 4)),
-          c.buf + kRopeOff + k * 1024);
-  }
-}
-__device__ __forceinline__ void issue_page(const uint8_t* __restrict__ kv, int page, int valid,
-                                           MLA_LDS uint8_t* buf, int w, int l) {
-  const PageCopy c{kv + (size_t)page * kBlockBytes, valid, buf};
-#pragma unroll
-  for (int i = 0; i < 18; ++i) issue_copy(c, i, w, l);
-}
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS uint8_t* p) {
   return *(const MLA_LDS bf16x8*)p;
@@ -132,118 +102,9 @@ __device__ __forceinline__ bool wg_or(bool f, MLA_LDS int* scratch) {
 }
 
 // Keep an O tile in AGPRs across a point where vector ALU code touched it.
-__device__ __forceinline__ void pin_agpr(f32x4& t) { asm volatile("" : "+a"(t)); }
 
-// Softmax state of the rows a wave scores: rows rbase + 16*nt + (lane % 16), nt < 2.
-struct RowState {
-  float m[2];       // reference max of x = s * scale * log2(e); O and lsum are relative to it
-  float lsum[2];    // sum of exp2(x - m)
-  float mtrue[2];   // running max of every x seen (for the restart pass)
-  bool over;        // some x exceeded m + kRefSlack: the pass must be redone
-};
 
-// ---- MFMA steps, written out so the register classes can be pinned -------------------
-// S accumulators live in VGPRs, O in AGPRs.  Chains accumulate into exactly the same
-// registers (no wait states needed between them); a first step takes C = 0; "s_nop 1"
-// covers a vector-ALU write of an operand just before (2 wait states); a step that ends
-// a chain read later by vector ALU code appends 21 wait states.
-template <int NMT>
-__device__ __forceinline__ void mfma_s_step(f32x4 (&s)[NMT][2], const bf16x8 (&ka)[NMT],
-                                            const bf16x8& q0, const bf16x8& q1, int kk) {
-  if constexpr (NMT == 2) {
-    if (kk == 0) {
-      asm volatile(
-          "s_nop 1\n\t"
-          "v_mfma_f32_16x16x32_bf16 %0, %4, %6, 0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %4, %7, 0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %2, %5, %6, 0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %3, %5, %7, 0"
-          : "=&v"(s[0][0]), "=&v"(s[0][1]), "=&v"(s[1][0]), "=&v"(s[1][1])
-          : "v"(ka[0]), "v"(ka[1]), "v"(q0), "v"(q1));
-    } else if (kk < 17) {
-      asm volatile(
-          "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
-          "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
-          "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
-          : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1])
-          : "v"(ka[0]), "v"(ka[1]), "v"(q0), "v"(q1));
-    } else {
-      asm volatile(
-          "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
-          "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
-          "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3\n\t"
-          "s_nop 15\n\t"
-          "s_nop 4"
-          : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1])
-          : "v"(ka[0]), "v"(ka[1]), "v"(q0), "v"(q1));
-    }
-  } else {
-    if (kk == 0) {
-      asm volatile(
-          "s_nop 1\n\t"
-          "v_mfma_f32_16x16x32_bf16 %0, %2, %3, 0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %2, %4, 0"
-          : "=&v"(s[0][0]), "=&v"(s[0][1])
-          : "v"(ka[0]), "v"(q0), "v"(q1));
-    } else if (kk < 17) {
-      asm volatile(
-          "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
-          : "+v"(s[0][0]), "+v"(s[0][1])
-          : "v"(ka[0]), "v"(q0), "v"(q1));
-    } else {
-      asm volatile(
-          "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %2, %4, %1\n\t"
-          "s_nop 15\n\t"
-          "s_nop 4"
-          : "+v"(s[0][0]), "+v"(s[0][1])
-          : "v"(ka[0]), "v"(q0), "v"(q1));
-    }
-  }
-}
 
-// Narrow split: one 16-wide value tile for the wave's 2 row tiles.
-__device__ __forceinline__ void mfma_pv32(f32x4& o0, f32x4& o1, const bf16x8& va, const bf16x8& p0,
-                                          const bf16x8& p1, bool last) {
-  if (!last)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
-        : "+a"(o0), "+a"(o1)
-        : "v"(va), "v"(p0), "v"(p1));
-  else
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %1, %2, %4, %1\n\t"
-        "s_nop 15\n\t"
-        "s_nop 4"
-        : "+a"(o0), "+a"(o1)
-        : "v"(va), "v"(p0), "v"(p1));
-}
-__device__ __forceinline__ void mfma_pv16(f32x4& o0, f32x4& o1, const s16x4& va, const s16x4& p0,
-                                          const s16x4& p1, bool last) {
-  if (!last)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_16x16x16_bf16 %0, %2, %3, %0\n\t"
-        "v_mfma_f32_16x16x16_bf16 %1, %2, %4, %1"
-        : "+a"(o0), "+a"(o1)
-        : "v"(va), "v"(p0), "v"(p1));
-  else
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_16x16x16_bf16 %0, %2, %3, %0\n\t"
-        "v_mfma_f32_16x16x16_bf16 %1, %2, %4, %1\n\t"
-        "s_nop 15\n\t"
-        "s_nop 4"
-        : "+a"(o0), "+a"(o1)
-        : "v"(va), "v"(p0), "v"(p1));
-}
 // Wide split (32x32x16 tiles).  S^T step: two 32-token tiles x the wave's 32 rows, one
 // 16-dim K step; accumulators in VGPRs.
 __device__ __forceinline__ void mfma32_s_step(f32x16& s0, f32x16& s1, const bf16x8& k0, const bf16x8& k1,
@@ -270,188 +131,63 @@ __device__ __forceinline__ void mfma32_s_step(f32x16& s0, f32x16& s1, const bf16
         : "+v"(s0), "+v"(s1)
         : "v"(k0), "v"(k1), "v"(q));
 }
-// O^T step: one 32-wide value tile x all 4 row tiles (128 rows), one 16-token K step;
-// accumulators in AGPRs.
-__device__ __forceinline__ void mfma32_pv_step(f32x16 (&o)[4], const bf16x8& va, const bf16x8 (&p)[4],
+// O^T step: one 32-wide value tile x the NRT live row tiles (32 rows each), one 16-token
+// K step; accumulators in AGPRs.  `last` drains the pipeline before AGPRs are read.
+template <int NRT>
+__device__ __forceinline__ void mfma32_pv_step(f32x16 (&o)[NRT], const bf16x8& va, const bf16x8 (&p)[4],
                                                bool last) {
-  if (!last)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
-        "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3"
-        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
-        : "v"(va), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
-  else
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
-        "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3\n\t"
-        "s_nop 15\n\t"
-        "s_nop 4"
-        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
-        : "v"(va), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
-}
-
-// Lane constants for LDS reads.
-struct LaneOffsets {
-  int k_v;      // K read, value part: token li row
-  int kx;       // K read chunk xor: chunk (4*kk + lq) ^ swz(li) == (4*kk) ^ kx
-  int k_r;      // K read, rope part
-  int v_base;   // V read: token 4*lq + li/4, byte 8*(li&1)
-  int vy[4];    // V read chunk offsets for value tile dt with dt % 4 == d
-};
-__device__ __forceinline__ LaneOffsets lane_offsets(int l) {
-  const int lq = l >> 4, li = l & 15;
-  LaneOffsets lo;
-  lo.kx = lq ^ swz(li);
-  lo.k_v = li * 1024;
-  lo.k_r = kRopeOff + li * 128;
-  const int vg = (((li >> 2) & 3) << 1) | (lq & 1);   // swz of token 4*lq + li/4
-  lo.v_base = (4 * lq + (li >> 2)) * 1024 + 8 * (li & 1);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) lo.vy[d] = ((2 * d + ((li & 3) >> 1)) ^ vg) << 4;
-  return lo;
-}
-
-// V^T fragment (16 value columns x 32 tokens from tokA) as the A operand: two transposing
-// reads, tokens tokA + {4*lq .. +3} and tokA + 16 + {4*lq .. +3} for column 16*dt + li.
-__device__ __forceinline__ bf16x8 load_v32(const MLA_LDS uint8_t* cur, const LaneOffsets& lo, int tokA,
-                                           int dt) {
-  const MLA_LDS uint8_t* vp = cur + lo.v_base + tokA * 1024 + (dt >> 2) * 128 + lo.vy[dt & 3];
-  return cat8(lds_read_tr(vp), lds_read_tr(vp + 16 * 1024));
-}
-
-// S^T for NMT 16-token tiles starting at token tokA, all 576 dims (K from LDS).
-template <int NMT>
-__device__ __forceinline__ void s_phase(f32x4 (&s)[NMT][2], const bf16x8 (&qf)[2][18],
-                                        const MLA_LDS uint8_t* cur, int tokA, const LaneOffsets& lo) {
-  auto load_k = [&](int kk, bf16x8(&ka)[NMT]) {
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const int t = tokA + 16 * mt;
-      if (kk < 16)
-        ka[mt] = lds_read_b128(cur + lo.k_v + t * 1024 + (((4 * kk) ^ lo.kx) << 4));
-      else
-        ka[mt] = lds_read_b128(cur + lo.k_r + t * 128 + (((4 * (kk - 16)) ^ lo.kx) << 4));
-    }
-  };
-  // K fragments are fetched kPrefK steps ahead through a small ring; the scheduling
-  // fences keep the compiler from hoisting further (Q already holds 144 VGPRs).
-  bf16x8 kring[kPrefK + 1][NMT];
-#pragma unroll
-  for (int kk = 0; kk < kPrefK; ++kk) load_k(kk, kring[kk]);
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    if (kk + kPrefK < 18) load_k(kk + kPrefK, kring[(kk + kPrefK) % (kPrefK + 1)]);
-    mfma_s_step<NMT>(s, kring[kk % (kPrefK + 1)], qf[0][kk], qf[1][kk], kk);
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NRT == 4) {
+    if (!last)
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
+          "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3"
+          : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
+          : "v"(va), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+    else
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
+          "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3\n\t"
+          "s_nop 15\n\t"
+          "s_nop 4"
+          : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
+          : "v"(va), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+  } else if constexpr (NRT == 2) {
+    if (!last)
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+          : "+a"(o[0]), "+a"(o[1]) : "v"(va), "v"(p[0]), "v"(p[1]));
+    else
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1\n\t"
+          "s_nop 15\n\t"
+          "s_nop 4"
+          : "+a"(o[0]), "+a"(o[1]) : "v"(va), "v"(p[0]), "v"(p[1]));
+  } else {
+    static_assert(NRT == 1, "1, 2 or 4 row tiles");
+    if (!last)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o[0]) : "v"(va), "v"(p[0]));
+    else
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 4"
+                   : "+a"(o[0]) : "v"(va), "v"(p[0]));
   }
 }
 
-// Softmax of the scores in s (lane owns rows li and 16 + li, 4*NMT keys each): masks
-// keys at positions >= nvis, updates the row state, returns P as bf16 B operands.
-template <int NMT>
-__device__ __forceinline__ void softmax_p(RowState& st, f32x4 (&s)[NMT][2], bf16x4 (&pb)[NMT][2],
-                                          bool need_mask, int pos0, const int (&nvis)[2],
-                                          float scale_log2, int l) {
-  const int lq = l >> 4;
-  float mx[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[mt][nt][e] * scale_log2;
-        if (need_mask) x = (pos0 + 16 * mt + 4 * lq + e < nvis[nt]) ? x : -INFINITY;
-        s[mt][nt][e] = x;
-        m = fmaxf(m, x);
-      }
-    m = wave_max_xor(m, 16);
-    mx[nt] = wave_max_xor(m, 32);
-  }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    st.mtrue[nt] = fmaxf(st.mtrue[nt], mx[nt]);
-    if (st.m[nt] == -INFINITY) st.m[nt] = mx[nt];     // nothing accumulated yet: exact
-    st.over |= mx[nt] > st.m[nt] + kRefSlack;
-  }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float msub = (st.m[nt] == -INFINITY) ? 0.f : st.m[nt];
-    float rs = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      f32x4 p;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(s[mt][nt][e] - msub);
-        rs += p[e];
-      }
-      pb[mt][nt] = to_bf16x4(p);
-    }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    st.lsum[nt] += rs;
-  }
-}
 
-// Per-segment setup shared by both splits.
-struct SegmentSetup {
-  int Lc;          // sequence length (0 if it is out of range)
-  bool bad_len;
-  int nvis[2];     // visible keys of this lane's two scored rows
-  int nmin;        // fewest visible keys over the workgroup's rows
-};
-__device__ __forceinline__ SegmentSetup segment_setup(const DecodeArgs& a, int b, int row0, int rbase,
-                                                      int li) {
-  SegmentSetup s;
-  const int L = ld_const(a.seqlens, b);
-  s.bad_len = (L < 0) || ((int64_t)L > (int64_t)kPage * a.max_blocks);
-  s.Lc = s.bad_len ? 0 : L;
-  const int R = a.rows;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = min(rbase + 16 * nt + li, R - 1);
-    int n = s.Lc;
-    if (a.causal && a.q_len > 1) n = s.Lc - a.q_len + 1 + r / a.heads;
-    s.nvis[nt] = max(n, 0);
-  }
-  s.nmin = s.Lc;
-  if (a.causal && a.q_len > 1) s.nmin = max(s.Lc - a.q_len + 1 + row0 / a.heads, 0);
-  return s;
-}
 
-// Q fragments (B operand of S^T = K Q^T): lane holds q[row][32*kk + 8*lq .. +8] for
-// rows rbase + 16*nt + li; rows >= row_end read as zero.
-__device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int rbase, int row0, int row_end,
-                                       int l, bf16x8 (&qf)[2][18]) {
-  const int lq = l >> 4, li = l & 15;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = rbase + 16 * nt + li;
-    const bool ok = r < row_end;
-    const bf16x8* src = (const bf16x8*)(a.q + ((size_t)b * a.rows + (ok ? r : row0)) * kRowBytes) + lq;
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      const bf16x8 v = src[4 * kk];
-      qf[nt][kk] = ok ? v : bf16x8{};
-    }
-  }
-}
 
-__device__ __forceinline__ void issue_block(const DecodeArgs& a, int b, int j, int Lc, MLA_LDS uint8_t* buf,
-                                            int w, int l, bool& bad_page) {
-  const int page = ld_const(a.block_table, (size_t)b * a.bt_stride + j);
-  const bool bad = page < 0 || page >= a.num_pages;
-  bad_page |= bad;
-  issue_page(a.kv, bad ? 0 : page, bad ? 1 : min(kPage, Lc - j * kPage), buf, w, l);
-}
+
+
+
 // Copy description of page j (pool index `page`), checking the index (a bad index reads
 // page 0 and poisons the segment).
 __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int j, int Lc, MLA_LDS uint8_t* buf,
@@ -461,7 +197,7 @@ __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int
   return PageCopy{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, bad ? 1 : min(kPage, Lc - j * kPage), buf};
 }
 
-// ===== wide split: more than 64 rows per workgroup =====================================
+// ===== page stream and decode segment ==================================================
 // 32x32x16 MFMA tiles.  Wave w scores rows row0 + 32w .. +31 (one row tile) over the
 // page's two 32-token tiles, publishes P (bf16) through LDS, and accumulates O^T for
 // value columns 128w .. 128w + 127 of all four row tiles:
@@ -553,6 +289,11 @@ __device__ __forceinline__ void wait_group(bool pre) {
   else wait_vm_barrier<copies_after_group(G)>();
 }
 
+// NRT = row tiles of 32 rows the workgroup holds (rows_per_wg <= 32 NRT).  Wave w scores
+// row tile w; waves w >= NRT score zero query rows (no branch around their MFMAs: the
+// MFMAs are assembly the compiler cannot see, so it must never have to move their
+// accumulators between branches), and only the NRT live row tiles enter P.V.
+template <int NRT>
 __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
                                                     int row0, int blk_lo, int blk_hi, int slot) {
   const int w = wave_id(), l = threadIdx.x & 63;
@@ -600,7 +341,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   const WideLane wl = wide_lane(l, w);
   MLA_LDS uint8_t* pbuf = lds + kPBufOff;
 
-  f32x16 o[4][4];
+  f32x16 o[4][NRT];
   float m_ref = -INFINITY, mtrue = -INFINITY, lsum = 0.f;
   bool over = false, bad_page = false;
   float mref_init = -INFINITY;
@@ -612,7 +353,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0; rt < NRT; ++rt) {
         o[dt][rt] = f32x16{};
         asm volatile("" : "+a"(o[dt][rt]));
       }
@@ -730,16 +471,16 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       for (int t = 0; t < kPrefV; ++t) vring[t] = load_v(t);
       bf16x8 pf[2][4];   // P fragments of K step ks (all 4 row tiles), read one step ahead
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) pf[0][rt] = lds_read_b128(pbuf + (rt * 64 + l) * 16);
+      for (int rt = 0; rt < NRT; ++rt) pf[0][rt] = lds_read_b128(pbuf + (rt * 64 + l) * 16);
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int ks = t >> 2, dt = t & 3;
         if (dt == 0 && ks < 3) {
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) pf[(ks + 1) & 1][rt] = lds_read_b128(pbuf + (((ks + 1) * 4 + rt) * 64 + l) * 16);
+          for (int rt = 0; rt < NRT; ++rt) pf[(ks + 1) & 1][rt] = lds_read_b128(pbuf + (((ks + 1) * 4 + rt) * 64 + l) * 16);
         }
         if (t + kPrefV < 16) vring[(t + kPrefV) % (kPrefV + 1)] = load_v(t + kPrefV);
-        mfma32_pv_step(o[dt], vring[t % (kPrefV + 1)], pf[ks & 1], t == 15);
+        mfma32_pv_step<NRT>(o[dt], vring[t % (kPrefV + 1)], pf[ks & 1], t == 15);
         if (pre) {
 #pragma unroll
           for (int i = 0; i < kCopyPV; ++i)
@@ -768,7 +509,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   // (c ^ (rr & 15))*16.  The page buffers are idle now.
   MLA_LDS uint8_t* ob = lds;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < NRT; ++rt) {
     const int rr = 32 * rt + lr;
     const float ls = stats[2 * rr + 1];
     const bool empty = ls == 0.f;   // no visible key; NaN propagates
@@ -803,203 +544,11 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   }
 }
 
-// ===== narrow split: at most 64 rows per workgroup =====================================
-// TG token groups x (4 / TG) row groups of 32 rows; each wave keeps O^T for its rows,
-// o[dt][nt] = columns 16dt + 4*(lane/16) + j of row rbase + 16nt + lane%16.
-struct NarrowState {
-  f32x4 o[32][2];
-  RowState r;
-};
-constexpr int kStateSlotFloats = (256 + 4) * 64;
-
-__device__ __forceinline__ void store_state(const NarrowState& st, MLA_LDS float* slot, int l) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) slot[((dt * 2 + nt) * 4 + j) * 64 + l] = st.o[dt][nt][j];
-    slot[256 * 64 + nt * 64 + l] = st.r.m[nt];
-    slot[256 * 64 + 128 + nt * 64 + l] = st.r.lsum[nt];
-  }
-}
-__device__ __forceinline__ void merge_state(NarrowState& st, const MLA_LDS float* slot, int l) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float mb = slot[256 * 64 + nt * 64 + l];
-    const float lb = slot[256 * 64 + 128 + nt * 64 + l];
-    const float mn = fmaxf(st.r.m[nt], mb);
-    const float ms = (mn == -INFINITY) ? 0.f : mn;
-    const float fa = __builtin_amdgcn_exp2f(st.r.m[nt] - ms), fb = __builtin_amdgcn_exp2f(mb - ms);
-    st.r.lsum[nt] = st.r.lsum[nt] * fa + lb * fb;
-    st.r.m[nt] = mn;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        st.o[dt][nt][j] = st.o[dt][nt][j] * fa + slot[((dt * 2 + nt) * 4 + j) * 64 + l] * fb;
-      pin_agpr(st.o[dt][nt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
-// One sub-block of NMT 16-token tiles at token tokA: scores, softmax, P.V for own rows.
-template <int NMT>
-__device__ __forceinline__ void narrow_sub_block(NarrowState& st, const bf16x8 (&qf)[2][18],
-                                                 const MLA_LDS uint8_t* cur, int tokA, const LaneOffsets& lo,
-                                                 bool need_mask, int pos0, const int (&nvis)[2],
-                                                 float scale_log2, int l) {
-  f32x4 s[NMT][2];
-  s_phase<NMT>(s, qf, cur, tokA, lo);
-  bf16x4 pb[NMT][2];
-  softmax_p<NMT>(st.r, s, pb, need_mask, pos0, nvis, scale_log2, l);
-  if constexpr (NMT == 2) {
-    bf16x8 pk[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) pk[nt] = cat8(pb[0][nt], pb[1][nt]);
-    bf16x8 vring[kPrefV + 1];
-#pragma unroll
-    for (int dt = 0; dt < kPrefV; ++dt) vring[dt] = load_v32(cur, lo, tokA, dt);
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      if (dt + kPrefV < 32) vring[(dt + kPrefV) % (kPrefV + 1)] = load_v32(cur, lo, tokA, dt + kPrefV);
-      mfma_pv32(st.o[dt][0], st.o[dt][1], vring[dt % (kPrefV + 1)], pk[0], pk[1], dt == 31);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else {
-    s16x4 pk[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) pk[nt] = __builtin_bit_cast(s16x4, pb[0][nt]);
-    auto load_v = [&](int dt) {
-      const MLA_LDS uint8_t* vp = cur + lo.v_base + tokA * 1024 + (dt >> 2) * 128 + lo.vy[dt & 3];
-      return __builtin_bit_cast(s16x4, lds_read_tr(vp));
-    };
-    s16x4 vring[kPrefV + 1];
-#pragma unroll
-    for (int dt = 0; dt < kPrefV; ++dt) vring[dt] = load_v(dt);
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      if (dt + kPrefV < 32) vring[(dt + kPrefV) % (kPrefV + 1)] = load_v(dt + kPrefV);
-      mfma_pv16(st.o[dt][0], st.o[dt][1], vring[dt % (kPrefV + 1)], pk[0], pk[1], dt == 31);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
-template <int TG>
-__device__ __forceinline__ void decode_segment_narrow(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
-                                                      int row0, int blk_lo, int blk_hi, int slot) {
-  constexpr int RG = 4 / TG;       // waves along rows
-  constexpr int WTOK = 64 / TG;    // tokens per wave per page
-  const int w = wave_id(), l = threadIdx.x & 63;
-  const int rg = w % RG, tg = w / RG;
-  const int lq = l >> 4, li = l & 15;
-  const int R = a.rows;
-  const int row_end = min(row0 + a.rows_per_wg, R);
-  const int rbase = row0 + 32 * rg;
-  const SegmentSetup ss = segment_setup(a, b, row0, rbase, li);
-
-  bf16x8 qf[2][18];
-  load_q(a, b, rbase, row0, row_end, l, qf);
-  const LaneOffsets lo = lane_offsets(l);
-  const int tok0 = WTOK * tg;
-
-  NarrowState st;
-  bool bad_page = false;
-  float mref_init[2] = {-INFINITY, -INFINITY};
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      st.r.m[nt] = mref_init[nt];
-      st.r.mtrue[nt] = -INFINITY;
-      st.r.lsum[nt] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pin_agpr(st.o[dt][nt]);
-      }
-    }
-    st.r.over = false;
-
-    __syncthreads();
-    if (blk_lo < blk_hi) issue_block(a, b, blk_lo, ss.Lc, lds, w, l, bad_page);
-    for (int j = blk_lo; j < blk_hi; ++j) {
-      const int it = j - blk_lo;
-      const MLA_LDS uint8_t* cur = lds + (it & 1) * kBlockBytes;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (j + 1 < blk_hi) issue_block(a, b, j + 1, ss.Lc, lds + ((it + 1) & 1) * kBlockBytes, w, l, bad_page);
-      if constexpr (WTOK >= 32) {
-#pragma unroll
-        for (int sb = 0; sb < WTOK / 32; ++sb) {
-          const int tokA = tok0 + 32 * sb;
-          const int pos0 = j * kPage + tokA;
-          narrow_sub_block<2>(st, qf, cur, tokA, lo, pos0 + 32 > ss.nmin, pos0, ss.nvis, a.scale_log2, l);
-        }
-      } else {
-        const int pos0 = j * kPage + tok0;
-        narrow_sub_block<1>(st, qf, cur, tok0, lo, pos0 + 16 > ss.nmin, pos0, ss.nvis, a.scale_log2, l);
-      }
-    }
-    if (!__syncthreads_or(st.r.over ? 1 : 0)) break;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) mref_init[nt] = st.r.mtrue[nt];
-  }
-
-  // merge token groups through LDS (the page buffers are free once all waves pass)
-  if constexpr (TG > 1) {
-    MLA_LDS float* slots = (MLA_LDS float*)lds;
-#pragma unroll
-    for (int step = TG / 2; step >= 1; step /= 2) {
-      __syncthreads();
-      if (tg >= step && tg < 2 * step) store_state(st, slots + (rg * step + (tg - step)) * kStateSlotFloats, l);
-      __syncthreads();
-      if (tg < step) merge_state(st, slots + (rg * step + tg) * kStateSlotFloats, l);
-    }
-  }
-
-  const bool poison = ss.bad_len || __syncthreads_or(bad_page ? 1 : 0);
-  if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
-  if (tg != 0) return;
-  const float nanv = __builtin_nanf("");
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = rbase + 16 * nt + li;
-    if (r >= row_end) continue;
-    const float ls = st.r.lsum[nt];
-    const bool empty = ls == 0.f;   // no visible key; NaN propagates
-    const float scale_o = poison ? nanv : (empty ? 0.f : 1.f / ls);
-    const float lse_v = poison ? nanv : (empty ? -INFINITY : (st.r.m[nt] + __log2f(ls)) * kLn2);
-    if (slot < 0) {
-      uint16_t* orow = a.out + ((size_t)b * R + r) * kDv + 4 * lq;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const f32x4 v = st.o[dt][nt] * scale_o;
-        const uint32_t lo2 = pack_bf16x2(v[0], v[1]);
-        const uint32_t hi2 = pack_bf16x2(v[2], v[3]);
-        *(u32x2*)(orow + 16 * dt) = u32x2{lo2, hi2};
-      }
-      if (lq == 0) a.lse[(size_t)b * R + r] = lse_v;
-    } else {
-      uint16_t* prow = a.ws_o + ((size_t)slot * a.rows_per_wg + (r - row0)) * kDv + 4 * lq;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const f32x4 v = st.o[dt][nt] * scale_o;
-        const uint32_t lo2 = pack_bf16x2(v[0], v[1]);
-        const uint32_t hi2 = pack_bf16x2(v[2], v[3]);
-        *(u32x2*)(prow + 16 * dt) = u32x2{lo2, hi2};
-      }
-      if (lq == 0) a.ws_lse[(size_t)slot * a.rows_per_wg + (r - row0)] = lse_v;
-    }
-  }
-}
-
 // ===== kernel ==========================================================================
-// TG = 1: wide split (rows_per_wg > 64); TG = 2, 4: narrow split.
-template <int TG>
+// NRT = 32-row tiles per workgroup (1, 2 or 4).
+template <int NRT>
 __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[TG == 1 ? kLdsBytes : 2 * kBlockBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)lds_raw;
   const bool planned = a.meta != nullptr;
   MetaView v = meta_view(a.meta, a.batch, a.row_split);
@@ -1042,10 +591,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
       slot = -1;
       pos = end;
     }
-    if constexpr (TG == 1)
-      decode_segment_wide(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
-    else
-      decode_segment_narrow<TG>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    decode_segment_wide<NRT>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
   }
 }
 
@@ -1054,10 +600,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream) {
   const int rpw = args->rows_per_wg;
   if (rpw > 64)
-    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<1>, dim3(grid), dim3(256), 0, stream, *args);
+    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<4>, dim3(grid), dim3(256), 0, stream, *args);
   else if (rpw > 32)
     hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<2>, dim3(grid), dim3(256), 0, stream, *args);
   else
-    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<4>, dim3(grid), dim3(256), 0, stream, *args);
+    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<1>, dim3(grid), dim3(256), 0, stream, *args);
   return hipGetLastError();
 }

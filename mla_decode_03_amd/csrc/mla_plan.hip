@@ -14,28 +14,39 @@
 
 namespace mla {
 
-// Block-wide exclusive scan of one value per thread (256 threads); returns the
-// exclusive prefix and writes the block total to *total.
+// Block-wide exclusive scan of one value per thread (256 threads = 4 waves): a scan
+// inside each wave, then the wave totals through LDS.  Returns the exclusive prefix and
+// writes the block total to *total.
 __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s, int32_t* total) {
-  const int t = threadIdx.x;
-  s[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int32_t add = (t >= off) ? s[t - off] : 0;
-    __syncthreads();
-    s[t] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int32_t incl = s[t];
-  *total = s[255];
+  if (lane == 63) s[wv] = x;
   __syncthreads();
-  return incl - v;
+  int32_t base = 0;
+  for (int k = 0; k < wv; ++k) base += s[k];
+  *total = s[0] + s[1] + s[2] + s[3];
+  __syncthreads();  // s is reused by the next scan
+  return base + x - v;
+}
+
+// floor(n / d) for 0 <= n < 2^53, 0 < d < 2^31: a double quotient, corrected to the
+// exact integer (the rounded quotient is off by at most one).
+__device__ inline int64_t floor_div(int64_t n, int64_t d) {
+  int64_t q = (int64_t)((double)n / (double)d);
+  if (q * d > n) --q;
+  else if ((q + 1) * d <= n) ++q;
+  return q;
 }
 
 // Workgroup holding global block position x (0 <= x < total): the largest w < num_wg
 // with floor(w*total/num_wg) <= x.
 __device__ inline int32_t wg_of(int64_t x, int64_t total, int64_t num_wg) {
-  return (int32_t)(((x + 1) * num_wg - 1) / total);
+  return (int32_t)floor_div((x + 1) * num_wg - 1, total);
 }
 
 __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict__ seqlens,
@@ -78,7 +89,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
 
   // 2. workgroup shares
   for (int w = t; w <= grid_wg; w += 256)
-    v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)((int64_t)w * total / num_wg) : (int32_t)total;
+    v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)floor_div((int64_t)w * total, num_wg) : (int32_t)total;
 
   // 3. units: which workgroups cover each, and the partial slots of the split ones
   const int units = batch * row_split;
