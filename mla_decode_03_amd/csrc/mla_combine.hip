@@ -14,7 +14,7 @@
 namespace mla {
 
 
-constexpr int kCombineRows = 8;
+constexpr int kCombineRows = 8;   // rows per workgroup (256 threads)
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   MetaView v = meta_view(const_cast<int32_t*>(a.meta), a.batch, a.row_split);
@@ -51,34 +51,32 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
       acc[8 + 2 * j + 1] += wgt * __uint_as_float(x1[j] & 0xffff0000u);
     }
   };
-  if (ns <= 4) {
-    // the common case: every load of the row issued before any is used
+  // M = the largest partial LSE (8 loads in flight per step)
+  float M = -INFINITY;
+  for (int base = 0; base < ns; base += 8) {
+    float ls[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      ls[k] = (base + k < ns) ? a.ws_lse[(size_t)(s0 + base + k) * a.rows_per_wg + rl] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, ls[k]);
+  }
+  Ms = (M == -INFINITY) ? 0.f : M;
+  // weighted sum, 4 splits per step with all their loads issued before any is used
+  for (int base = 0; base < ns; base += 4) {
     float ls[4];
     u32x4 x[4][2];
 #pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx) {
-      if (sidx < ns) {
-        ls[sidx] = a.ws_lse[(size_t)(s0 + sidx) * a.rows_per_wg + rl];
-        x[sidx][0] = part(sidx)[0];
-        x[sidx][1] = part(sidx)[1];
+    for (int k = 0; k < 4; ++k) {
+      if (base + k < ns) {
+        ls[k] = a.ws_lse[(size_t)(s0 + base + k) * a.rows_per_wg + rl];
+        x[k][0] = part(base + k)[0];
+        x[k][1] = part(base + k)[1];
       }
     }
-    float M = -INFINITY;
 #pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx)
-      if (sidx < ns) M = fmaxf(M, ls[sidx]);
-    Ms = (M == -INFINITY) ? 0.f : M;
-#pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx)
-      if (sidx < ns) accumulate(expf(ls[sidx] - Ms), x[sidx][0], x[sidx][1]);
-  } else {
-    float M = -INFINITY;
-    for (int sidx = 0; sidx < ns; ++sidx) M = fmaxf(M, a.ws_lse[(size_t)(s0 + sidx) * a.rows_per_wg + rl]);
-    Ms = (M == -INFINITY) ? 0.f : M;
-    for (int sidx = 0; sidx < ns; ++sidx) {
-      const float wgt = expf(a.ws_lse[(size_t)(s0 + sidx) * a.rows_per_wg + rl] - Ms);
-      accumulate(wgt, part(sidx)[0], part(sidx)[1]);
-    }
+    for (int k = 0; k < 4; ++k)
+      if (base + k < ns) accumulate(expf(ls[k] - Ms), x[k][0], x[k][1]);
   }
   const bool empty = tot == 0.f;  // NaN (a poisoned split) propagates
   const float inv = empty ? 0.f : 1.f / tot;
