@@ -14,6 +14,8 @@
 
 namespace mla {
 
+constexpr int kPlanLdsBatch = 4095;   // batches up to this size keep cu_blocks in LDS
+
 // Block-wide exclusive scan of one value per thread (256 threads = 4 waves): a scan
 // inside each wave, then the wave totals through LDS.  Returns the exclusive prefix and
 // writes the block total to *total.
@@ -55,7 +57,9 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
                                                        int min_blocks, int max_blocks,
                                                        int max_partials) {
   __shared__ int32_t s_scan[256];
+  __shared__ int32_t s_cu[kPlanLdsBatch + 1];   // cu_blocks, when the batch fits
   const int t = threadIdx.x;
+  const bool cu_in_lds = batch <= kPlanLdsBatch;
   MetaView v = meta_view(meta, batch, row_split);
   int err = 0;
 
@@ -73,10 +77,16 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
     }
     int32_t tot;
     const int32_t excl = block_exclusive_scan(nb, s_scan, &tot);
-    if (b < batch) v.cu_blocks[b] = carry + excl;
+    if (b < batch) {
+      v.cu_blocks[b] = carry + excl;
+      if (cu_in_lds) s_cu[b] = carry + excl;
+    }
     carry += tot;
   }
-  if (t == 0) v.cu_blocks[batch] = carry;
+  if (t == 0) {
+    v.cu_blocks[batch] = carry;
+    if (cu_in_lds) s_cu[batch] = carry;
+  }
   __syncthreads();  // cu_blocks visible to the whole workgroup
 
   const int64_t total = (int64_t)row_split * carry;
@@ -99,9 +109,11 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
     int32_t ns = 0, first = -1;
     if (u < units) {
       const int b = u / row_split, g = u % row_split;
-      const int32_t nb = v.cu_blocks[b + 1] - v.cu_blocks[b];
+      const int32_t cb0 = cu_in_lds ? s_cu[b] : v.cu_blocks[b];
+      const int32_t cb1 = cu_in_lds ? s_cu[b + 1] : v.cu_blocks[b + 1];
+      const int32_t nb = cb1 - cb0;
       if (nb > 0) {
-        const int64_t start = (int64_t)row_split * v.cu_blocks[b] + (int64_t)g * nb;
+        const int64_t start = (int64_t)row_split * cb0 + (int64_t)g * nb;
         first = wg_of(start, total, num_wg);
         const int32_t last = wg_of(start + nb - 1, total, num_wg);
         ns = last - first + 1;
