@@ -315,21 +315,33 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   // workgroup's rows are contiguous in q, so they come in as (up to) two 64-row "pages"
   // through the page buffers, with the KV pages' column-block copies (whole 128-byte
   // lines per copy); each wave then reads its 32 rows' fragments.
+  // With 64 rows or fewer Q fits the second buffer, and page blk_lo streams into the
+  // first one meanwhile.
   bf16x8 qf[36];
+  const int nq = row_end - row0;
+  const bool q_one = nq <= 64;
+  const int* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  bool bad_page = false, first_issued = false;
   {
-    const int nq = row_end - row0;
     __syncthreads();   // LDS free (a previous segment may still be reading it)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (64 * h < nq) {
         const PageCopy qc{a.q + ((size_t)b * R + row0 + 64 * h) * kRowBytes, min(64, nq - 64 * h),
-                          lds + h * kBlockBytes};
+                          lds + (q_one ? 1 : h) * kBlockBytes};
 #pragma unroll
         for (int i = 0; i < 18; ++i) issue_col_copy(qc, i, w, l);
       }
-    wait_vm_barrier<0>();
+    if (q_one && blk_lo < blk_hi) {
+      const PageCopy first = page_copy(a, ld_const(bt_row, blk_lo), blk_lo, Lc, lds, bad_page);
+#pragma unroll
+      for (int i = 0; i < 18; ++i) issue_col_copy(first, i, w, l);
+      first_issued = true;
+    }
+    if (first_issued) wait_vm_barrier<18>();   // Q's copies (page blk_lo's may still fly)
+    else wait_vm_barrier<0>();
     const int rr = (32 * w + lr) & 63;                        // row within its 64-row half
-    const MLA_LDS uint8_t* qb = lds + (w >> 1) * kBlockBytes + rr * 128;
+    const MLA_LDS uint8_t* qb = lds + (q_one ? 1 : (w >> 1)) * kBlockBytes + rr * 128;
     const int sq = cswz(rr);
     const bool ok = myrow < row_end;
 #pragma unroll
@@ -343,7 +355,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 
   f32x16 o[4][NRT];
   float m_ref = -INFINITY, mtrue = -INFINITY, lsum = 0.f;
-  bool over = false, bad_page = false;
+  bool over = false;
   float mref_init = -INFINITY;
   for (int pass = 0; pass < 2; ++pass) {
     m_ref = mref_init;
@@ -359,8 +371,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       }
 
     __syncthreads();  // LDS free (a previous segment or pass may still be reading it)
-    const int* bt_row = a.block_table + (size_t)b * a.bt_stride;
-    if (blk_lo < blk_hi) {
+    if (blk_lo < blk_hi && !(pass == 0 && first_issued)) {
       const PageCopy first = page_copy(a, ld_const(bt_row, blk_lo), blk_lo, Lc, lds, bad_page);
 #pragma unroll
       for (int i = 0; i < 18; ++i) issue_col_copy(first, i, w, l);
