@@ -89,7 +89,7 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
 }
 
 // Workgroup-wide OR through 4 words of caller-provided LDS that no wave touches
-// between the two barriers (the wide split uses every byte of LDS, so the OR cannot
+// between the two barriers (the decode uses every byte of LDS, so the OR cannot
 // reserve its own).
 __device__ __forceinline__ bool wg_or(bool f, MLA_LDS int* scratch) {
   const int w = wave_id();
@@ -105,7 +105,7 @@ __device__ __forceinline__ bool wg_or(bool f, MLA_LDS int* scratch) {
 
 
 
-// Wide split (32x32x16 tiles).  S^T step: two 32-token tiles x the wave's 32 rows, one
+// Score step (32x32x16 tiles): two 32-token tiles x the wave's 32 rows, one
 // 16-dim K step; accumulators in VGPRs.
 __device__ __forceinline__ void mfma32_s_step(f32x16& s0, f32x16& s1, const bf16x8& k0, const bf16x8& k1,
                                               const bf16x8& q, int kk) {
@@ -204,7 +204,7 @@ __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int
 //   o[dt][rt] lane l, index 4i + j:  column 128w + 32dt + 8i + 4(l/32) + j,  row row0 + 32rt + l%32.
 // P buffer (16 KB after the two page buffers): [K step ks 0..3][row tile 0..3][lane][8 bf16],
 // the B operand of O^T += V^T . P^T for tokens 16ks .. 16ks + 15.
-// The wide split stores a page as 9 column blocks (dims 64c .. 64c + 63 of all 64
+// A page is stored in LDS as 9 column blocks (dims 64c .. 64c + 63 of all 64
 // tokens, 8 KB each, the rope block last): token t, 16-byte chunk p of block c at
 // c*8192 + t*128 + (p ^ cswz(t))*16.  The score loop walks the dims in block order, so it
 // can start on a page once its first blocks have landed.
