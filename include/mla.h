@@ -106,6 +106,7 @@ typedef struct {
   int32_t num_workgroups;      /* decode workgroups to spread the work over (default: one per CU) */
   int32_t min_blocks_per_wg;   /* smallest share of 64-token blocks per workgroup (default 4) */
   int32_t row_split;           /* split each sequence's rows over this many workgroups: 1, 2 or 4 (default 1) */
+  int32_t fixed_split_blocks;  /* > 0: batch-invariant plan (below); 0: balanced shares (default) */
 } mla_plan_options_t;
 
 /* Human-readable name of a status code (static string). */
@@ -153,6 +154,12 @@ typedef struct {
  * laid end to end and cut into num_workgroups contiguous, equal (+-1 block)
  * shares, so all CUs stream the same amount of KV; a sequence cut across k > 1
  * workgroups gets k partial results that mla_decode merges by log-sum-exp.
+ * With options->fixed_split_blocks = C > 0 the plan is batch-invariant instead: every
+ * sequence (row slice) is cut into chunks of C blocks from its own start, one chunk per
+ * workgroup, so where a sequence is split -- and so every bit of its output -- does
+ * not depend on the other sequences of the batch or on the CU count.  grid_wg is then
+ * batch * row_split * ceil(max_blocks_per_seq / C) (workgroups beyond the chunks exit;
+ * num_workgroups and min_blocks_per_wg are ignored).
  * One single-workgroup kernel launch on `stream`; fills the host fields of *plan.
  */
 MLA_API int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,

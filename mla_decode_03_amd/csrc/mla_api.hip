@@ -51,7 +51,7 @@ int32_t resolve_cus(int32_t num_cus, int32_t* out) {
 }
 
 struct PlanShape {
-  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials;
+  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials, fixed_blocks;
 };
 
 int32_t plan_shape(const mla_problem_t* p, const mla_plan_options_t* o, int32_t num_cus, PlanShape* s) {
@@ -66,14 +66,22 @@ int32_t plan_shape(const mla_problem_t* p, const mla_plan_options_t* o, int32_t 
   int rsplit = (o && o->row_split > 0) ? o->row_split : 1;
   if (rsplit != 1 && rsplit != 2 && rsplit != 4) return MLA_ERR_UNSUPPORTED;
   if (rows % rsplit != 0) return MLA_ERR_UNSUPPORTED;
+  const int fixed = (o && o->fixed_split_blocks > 0) ? o->fixed_split_blocks : 0;
+  const int64_t units = (int64_t)p->batch * rsplit;
+  if (fixed > 0) {
+    // one workgroup per chunk of `fixed` blocks, at most ceil(max_blocks / fixed) per unit
+    const int64_t g = units * ((p->max_blocks_per_seq + fixed - 1) / fixed);
+    if (g > 65536) return MLA_ERR_SHAPE;
+    grid = (int)(g > 0 ? g : 1);
+  }
   if (grid > 65536) return MLA_ERR_SHAPE;
   s->grid_wg = grid;
   s->row_split = rsplit;
   s->rows_per_wg = rows / rsplit;
   s->min_blocks = minb;
-  const int64_t units = (int64_t)p->batch * rsplit;
-  // each workgroup range holds at most one partial segment at each end
-  s->max_partials = (int)(grid + (units < grid ? units : grid));
+  s->fixed_blocks = fixed;
+  // each workgroup range holds at most one partial segment at each end (fixed chunks: one)
+  s->max_partials = fixed > 0 ? grid : (int)(grid + (units < grid ? units : grid));
   return MLA_OK;
 }
 
@@ -140,7 +148,7 @@ int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seql
   plan->rows = problem->q_len * problem->num_heads;
   if (mla_launch_plan(cache_seqlens, static_cast<int32_t*>(plan->metadata), problem->batch,
                       plan->rows, s.row_split, s.grid_wg, s.min_blocks, problem->max_blocks_per_seq,
-                      s.max_partials, static_cast<hipStream_t>(stream)) != hipSuccess)
+                      s.max_partials, s.fixed_blocks, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }

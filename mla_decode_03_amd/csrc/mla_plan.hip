@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ meta, int batch,
                                                        int rows, int row_split, int grid_wg,
                                                        int min_blocks, int max_blocks,
-                                                       int max_partials) {
+                                                       int max_partials, int fixed_blocks) {
   __shared__ int32_t s_scan[256];
   __shared__ int32_t s_cu[kPlanLdsBatch + 1];   // cu_blocks, when the batch fits
   const int t = threadIdx.x;
@@ -90,41 +90,75 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
   __syncthreads();  // cu_blocks visible to the whole workgroup
 
   const int64_t total = (int64_t)row_split * carry;
-  int64_t num_wg = 0;
-  if (total > 0) {
-    num_wg = (total + min_blocks - 1) / min_blocks;
-    if (num_wg > grid_wg) num_wg = grid_wg;
-    if (num_wg < 1) num_wg = 1;
-  }
-
-  // 2. workgroup shares
-  for (int w = t; w <= grid_wg; w += 256)
-    v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)floor_div((int64_t)w * total, num_wg) : (int32_t)total;
-
-  // 3. units: which workgroups cover each, and the partial slots of the split ones
   const int units = batch * row_split;
+  int64_t num_wg = 0;
   int32_t pcarry = 0;
-  for (int base = 0; base < units; base += 256) {
-    const int u = base + t;
-    int32_t ns = 0, first = -1;
-    if (u < units) {
-      const int b = u / row_split, g = u % row_split;
-      const int32_t cb0 = cu_in_lds ? s_cu[b] : v.cu_blocks[b];
-      const int32_t cb1 = cu_in_lds ? s_cu[b + 1] : v.cu_blocks[b + 1];
-      const int32_t nb = cb1 - cb0;
-      if (nb > 0) {
-        const int64_t start = (int64_t)row_split * cb0 + (int64_t)g * nb;
-        first = wg_of(start, total, num_wg);
-        const int32_t last = wg_of(start + nb - 1, total, num_wg);
-        ns = last - first + 1;
+  if (fixed_blocks > 0) {
+    // Batch-invariant plan: every unit cut into chunks of fixed_blocks blocks from its own
+    // start, one chunk per workgroup, in unit order.
+    int32_t ccarry = 0;
+    for (int base = 0; base < units; base += 256) {
+      const int u = base + t;
+      int32_t ns = 0;
+      int64_t ustart = 0;
+      if (u < units) {
+        const int b = u / row_split, g = u % row_split;
+        const int32_t cb0 = cu_in_lds ? s_cu[b] : v.cu_blocks[b];
+        const int32_t cb1 = cu_in_lds ? s_cu[b + 1] : v.cu_blocks[b + 1];
+        const int32_t nb = cb1 - cb0;
+        ustart = (int64_t)row_split * cb0 + (int64_t)g * nb;
+        ns = (nb + fixed_blocks - 1) / fixed_blocks;
       }
-      v.num_splits[u] = ns;
-      v.first_wg[u] = first;
+      int32_t ctot, ptot;
+      const int32_t first = ccarry + block_exclusive_scan(ns, s_scan, &ctot);
+      const int32_t poff = pcarry + block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &ptot);
+      if (u < units) {
+        v.num_splits[u] = ns;
+        v.first_wg[u] = ns > 0 ? first : -1;
+        v.part_off[u] = poff;
+        for (int k = 0; k < ns; ++k)
+          if (first + k < grid_wg) v.wg_begin[first + k] = (int32_t)(ustart + (int64_t)k * fixed_blocks);
+      }
+      ccarry += ctot;
+      pcarry += ptot;
     }
-    int32_t tot;
-    const int32_t excl = block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &tot);
-    if (u < units) v.part_off[u] = pcarry + excl;
-    pcarry += tot;
+    num_wg = ccarry;
+    if (num_wg > grid_wg) err = 1;   // cannot happen when grid_wg covers max_blocks
+    for (int w = (int)min<int64_t>(num_wg, grid_wg) + t; w <= grid_wg; w += 256) v.wg_begin[w] = (int32_t)total;
+  } else {
+    if (total > 0) {
+      num_wg = (total + min_blocks - 1) / min_blocks;
+      if (num_wg > grid_wg) num_wg = grid_wg;
+      if (num_wg < 1) num_wg = 1;
+    }
+
+    // 2. workgroup shares
+    for (int w = t; w <= grid_wg; w += 256)
+      v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)floor_div((int64_t)w * total, num_wg) : (int32_t)total;
+
+    // 3. units: which workgroups cover each, and the partial slots of the split ones
+    for (int base = 0; base < units; base += 256) {
+      const int u = base + t;
+      int32_t ns = 0, first = -1;
+      if (u < units) {
+        const int b = u / row_split, g = u % row_split;
+        const int32_t cb0 = cu_in_lds ? s_cu[b] : v.cu_blocks[b];
+        const int32_t cb1 = cu_in_lds ? s_cu[b + 1] : v.cu_blocks[b + 1];
+        const int32_t nb = cb1 - cb0;
+        if (nb > 0) {
+          const int64_t start = (int64_t)row_split * cb0 + (int64_t)g * nb;
+          first = wg_of(start, total, num_wg);
+          const int32_t last = wg_of(start + nb - 1, total, num_wg);
+          ns = last - first + 1;
+        }
+        v.num_splits[u] = ns;
+        v.first_wg[u] = first;
+      }
+      int32_t tot;
+      const int32_t excl = block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &tot);
+      if (u < units) v.part_off[u] = pcarry + excl;
+      pcarry += tot;
+    }
   }
 
   // 4. header (the error flag is the OR over threads)
@@ -146,7 +180,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
     v.hdr[kHdrError] = (s_err || pcarry > max_partials) ? 1 : 0;
     v.hdr[kHdrMaxPartials] = max_partials;
     v.hdr[kHdrMaxBlocks] = max_blocks;
-    if (pcarry > max_partials) v.hdr[kHdrNumWg] = 0;  // refuse to run a plan that overflows
+    if (pcarry > max_partials || num_wg > grid_wg) v.hdr[kHdrNumWg] = 0;  // refuse to run a plan that overflows
   }
 }
 
@@ -154,8 +188,8 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
 
 extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32_t* meta, int batch, int rows,
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
-                                      int max_partials, hipStream_t stream) {
+                                      int max_partials, int fixed_blocks, hipStream_t stream) {
   hipLaunchKernelGGL(mla::mla_plan_kernel, dim3(1), dim3(256), 0, stream, seqlens, meta, batch,
-                     rows, row_split, grid_wg, min_blocks, max_blocks, max_partials);
+                     rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks);
   return hipGetLastError();
 }

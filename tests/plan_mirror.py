@@ -15,13 +15,15 @@ from __future__ import annotations
 PAGE = 64
 
 
-def make_plan(seqlens, *, row_split=1, grid_wg=256, min_blocks=4, max_blocks=1 << 30):
+def make_plan(seqlens, *, row_split=1, grid_wg=256, min_blocks=4, max_blocks=1 << 30, fixed_blocks=0):
     B = len(seqlens)
     nblk = [min((max(int(L), 0) + PAGE - 1) // PAGE, max_blocks) for L in seqlens]
     cu = [0]
     for n in nblk:
         cu.append(cu[-1] + n)
     total = row_split * cu[B]
+    if fixed_blocks > 0:
+        return _fixed_plan(nblk, cu, total, row_split, grid_wg, fixed_blocks)
     num_wg = 0
     if total > 0:
         num_wg = max(1, min(grid_wg, -(-total // min_blocks)))
@@ -51,6 +53,29 @@ def make_plan(seqlens, *, row_split=1, grid_wg=256, min_blocks=4, max_blocks=1 <
         part_off.append(slot)
         if num_splits[-1] > 1:
             slot += num_splits[-1]
+    return dict(cu_blocks=cu, num_wg=num_wg, total=total, wg_begin=wg_begin, num_splits=num_splits,
+                first_wg=first_wg, part_off=part_off, num_partials=slot, row_split=row_split, batch=B)
+
+
+def _fixed_plan(nblk, cu, total, row_split, grid_wg, fixed):
+    """Batch-invariant rule: each unit cut into chunks of `fixed` blocks from its own
+    start, one chunk per workgroup, chunks numbered unit by unit."""
+    B = len(nblk)
+    wg_begin, num_splits, first_wg, part_off = [], [], [], []
+    slot = 0
+    for u in range(B * row_split):
+        b, g = divmod(u, row_split)
+        nb = nblk[b]
+        start = row_split * cu[b] + g * nb
+        k = -(-nb // fixed) if nb > 0 else 0
+        first_wg.append(len(wg_begin) if k > 0 else -1)
+        num_splits.append(k)
+        part_off.append(slot)
+        if k > 1:
+            slot += k
+        wg_begin += [start + i * fixed for i in range(k)]
+    num_wg = len(wg_begin)
+    wg_begin += [total] * (grid_wg + 1 - num_wg)
     return dict(cu_blocks=cu, num_wg=num_wg, total=total, wg_begin=wg_begin, num_splits=num_splits,
                 first_wg=first_wg, part_off=part_off, num_partials=slot, row_split=row_split, batch=B)
 

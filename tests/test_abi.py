@@ -94,6 +94,12 @@ def test_plan_sizes_and_workspace_checks():
     opts = m.PlanOptions(num_workgroups=8, min_blocks_per_wg=1, row_split=2)
     assert m.workspace_bytes(p, opts, 256) == (8 + 8) * 64 * (512 * 2 + 4)
     assert m.workspace_bytes(p, m.PlanOptions(row_split=3), 256) == 0  # unsupported split
+    # batch-invariant plan: one workgroup and one partial slot per possible chunk
+    fo = m.PlanOptions(fixed_split_blocks=5, row_split=2, num_workgroups=3)
+    grid = 4 * 2 * 4                                       # units * ceil(16 / 5)
+    assert m.metadata_bytes(p, fo, 256) == 4 * (16 + 5 + 3 * 8 + grid + 1)
+    assert m.workspace_bytes(p, fo, 256) == grid * 64 * (512 * 2 + 4)
+    assert m.workspace_bytes(p, fo, 80) == m.workspace_bytes(p, fo, 256)   # no CU dependence
     L = m.lib()
     a = ctypes.c_void_p(0x10000)
     # metadata buffer too small: refused before any launch

@@ -47,7 +47,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["plan", "forced_splits", "unsplit"])
+@pytest.mark.parametrize("mode", ["plan", "forced_splits", "unsplit", "fixed_splits"])
 @pytest.mark.parametrize("B,T,H,lens,causal", SMALL)
 def test_small_parity(B, T, H, lens, causal, mode):
     import mla_decode_03_amd as mla
@@ -59,6 +59,8 @@ def test_small_parity(B, T, H, lens, causal, mode):
         kw = dict(options=mla.PlanOptions(num_workgroups=7, min_blocks_per_wg=1))
     elif mode == "unsplit":
         kw = dict(split=False)
+    elif mode == "fixed_splits":
+        kw = dict(options=mla.PlanOptions(fixed_split_blocks=2))
     o, l, _ = run(case, **kw)
     compare(o, l, ref_o, ref_l, "small %s" % mode)
 
@@ -156,6 +158,65 @@ def test_device_plan_matches_mirror():
                                case.block_table.shape[1])
         assert list(words[:12]) == hdr
         assert list(words[16:16 + len(arrays)]) == arrays
+
+
+def test_device_fixed_plan_matches_mirror():
+    import torch
+    import mla_decode_03_amd as mla
+    from plan_mirror import make_plan, to_words
+    rng = np.random.default_rng(4)
+    lens = [int(x) for x in rng.integers(0, 5000, size=29)]
+    lens[5] = 0
+    case = _case(29, 1, 128, lens, seed=42)
+    q, kv, bt, lt = to_device(case)
+    maxb = case.block_table.shape[1]
+    for C, rs in ((3, 1), (16, 2), (1, 1)):
+        opts = mla.PlanOptions(fixed_split_blocks=C, row_split=rs)
+        dec = mla.Decoder(q, kv, bt, options=opts, num_cus=256)
+        plan = dec.plan_for(lt)
+        torch.cuda.synchronize()
+        grid = 29 * rs * (-(-maxb // C))
+        assert plan.grid_wg == grid and plan.max_partials == grid
+        words = plan.metadata.view(torch.int32).cpu().numpy()
+        ref = make_plan(lens, row_split=rs, grid_wg=grid, fixed_blocks=C)
+        hdr, arrays = to_words(ref, grid, 128, plan.max_partials, maxb)
+        say("fixed plan C=%d rs=%d: %d chunks of %d slots" % (C, rs, ref["num_wg"], grid))
+        assert list(words[:12]) == hdr
+        assert list(words[16:16 + len(arrays)]) == arrays
+
+
+def test_fixed_split_plan_is_batch_invariant():
+    """With fixed-size splits a sequence's output bits do not depend on the rest of the
+    batch (its position, its neighbours, the batch size) nor on the CU count; the balanced
+    plan gives no such promise.  Every run also meets the oracle."""
+    import torch
+    import mla_decode_03_amd as mla
+    lens = [3000, 129, 777, 64, 2500, 1]
+    case = _case(len(lens), 1, 128, lens, seed=71)
+    q, kv, bt, lt = to_device(case)
+    ref_o, ref_l = oracle_rows(case)
+    R = 128
+    opts = mla.PlanOptions(fixed_split_blocks=4)
+
+    def decode(idx, num_cus):
+        ix = torch.tensor(idx, device=q.device)
+        qs, bts, ls = q[ix].contiguous(), bt[ix].contiguous(), lt[ix].contiguous()
+        dec = mla.Decoder(qs, kv, bts, options=opts, num_cus=num_cus)
+        out, lse = dec(qs, kv, bts, ls, case.scale)
+        torch.cuda.synchronize()
+        return (out.view(torch.int16).cpu().numpy().reshape(len(idx), R, 512),
+                lse.cpu().numpy().reshape(len(idx), R))
+
+    full_o, full_l = decode(list(range(len(lens))), 256)
+    o64 = full_o.view(np.uint16).astype(np.uint32) << 16
+    compare(o64.view(np.float32).astype(np.float64).reshape(-1, 512), full_l.reshape(-1).astype(np.float64),
+            ref_o, ref_l, "fixed splits, whole batch")
+    for idx, cus in (([4, 0], 256), ([2, 2, 0, 5, 1], 80), ([0], 7), ([3, 4, 1, 0, 2, 5, 4], 256)):
+        say("  invariance", idx, cus)
+        o, l = decode(idx, cus)
+        for j, b in enumerate(idx):
+            assert np.array_equal(o[j], full_o[b]), (idx, j, b)
+            assert np.array_equal(l[j].view(np.uint32), full_l[b].view(np.uint32)), (idx, j, b)
 
 
 def test_bad_page_is_flagged_and_poisoned():

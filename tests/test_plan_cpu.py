@@ -67,3 +67,29 @@ def test_small_problem_is_not_over_split_and_empty_batch():
     assert plan["num_wg"] == 1 and plan["num_splits"] == [1, 1] and plan["num_partials"] == 0
     plan = make_plan([0, 0], grid_wg=8)
     assert plan["num_wg"] == 0 and plan["num_splits"] == [0, 0] and segments(plan) == []
+
+
+def test_fixed_split_plan_is_aligned_and_batch_invariant():
+    """Batch-invariant mode: chunks start at each sequence's own start, hold at most C
+    blocks, and a sequence's chunking is the same whatever else is in the batch."""
+    C = 4
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(0, 3000, size=9)]
+
+    def chunks_of(plan, b):
+        return [(lo, hi) for (_, bb, _, lo, hi, _) in segments(plan) if bb == b]
+
+    plan = make_plan(lens, grid_wg=10000, fixed_blocks=C)
+    for b, L in enumerate(lens):
+        nb = -(-L // 64)
+        ch = chunks_of(plan, b)
+        assert ch == [(s, min(s + C, nb)) for s in range(0, nb, C)]
+        assert plan["num_splits"][b] == len(ch)
+    # the same sequence in another batch, at another position
+    other = [17, lens[3], 5000, 1]
+    plan2 = make_plan(other, grid_wg=10000, fixed_blocks=C)
+    assert chunks_of(plan2, 1) == chunks_of(plan, 3)
+    # every chunk of a split sequence owns one slot, in chunk order
+    for (w, b, g, lo, hi, slot) in segments(plan):
+        if plan["num_splits"][b] > 1:
+            assert slot == plan["part_off"][b] + lo // C
