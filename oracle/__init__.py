@@ -56,7 +56,7 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-            ctypes.c_int32, ctypes.c_double,
+            ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
         lib.mla_oracle_max_threads.restype = ctypes.c_int32
@@ -70,13 +70,15 @@ def max_threads() -> int:
 
 def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32",
            causal: bool = False, rows=None, d_v: int = 512, page: int | None = None,
-           threads: int = 0):
+           threads: int = 0, sinks=None):
     """float64 MLA decode.
 
     q:  [B, T, H, d_qk] float32 values, or uint16 bf16 bits when dtype == "bf16"
     kv: [num_pages, page, d_qk] same dtype convention
     block_table: [B, stride] int32; cache_seqlens: [B] int32
     rows: optional flat row ids (b*T + t)*H + h to compute; default all rows.
+    sinks: optional per-head sink logits [H] (an extra softmax term with a zero value
+           row; see mla_oracle.c), taken as float64.
     Returns (out [n_rows, d_v] float64, lse [n_rows] float64), rows in the order asked.
     """
     q = np.ascontiguousarray(q)
@@ -97,12 +99,17 @@ def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32
     else:
         rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
         n_rows = rows_arr.size
+    sk = None
+    if sinks is not None:
+        sk = np.ascontiguousarray(sinks, dtype=np.float64)
+        assert sk.shape == (H,), sk.shape
     out = np.empty((n_rows, d_v), dtype=np.float64)
     lse = np.empty((n_rows,), dtype=np.float64)
     rc = _load().mla_oracle_decode(
         q.ctypes.data, kv.ctypes.data, DTYPE_CODES[dtype],
         bt.ctypes.data, bt.shape[1], lens.ctypes.data,
         B, T, H, npages, pg, d_qk, d_v, int(bool(causal)), float(scale),
+        sk.ctypes.data if sk is not None else None,
         rows_arr.ctypes.data if rows_arr is not None else None, n_rows,
         out.ctypes.data, lse.ctypes.data, int(threads))
     if rc != 0:
@@ -110,8 +117,8 @@ def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32
     return out, lse
 
 
-def decode_case(case, rows=None, threads: int = 0):
+def decode_case(case, rows=None, threads: int = 0, sinks=None):
     """decode() on a `mla_inputs.Case`."""
     return decode(case.q_array(), case.kv_array(), case.block_table, case.cache_seqlens,
                   scale=case.scale, dtype=case.dtype, causal=case.causal, rows=rows,
-                  threads=threads)
+                  threads=threads, sinks=sinks)

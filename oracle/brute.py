@@ -9,19 +9,21 @@ with values v_p = k_p[:d_v]:
     s_p   = scale * sum_d q[d] * k_p[d]
     lse   = log(sum_p exp(s_p))                (computed as m + log(sum exp(s_p - m)))
     out_d = sum_p exp(s_p - lse) * v_p[d]
+With a sink logit sigma (attention-sink reading: one more term in the softmax, with a
+zero value row) the score list gains sigma and the value sum does not.
 """
 from __future__ import annotations
 
 import math
 
 
-def attend_row(q, keys, scale, d_v):
-    """Return (out list[d_v], lse float).  Empty `keys` -> zeros and -inf."""
-    if not keys:
+def attend_row(q, keys, scale, d_v, sink=None):
+    """Return (out list[d_v], lse float).  Empty `keys` and no sink -> zeros and -inf."""
+    if not keys and sink is None:
         return [0.0] * d_v, -math.inf
     s = [scale * math.fsum(qd * kd for qd, kd in zip(q, k)) for k in keys]
-    m = max(s)
+    m = max(s + ([sink] if sink is not None else []))
     w = [math.exp(x - m) for x in s]
-    tot = math.fsum(w)
+    tot = math.fsum(w + ([math.exp(sink - m)] if sink is not None else []))
     out = [math.fsum(wp * k[d] for wp, k in zip(w, keys)) / tot for d in range(d_v)]
     return out, m + math.log(tot)

@@ -31,6 +31,16 @@
  * and bitwise alignment asks for IEEE behaviour by default).
  *
  * Degenerate rows: a row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Attention sinks (optional).  The TileLang notes list an attention-sink variant of
+ * MHA a few lines away from the standard kernel (main results table and the
+ * programmability remarks after it) without writing it out.  Reading taken: head h
+ * has one sink logit sigma_h that takes part in the softmax like an extra key with
+ * score sigma_h (already in score units: not multiplied by `scale`) and a value row
+ * of zeros.  So, with the sink, the weights are exp(s_p) / (exp(sigma_h) +
+ * sum_q exp(s_q)), out is their sum over the real value rows, and lse is the natural
+ * log of that whole denominator.  A row with no visible key then gets out = 0 and
+ * lse = sigma_h; sigma_h = -inf is the plain decode.
  */
 #include <math.h>
 #include <stdint.h>
@@ -63,6 +73,7 @@ static int64_t visible(int64_t seqlen, int32_t q_len, int32_t t, int32_t causal)
 
 /*
  * Decode the requested rows.
+ *   sinks        per-head sink logits [heads] (double), or NULL for none
  *   q            [batch, q_len, heads, d_qk]           (dtype)
  *   kv           [num_pages, page, d_qk]               (dtype)
  *   block_table  int32, row b at block_table + b*bt_stride
@@ -76,7 +87,7 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
                       const int32_t* cache_seqlens,
                       int32_t batch, int32_t q_len, int32_t heads,
                       int64_t num_pages, int32_t page, int32_t d_qk, int32_t d_v,
-                      int32_t causal, double scale,
+                      int32_t causal, double scale, const double* sinks,
                       const int64_t* rows, int64_t n_rows,
                       double* out, double* lse, int32_t n_threads) {
   if (!q || !kv || !block_table || !cache_seqlens || !out || !lse) return ORACLE_ERR_ARG;
@@ -119,6 +130,9 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
       }
       const int32_t b = (int32_t)(r / ((int64_t)q_len * heads));
       const int32_t t = (int32_t)((r / heads) % q_len);
+      const int32_t h = (int32_t)(r % heads);
+      const double sink = sinks ? sinks[h] : -INFINITY;
+      const int has_sink = sink > -INFINITY || isnan(sink);
       const int64_t n = visible(cache_seqlens[b], q_len, t, causal);
       double* o = out + i * d_v;
 
@@ -134,7 +148,7 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
         err = ORACLE_ERR_PAGE;
         continue;
       }
-      if (n == 0) {
+      if (n == 0 && !has_sink) {
         for (int32_t d = 0; d < d_v; ++d) o[d] = 0.0;
         lse[i] = -INFINITY;
         continue;
@@ -147,12 +161,13 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
           dot += load_elem(q, dtype, qbase + d) * load_elem(kv, dtype, kbase[p] + d);
         s[p] = scale * dot;
       }
-      /* pass 1: maximum score */
-      double m = s[0];
-      for (int64_t p = 1; p < n; ++p)
+      /* pass 1: maximum score (the sink counts as one more score) */
+      double m = has_sink ? sink : s[0];
+      for (int64_t p = 0; p < n; ++p)
         if (s[p] > m) m = s[p];
-      /* pass 2: shifted exponentials, their sum, and the weighted sum of value rows */
-      double l = 0.0;
+      /* pass 2: shifted exponentials, their sum, and the weighted sum of value rows;
+         the sink adds its exponential to the sum and nothing to the values */
+      double l = has_sink ? exp(sink - m) : 0.0;
       for (int32_t d = 0; d < d_v; ++d) acc[d] = 0.0;
       for (int64_t p = 0; p < n; ++p) {
         const double w = exp(s[p] - m);

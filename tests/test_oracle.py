@@ -237,3 +237,65 @@ def test_bad_page_is_reported():
     case.block_table[0, 1] = case.num_pages + 5
     with pytest.raises(RuntimeError):
         oracle.decode_case(case)
+
+
+# ---- attention sinks: one more softmax term per head, with a zero value row -------------
+
+def test_sink_hand_worked_two_keys():
+    g = json.load(open(os.path.join(HERE, "golden", "hand_two_keys_sink.json")))
+    q = np.array(g["q"], dtype=np.float32).reshape(1, 1, 1, 2)
+    kv = np.array(g["keys"], dtype=np.float32).reshape(1, 2, 2)
+    bt = np.zeros((1, 1), dtype=np.int32)
+    out, lse = oracle.decode(q, kv, bt, np.array([2], np.int32), scale=g["scale"], d_v=g["d_v"],
+                             sinks=[g["sink"]])
+    assert abs(out[0, 0] - g["out"][0]) < 1e-7
+    assert abs(lse[0] - g["lse"]) < 1e-7
+
+
+@pytest.mark.parametrize("causal,T", [(False, 1), (True, 2)])
+def test_sink_brute_force_tiny(causal, T):
+    """The C oracle with sinks against the pure-Python brute force (the sink appended to
+    the score list), real dims, a page crossing, permuted pages, an empty causal row."""
+    lens = [70, 1] if T == 1 else [66, 1]
+    H = 3
+    case = _f32_case(2, T, H, lens, seed=80 + T, causal=causal)
+    sinks = np.array([0.75, -2.0, 40.0])          # the last one outweighs every key
+    out, lse = oracle.decode_case(case, sinks=sinks)
+    for b in range(2):
+        keys = [list(k) for k in _logical_keys(case, b)]
+        L = len(keys)
+        for t in range(T):
+            n = L - T + 1 + t if causal else L
+            for h in range(H):
+                r = (b * T + t) * H + h
+                ref, ref_lse = brute.attend_row(list(case.q[b, t, h].astype(np.float64)),
+                                                keys[:max(n, 0)], case.scale, D_V, sink=float(sinks[h]))
+                np.testing.assert_allclose(out[r], ref, rtol=0, atol=1e-12)
+                assert abs(lse[r] - ref_lse) < 1e-12 * max(1.0, abs(ref_lse))
+
+
+def test_sink_rescales_the_plain_result():
+    """Identity of the reading: adding a term e^sigma to the denominator scales every
+    weight by Z / (Z + e^sigma) with Z = e^lse, so out_sink = out / (1 + e^(sigma - lse))
+    and lse_sink = ln(e^lse + e^sigma).  A sink that leaked into the values, or that was
+    left out of lse, fails this."""
+    case = _f32_case(2, 2, 4, [130, 9], seed=82, causal=True)
+    plain_o, plain_l = oracle.decode_case(case)
+    sinks = np.array([-1.0, 0.5, 3.0, 12.0])
+    o, l = oracle.decode_case(case, sinks=sinks)
+    h = np.arange(plain_l.size) % 4
+    sig = sinks[h]
+    np.testing.assert_allclose(l, np.logaddexp(plain_l, sig), rtol=1e-14, atol=1e-14)
+    factor = 1.0 / (1.0 + np.exp(sig - plain_l))
+    np.testing.assert_allclose(o, plain_o * factor[:, None], rtol=1e-12, atol=1e-15)
+
+
+def test_sink_minus_inf_is_the_plain_decode_and_empty_rows_take_the_sink():
+    case = _f32_case(2, 2, 2, [1, 40], seed=83, causal=True)
+    o0, l0 = oracle.decode_case(case)
+    o1, l1 = oracle.decode_case(case, sinks=[-np.inf, -np.inf])
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    o2, l2 = oracle.decode_case(case, sinks=[1.5, -3.0])
+    # b=0, t=0 sees no key: out 0, lse = its head's sink
+    assert np.all(o2[0] == 0.0) and l2[0] == 1.5
+    assert np.all(o2[1] == 0.0) and l2[1] == -3.0
