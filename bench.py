@@ -86,6 +86,10 @@ def main():
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--min-blocks", type=int, default=0)
     ap.add_argument("--row-split", type=int, default=0)
+    ap.add_argument("--fixed-split-blocks", type=int, default=0,
+                    help="batch-invariant plan: fixed chunks of this many 64-token blocks")
+    ap.add_argument("--sinks", action="store_true",
+                    help="attention-sink variant (seeded per-head sink logits)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device to device 3 times (the reference "
                          "dispatch that scales the HBM byte counters of a profiled run)")
@@ -101,7 +105,7 @@ def main():
     import numpy as np
     import torch
     import mla_decode_03_amd as mla
-    from mla_inputs import CONFIGS, make_config
+    from mla_inputs import CONFIGS, make_config, make_sinks
 
     mla.lib()
     dev = torch.device("cuda:0")
@@ -120,10 +124,11 @@ def main():
     B, T, H = case.batch, case.q_len, case.num_heads
     out = torch.empty((B, T, H, 512), dtype=q.dtype, device=dev)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    sinks = torch.from_numpy(make_sinks(H, seed=1)).to(dev) if args.sinks else None
     opts = None
-    if args.num_workgroups or args.min_blocks or args.row_split:
+    if args.num_workgroups or args.min_blocks or args.row_split or args.fixed_split_blocks:
         opts = mla.PlanOptions(num_workgroups=args.num_workgroups, min_blocks_per_wg=args.min_blocks,
-                               row_split=args.row_split)
+                               row_split=args.row_split, fixed_split_blocks=args.fixed_split_blocks)
     split = case.dtype == "bf16"
     dec = mla.Decoder(q, kv_a, bt, causal=case.causal, split=split, options=opts)
     pools = (kv_a, kv_b)
@@ -132,15 +137,16 @@ def main():
     def step(i, events=None):
         kv = pools[i & 1]
         if not split:
-            mla.decode(dec.problem, q, kv, bt, lens, case.scale, out, lse, None, None, stream)
+            mla.decode(dec.problem, q, kv, bt, lens, case.scale, out, lse, None, None, stream, sinks)
             return
         plan = dec.plan_for(lens, stream)
         if events is not None:
             events[0].record(stream)
-        mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace, stream)
+        mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace, stream,
+                          sinks)
         if events is not None:
             events[1].record(stream)
-        mla.combine(dec.problem, out, lse, plan, dec.workspace, stream)
+        mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks)
 
     for i in range(args.warmup):
         step(i)
@@ -211,7 +217,9 @@ def main():
         "config": {"workload": CONFIGS[args.config]["name"], "batch": B, "heads": H, "q_len": T,
                    "seqlen": int(case.cache_seqlens.max()), "page": 64, "d_qk": 576, "d_v": 512,
                    "causal": case.causal, "kv_pools_alternated": 2,
-                   "plan": {"num_workgroups": dec.plan.grid_wg if dec.plan else None}},
+                   "variant": "attention_sink" if args.sinks else "plain",
+                   "plan": {"num_workgroups": dec.plan.grid_wg if dec.plan else None,
+                            "fixed_split_blocks": args.fixed_split_blocks or None}},
         "kv_gb_per_s": round(kv_gbs, 1),
         "frac_hbm_total_bytes": round(frac_hbm, 4),
         "frac_mfma_bf16": round(frac_mfma, 4),

@@ -19,6 +19,16 @@
  *     out[d] = sum_p exp(s_p - lse) * k_p[d]        for d < 512   (V = first 512 dims)
  *   A row with n == 0 gets out = 0 and lse = -inf.
  *
+ * Attention sinks (mla_decode_ex with variant->sinks != NULL).  The TileLang notes name
+ * an attention-sink variant of attention a few lines away from the standard kernel (main
+ * results table, and the programmability remarks after it) without writing it out.
+ * This library reads it as one more softmax term per head: a logit sinks[h], in score
+ * units (the scale does not multiply it), whose value row is zero:
+ *     lse    = ln(exp(sinks[h]) + sum_p exp(s_p))
+ *     out[d] = sum_p exp(s_p - lse) * k_p[d]
+ *   A row with n == 0 then gets out = 0 and lse = sinks[h]; sinks[h] = -inf is the
+ *   plain decode for head h, bit for bit.
+ *
  * Sizes fixed by the library: 576-wide cache rows (512 latent + 64 rope), 512-wide
  * values, 64-token pages.  q_len * num_heads (rows per sequence) must be <= 128.
  *
@@ -109,6 +119,11 @@ typedef struct {
   int32_t fixed_split_blocks;  /* > 0: batch-invariant plan (below); 0: balanced shares (default) */
 } mla_plan_options_t;
 
+/* Variants of the operation.  NULL (or every field NULL) = plain MLA decode. */
+typedef struct {
+  const float* sinks;          /* DEVICE float32 [num_heads] attention-sink logits, or NULL */
+} mla_variant_t;
+
 /* Human-readable name of a status code (static string). */
 MLA_API const char* mla_status_string(int32_t status);
 
@@ -186,22 +201,39 @@ MLA_API int32_t mla_decode(const mla_problem_t* problem,
                    void* stream);
 
 /*
- * The two launches of mla_decode, for callers (and benchmarks) that want them apart.
+ * mla_decode with a variant of the operation (see the top of this file): identical
+ * arguments, plus `variant` (NULL = mla_decode).  sinks must be 4-byte aligned
+ * (MLA_ERR_ALIGN) and is read on the device only.  The sink enters each row once, where
+ * its final result is formed: in the decode kernel for an unsplit sequence, in the
+ * combine for a split one (partials never include it), so split and unsplit plans
+ * agree to rounding.
+ */
+MLA_API int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t* variant,
+                              const void* q, const void* kv_cache,
+                              const int32_t* block_table, const int32_t* cache_seqlens,
+                              float scale, void* out, float* lse,
+                              const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * The two launches of mla_decode_ex, for callers (and benchmarks) that want them apart.
  * mla_decode_splits: the split-KV decode kernel alone -- writes out/lse of every
  *   sequence the plan did not split, and the partials of the split ones into
  *   `workspace` (per split: normalised output rounded to bf16, natural-log LSE in
  *   float32).
  * mla_combine: merges those partials by log-sum-exp into out/lse (sequences with no
  *   cached tokens get out = 0, lse = -inf).  Same plan and workspace as the decode.
- * Both require a plan and a bf16 problem; mla_decode(plan != NULL) == splits + combine.
+ * Both require a plan and a bf16 problem, and take the same `variant` (NULL = plain);
+ * mla_decode_ex(plan != NULL) == splits + combine.
  */
-MLA_API int32_t mla_decode_splits(const mla_problem_t* problem,
+MLA_API int32_t mla_decode_splits(const mla_problem_t* problem, const mla_variant_t* variant,
                                   const void* q, const void* kv_cache,
                                   const int32_t* block_table, const int32_t* cache_seqlens,
                                   float scale, void* out, float* lse,
                                   const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
                                   void* stream);
-MLA_API int32_t mla_combine(const mla_problem_t* problem, void* out, float* lse,
+MLA_API int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant,
+                            void* out, float* lse,
                             const mla_plan_t* plan, const void* workspace, size_t workspace_bytes,
                             void* stream);
 

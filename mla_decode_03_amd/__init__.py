@@ -13,6 +13,8 @@ The C ABI (include/mla.h) defines the operation:
 
 over the cached rows k_p (576 wide) of sequence b, gathered from 64-token pages
 through the block table, with optional causal masking among the q_len new tokens.
+With `sinks` (float32 [H] on the device) head h's softmax gains one more term
+exp(sinks[h]) whose value row is zero (attention sinks; mla_decode_ex).
 """
 from __future__ import annotations
 
@@ -103,32 +105,44 @@ def get_metadata(problem: Problem, cache_seqlens, metadata, options: PlanOptions
     return Plan(metadata, c_plan)
 
 
+def _variant(sinks):
+    """ctypes variant argument: None (plain decode) or a pointer to an mla_variant_t."""
+    if sinks is None:
+        return None
+    return ctypes.byref(_abi.Variant(sinks=sinks.data_ptr()))
+
+
 def decode(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: float, out, lse,
-           plan: Plan | None = None, workspace=None, stream=None) -> None:
-    """Enqueue the decode; outputs are written into `out` and `lse` (caller-owned)."""
+           plan: Plan | None = None, workspace=None, stream=None, sinks=None) -> None:
+    """Enqueue the decode; outputs are written into `out` and `lse` (caller-owned).
+    `sinks` (float32 [H] device tensor) selects the attention-sink variant (mla_decode_ex)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().mla_decode(ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(block_table),
-                          _ptr(cache_seqlens), ctypes.c_float(scale), _ptr(out), _ptr(lse),
-                          ctypes.byref(plan.c_plan) if plan is not None else None,
-                          _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
-    _abi.check(rc, "mla_decode")
+    args = (_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), ctypes.c_float(scale),
+            _ptr(out), _ptr(lse), ctypes.byref(plan.c_plan) if plan is not None else None,
+            _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    if sinks is None:
+        _abi.check(lib().mla_decode(ctypes.byref(problem), *args), "mla_decode")
+    else:
+        _abi.check(lib().mla_decode_ex(ctypes.byref(problem), _variant(sinks), *args), "mla_decode_ex")
 
 
 def decode_splits(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: float, out, lse,
-                  plan: Plan, workspace, stream=None) -> None:
+                  plan: Plan, workspace, stream=None, sinks=None) -> None:
     """Enqueue only the split-KV decode kernel (partials for split sequences)."""
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = lib().mla_decode_splits(ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+    rc = lib().mla_decode_splits(ctypes.byref(problem), _variant(sinks), _ptr(q), _ptr(kv_cache),
+                                 _ptr(block_table),
                                  _ptr(cache_seqlens), ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                  ctypes.byref(plan.c_plan), _ptr(workspace), ctypes.c_size_t(ws_bytes),
                                  _stream_handle(stream))
     _abi.check(rc, "mla_decode_splits")
 
 
-def combine(problem: Problem, out, lse, plan: Plan, workspace, stream=None) -> None:
+def combine(problem: Problem, out, lse, plan: Plan, workspace, stream=None, sinks=None) -> None:
     """Enqueue only the log-sum-exp combine of the split partials."""
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = lib().mla_combine(ctypes.byref(problem), _ptr(out), _ptr(lse), ctypes.byref(plan.c_plan),
+    rc = lib().mla_combine(ctypes.byref(problem), _variant(sinks), _ptr(out), _ptr(lse),
+                           ctypes.byref(plan.c_plan),
                            _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
     _abi.check(rc, "mla_combine")
 
@@ -168,7 +182,7 @@ class Decoder:
         return self.plan
 
     def __call__(self, q, kv_cache, block_table, cache_seqlens, scale: float, out=None, lse=None,
-                 replan: bool = True, stream=None):
+                 replan: bool = True, stream=None, sinks=None):
         import torch
         B, T, H, _ = q.shape
         if out is None:
@@ -178,7 +192,7 @@ class Decoder:
         if replan or self.plan is None:
             self.plan_for(cache_seqlens, stream)
         decode(self.problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse,
-               self.plan, self.workspace, stream)
+               self.plan, self.workspace, stream, sinks)
         return out, lse
 
 

@@ -24,7 +24,8 @@ MLA_ERR_BAD_INPUT = 9
 
 # Exported functions, as declared in include/mla.h.
 EXPORTS = ("mla_status_string", "mla_device_num_cus", "mla_metadata_bytes", "mla_workspace_bytes",
-           "mla_get_metadata", "mla_decode", "mla_decode_splits", "mla_combine", "mla_plan_error")
+           "mla_get_metadata", "mla_decode", "mla_decode_ex", "mla_decode_splits", "mla_combine",
+           "mla_plan_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmla.so")
@@ -48,6 +49,10 @@ class Problem(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("num_workgroups", ctypes.c_int32), ("min_blocks_per_wg", ctypes.c_int32),
                 ("row_split", ctypes.c_int32), ("fixed_split_blocks", ctypes.c_int32)]
+
+
+class Variant(ctypes.Structure):
+    _fields_ = [("sinks", ctypes.c_void_p)]
 
 
 class CPlan(ctypes.Structure):
@@ -84,11 +89,15 @@ def lib():
         L.mla_decode.restype = i32
         L.mla_decode.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                  ctypes.POINTER(CPlan), vp, sz, vp]
+        V = ctypes.POINTER(Variant)
+        L.mla_decode_ex.restype = i32
+        L.mla_decode_ex.argtypes = [ctypes.POINTER(Problem), V, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                    ctypes.POINTER(CPlan), vp, sz, vp]
         L.mla_decode_splits.restype = i32
-        L.mla_decode_splits.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, ctypes.c_float, vp, vp,
+        L.mla_decode_splits.argtypes = [ctypes.POINTER(Problem), V, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                         ctypes.POINTER(CPlan), vp, sz, vp]
         L.mla_combine.restype = i32
-        L.mla_combine.argtypes = [ctypes.POINTER(Problem), vp, vp, ctypes.POINTER(CPlan), vp, sz, vp]
+        L.mla_combine.argtypes = [ctypes.POINTER(Problem), V, vp, vp, ctypes.POINTER(CPlan), vp, sz, vp]
         L.mla_plan_error.restype = i32
         L.mla_plan_error.argtypes = [ctypes.POINTER(CPlan), vp]
         _lib = L

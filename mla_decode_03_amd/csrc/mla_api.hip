@@ -188,6 +188,15 @@ int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* 
   a->ws_lse = nullptr;
   a->rows_per_wg = a->rows;
   a->row_split = 1;
+  a->sinks = nullptr;
+  return MLA_OK;
+}
+
+// Reads the variant into *a (NULL = the plain operation).
+int32_t attach_variant(const mla_variant_t* variant, mla::DecodeArgs* a) {
+  if (!variant) return MLA_OK;
+  if (variant->sinks && !aligned(variant->sinks, 4)) return MLA_ERR_ALIGN;
+  a->sinks = variant->sinks;
   return MLA_OK;
 }
 
@@ -223,6 +232,8 @@ int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
   c.rows = a.rows;
   c.rows_per_wg = a.rows_per_wg;
   c.row_split = a.row_split;
+  c.heads = a.heads;
+  c.sinks = a.sinks;
   return mla_launch_combine(&c, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
@@ -232,6 +243,14 @@ int32_t mla_decode(const mla_problem_t* problem, const void* q, const void* kv_c
                    const int32_t* block_table, const int32_t* cache_seqlens, float scale, void* out,
                    float* lse, const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
                    void* stream) {
+  return mla_decode_ex(problem, nullptr, q, kv_cache, block_table, cache_seqlens, scale, out, lse, plan,
+                       workspace, workspace_bytes, stream);
+}
+
+int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t* variant, const void* q,
+                      const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                      float scale, void* out, float* lse, const mla_plan_t* plan, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int32_t rc = check_problem(problem);
   if (rc != MLA_OK) return rc;
   if (problem->batch == 0) return MLA_OK;
@@ -240,6 +259,8 @@ int32_t mla_decode(const mla_problem_t* problem, const void* q, const void* kv_c
     mla::DecodeArgs d;
     rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &d);
     if (rc != MLA_OK) return rc;
+    rc = attach_variant(variant, &d);
+    if (rc != MLA_OK) return rc;
     mla::F32Args a;
     a.q = static_cast<const float*>(q);
     a.kv = static_cast<const float*>(kv_cache);
@@ -247,6 +268,7 @@ int32_t mla_decode(const mla_problem_t* problem, const void* q, const void* kv_c
     a.seqlens = cache_seqlens;
     a.out = static_cast<float*>(out);
     a.lse = lse;
+    a.sinks = d.sinks;
     a.scale = scale;
     a.batch = d.batch;
     a.rows = d.rows;
@@ -261,6 +283,8 @@ int32_t mla_decode(const mla_problem_t* problem, const void* q, const void* kv_c
   mla::DecodeArgs a;
   rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &a);
   if (rc != MLA_OK) return rc;
+  rc = attach_variant(variant, &a);
+  if (rc != MLA_OK) return rc;
   if (!plan) return mla_launch_decode_bf16(&a, problem->batch, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
@@ -268,7 +292,8 @@ int32_t mla_decode(const mla_problem_t* problem, const void* q, const void* kv_c
   return launch_combine(a, st);
 }
 
-int32_t mla_decode_splits(const mla_problem_t* problem, const void* q, const void* kv_cache,
+int32_t mla_decode_splits(const mla_problem_t* problem, const mla_variant_t* variant, const void* q,
+                          const void* kv_cache,
                           const int32_t* block_table, const int32_t* cache_seqlens, float scale,
                           void* out, float* lse, const mla_plan_t* plan, void* workspace,
                           size_t workspace_bytes, void* stream) {
@@ -279,14 +304,16 @@ int32_t mla_decode_splits(const mla_problem_t* problem, const void* q, const voi
   mla::DecodeArgs a;
   rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &a);
   if (rc != MLA_OK) return rc;
+  rc = attach_variant(variant, &a);
+  if (rc != MLA_OK) return rc;
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
   return mla_launch_decode_bf16(&a, plan->grid_wg, static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
-int32_t mla_combine(const mla_problem_t* problem, void* out, float* lse, const mla_plan_t* plan,
-                    const void* workspace, size_t workspace_bytes, void* stream) {
+int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant, void* out, float* lse,
+                    const mla_plan_t* plan, const void* workspace, size_t workspace_bytes, void* stream) {
   int32_t rc = check_problem(problem);
   if (rc != MLA_OK) return rc;
   if (problem->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
@@ -298,6 +325,9 @@ int32_t mla_combine(const mla_problem_t* problem, void* out, float* lse, const m
   a.lse = lse;
   a.batch = problem->batch;
   a.rows = problem->q_len * problem->num_heads;
+  a.heads = problem->num_heads;
+  rc = attach_variant(variant, &a);
+  if (rc != MLA_OK) return rc;
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
   return launch_combine(a, static_cast<hipStream_t>(stream));

@@ -17,6 +17,7 @@ struct DecodeArgs {
   int32_t* meta;               // plan, or nullptr (one workgroup per sequence)
   uint16_t* ws_o;              // partial outputs, bf16 [slots, rows_per_wg, 512]
   float* ws_lse;               // partial log-sum-exp [slots, rows_per_wg]
+  const float* sinks;          // attention-sink logits [heads], or nullptr
   float scale_log2;            // scale * log2(e)
   int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
   int rows_per_wg, row_split;
@@ -28,7 +29,8 @@ struct CombineArgs {
   const float* ws_lse;
   uint16_t* out;    // bf16 [B, R, 512]
   float* lse;       // [B, R]
-  int batch, rows, rows_per_wg, row_split;
+  const float* sinks;  // attention-sink logits [heads], or nullptr
+  int batch, rows, rows_per_wg, row_split, heads;
 };
 
 struct F32Args {
@@ -38,6 +40,7 @@ struct F32Args {
   const int32_t* seqlens;      // [B]
   float* out;                  // [B, R, 512]
   float* lse;                  // [B, R]
+  const float* sinks;          // attention-sink logits [heads], or nullptr
   float scale;
   int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
 };

@@ -7,6 +7,8 @@
 //     out = sum_s exp(lse_s - lse) * o_s
 // A partial with lse_s = -inf weighs 0; a NaN partial (a poisoned segment) makes the row NaN.  Units with no blocks at all get out = 0,
 // lse = -inf.  Units decoded by one workgroup were written directly and are skipped.
+// With attention sinks the merged row takes its head's sink here (one more softmax term
+// with a zero value row): the partials never include it.
 // Memory-bound: 8 rows per workgroup, 32 threads per row, 16 output dims per thread.
 #include "mla_args.h"
 #include "mla_device.h"
@@ -31,7 +33,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   if (ns == 0) {
     *(u32x4*)orow = u32x4{0u, 0u, 0u, 0u};
     *(u32x4*)(orow + 8) = u32x4{0u, 0u, 0u, 0u};
-    if (t == 0) a.lse[(size_t)b * a.rows + r] = -INFINITY;
+    if (t == 0) a.lse[(size_t)b * a.rows + r] = a.sinks ? a.sinks[r % a.heads] : -INFINITY;
     return;
   }
   const int s0 = v.part_off[u];
@@ -79,14 +81,20 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
       if (base + k < ns) accumulate(expf(ls[k] - Ms), x[k][0], x[k][1]);
   }
   const bool empty = tot == 0.f;  // NaN (a poisoned split) propagates
-  const float inv = empty ? 0.f : 1.f / tot;
+  float inv = empty ? 0.f : 1.f / tot;
+  float lse_v = empty ? -INFINITY : Ms + logf(tot);
+  if (a.sinks) {
+    const SinkFold f = fold_sink<false>(Ms, tot, a.sinks[r % a.heads]);
+    inv = f.scale_o;
+    lse_v = f.lse;
+  }
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     packed[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   *(u32x4*)orow = u32x4{packed[0], packed[1], packed[2], packed[3]};
   *(u32x4*)(orow + 8) = u32x4{packed[4], packed[5], packed[6], packed[7]};
-  if (t == 0) a.lse[(size_t)b * a.rows + r] = empty ? -INFINITY : Ms + logf(tot);
+  if (t == 0) a.lse[(size_t)b * a.rows + r] = lse_v;
 }
 
 }  // namespace mla

@@ -508,13 +508,30 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   // ---- epilogue: every wave needs the row statistics of all 128 rows ---------------------
   const bool poison = bad_len || wg_or(bad_page, (MLA_LDS int*)pbuf);
   if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
-  MLA_LDS float* stats = (MLA_LDS float*)pbuf;   // [row][m, lsum]
+  // Per row, once: the factor that normalises O and the natural-log LSE.  The attention
+  // sink enters a row once, where its final result is formed: here for an unsplit range,
+  // in the combine for the partials of a split one.
+  MLA_LDS float* stats = (MLA_LDS float*)pbuf;   // [row][scale_o, lse]
+  const float nanv = __builtin_nanf("");
   if (g == 0) {
-    stats[2 * (32 * w + lr)] = m_ref;
-    stats[2 * (32 * w + lr) + 1] = lsum;
+    const int rr = 32 * w + lr;
+    float so, lse_v;
+    if (poison) {
+      so = nanv;
+      lse_v = nanv;
+    } else if (slot < 0 && a.sinks) {
+      const SinkFold f = fold_sink<true>(m_ref, lsum, a.sinks[(row0 + rr) % a.heads] * kLog2e);
+      so = f.scale_o;
+      lse_v = f.lse * kLn2;
+    } else {
+      const bool empty = lsum == 0.f;   // no visible key; NaN propagates
+      so = empty ? 0.f : 1.f / lsum;
+      lse_v = empty ? -INFINITY : (m_ref + __log2f(lsum)) * kLn2;
+    }
+    stats[2 * rr] = so;
+    stats[2 * rr + 1] = lse_v;
   }
   __syncthreads();
-  const float nanv = __builtin_nanf("");
   // O (normalised, bf16) goes through LDS so that every store writes a whole 1 KB row:
   // row rr of the workgroup at rr*1024, 16-byte chunk c (values 8c .. 8c+7) at
   // (c ^ (rr & 15))*16.  The page buffers are idle now.
@@ -522,9 +539,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int rr = 32 * rt + lr;
-    const float ls = stats[2 * rr + 1];
-    const bool empty = ls == 0.f;   // no visible key; NaN propagates
-    const float scale_o = poison ? nanv : (empty ? 0.f : 1.f / ls);
+    const float scale_o = stats[2 * rr];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -547,9 +562,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   }
   if (threadIdx.x < 128 && row0 + (int)threadIdx.x < row_end) {
     const int rr = threadIdx.x;
-    const float mr = stats[2 * rr], ls = stats[2 * rr + 1];
-    const bool empty = ls == 0.f;
-    const float lse_v = poison ? nanv : (empty ? -INFINITY : (mr + __log2f(ls)) * kLn2);
+    const float lse_v = stats[2 * rr + 1];
     if (slot < 0) a.lse[(size_t)b * R + row0 + rr] = lse_v;
     else a.ws_lse[(size_t)slot * a.rows_per_wg + rr] = lse_v;
   }

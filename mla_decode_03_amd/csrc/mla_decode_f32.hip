@@ -71,12 +71,18 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
     }
   }
   const bool empty = lsum == 0.f;  // no visible key; NaN propagates
-  const float inv = poison ? __builtin_nanf("") : (empty ? 0.f : 1.f / lsum);
+  float inv = poison ? __builtin_nanf("") : (empty ? 0.f : 1.f / lsum);
+  float lse_v = poison ? __builtin_nanf("") : (empty ? -INFINITY : m + logf(lsum));
+  if (a.sinks && !poison) {   // attention sink: one more softmax term, zero value row
+    const SinkFold f = fold_sink<false>(m, lsum, a.sinks[r % a.heads]);
+    inv = f.scale_o;
+    lse_v = f.lse;
+  }
   float* orow = a.out + ((size_t)b * a.rows + r) * kDv;
 #pragma unroll
   for (int i = 0; i < 8; ++i) orow[l + 64 * i] = o[i] * inv;
   if (l == 0)
-    a.lse[(size_t)b * a.rows + r] = poison ? __builtin_nanf("") : (empty ? -INFINITY : m + logf(lsum));
+    a.lse[(size_t)b * a.rows + r] = lse_v;
 }
 
 }  // namespace mla

@@ -93,4 +93,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Attention sink folded into one row's softmax statistics: m = the row's shift, l = sum
+// over its keys of exp(s - m) (0: no key), sink = the sink logit, all in the units of
+// the exponential (base 2 or e, per Base2).  The sink is one more softmax term with a
+// zero value row, so the denominator becomes l*exp(m) + exp(sink).  Returns the factor
+// that maps the unnormalised output sum (taken with shift m) to the final output, and
+// the log of the denominator.  Both terms are taken relative to max(m, sink), so
+// neither overflows; sink = -inf gives exactly 1/l and m + log(l), as without a sink.
+struct SinkFold {
+  float scale_o, lse;
+};
+template <bool Base2>
+__device__ inline SinkFold fold_sink(float m, float l, float sink) {
+  if (l == 0.f) return {0.f, sink};                  // no key: out 0, lse = the sink
+  const float mx = fmaxf(m, sink);                   // NaN sink: c below is NaN
+  const float a = Base2 ? __builtin_amdgcn_exp2f(m - mx) : expf(m - mx);
+  const float c = Base2 ? __builtin_amdgcn_exp2f(sink - mx) : expf(sink - mx);
+  const float den = fmaf(l, a, c);
+  return {a / den, mx + (Base2 ? __log2f(den) : logf(den))};
+}
+
 }  // namespace mla

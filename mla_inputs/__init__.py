@@ -163,6 +163,14 @@ def make_config(index: int, seed: int | None = None) -> Case:
     return make_case(seed=1000 + index if seed is None else seed, **cfg)
 
 
+def make_sinks(num_heads: int, seed: int, lo: float = -4.0, hi: float = 12.0) -> np.ndarray:
+    """Per-head attention-sink logits, float32, uniform on [lo, hi).  The default range
+    spans the natural-log sums of exp that N(0, 1) inputs at scale 192^-0.5 give for one
+    to 8192 keys (about 2 to 11), so some sinks barely count and some dominate."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(lo, hi, size=num_heads).astype(np.float32)
+
+
 def poison_unused(case: Case, value=np.nan) -> None:
     """Overwrite every KV slot no query may read (tail slots of each sequence's last
     page and every page not named by a block table) with `value`, in place."""

@@ -126,6 +126,27 @@ def test_plan_sizes_and_workspace_checks():
                             None) == _abi.MLA_ERR_SHAPE, bad
 
 
+def test_variant_checks():
+    """mla_decode_ex: a misaligned sinks pointer is refused before any launch, by every
+    entry that takes the variant."""
+    p = _problem()
+    a = ctypes.c_void_p(0x10000)
+    L = m.lib()
+    bad = ctypes.byref(_abi.Variant(sinks=0x10002))
+    assert L.mla_decode_ex(ctypes.byref(p), bad, a, a, a, a, 1.0, a, a, None, None, 0,
+                           None) == _abi.MLA_ERR_ALIGN
+    mb, wb = m.metadata_bytes(p, None, 256), m.workspace_bytes(p, None, 256)
+    plan = _abi.CPlan(metadata=0x10000, metadata_bytes=mb, grid_wg=256, row_split=1, rows_per_wg=128,
+                      max_partials=260, batch=4, rows=128)
+    assert L.mla_decode_splits(ctypes.byref(p), bad, a, a, a, a, 1.0, a, a, ctypes.byref(plan), a, wb,
+                               None) == _abi.MLA_ERR_ALIGN
+    assert L.mla_combine(ctypes.byref(p), bad, a, a, ctypes.byref(plan), a, wb, None) == _abi.MLA_ERR_ALIGN
+    # the problem is checked first, with or without a variant
+    p129 = _problem(num_heads=129)
+    assert L.mla_decode_ex(ctypes.byref(p129), bad, a, a, a, a, 1.0, a, a, None, None, 0,
+                           None) == _abi.MLA_ERR_SHAPE
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     monkeypatch.setattr(_abi, "_LIB_PATH", str(tmp_path / "libmla.so"))

@@ -255,3 +255,61 @@ def test_tolerance_is_not_vacuous():
 def _case_f32(case):
     case.dtype = "f32"
     return case
+
+
+# ---- attention sinks (mla_decode_ex) -----------------------------------------------------
+
+SINK_CASES = [
+    (2, 1, 128, [1, 70], False),
+    (3, 1, 128, [0, 50, 4097], False),
+    (3, 2, 16, [1, 3, 64], True),
+    (2, 1, 48, [130, 77], False),
+]
+
+
+@pytest.mark.parametrize("mode", ["plan", "forced_splits", "unsplit", "fixed_splits"])
+@pytest.mark.parametrize("B,T,H,lens,causal", SINK_CASES)
+def test_sink_parity(B, T, H, lens, causal, mode):
+    """Sinks enter once per row: in the decode epilogue for unsplit ranges, in the combine
+    for split ones; every plan must meet the oracle with sinks."""
+    import mla_decode_03_amd as mla
+    from mla_inputs import make_sinks
+    case = _case(B, T, H, lens, seed=500 + B * 10 + T + H, causal=causal)
+    sinks = make_sinks(H, seed=H + T)
+    say("sink", B, T, H, lens, causal, mode)
+    ref_o, ref_l = oracle_rows(case, sinks=sinks)
+    kw = {"unsplit": dict(split=False),
+          "forced_splits": dict(options=mla.PlanOptions(num_workgroups=7, min_blocks_per_wg=1)),
+          "fixed_splits": dict(options=mla.PlanOptions(fixed_split_blocks=1)),
+          "plan": {}}[mode]
+    o, l, _ = run(case, sinks=sinks, **kw)
+    compare(o, l, ref_o, ref_l, "sink %s" % mode)
+
+
+def test_sink_fp32_path():
+    from mla_inputs import make_sinks
+    case = _case(2, 2, 16, [0, 200], seed=77, causal=True, dtype="f32")
+    sinks = make_sinks(16, seed=5, lo=-2.0, hi=8.0)
+    ref_o, ref_l = oracle_rows(case, sinks=sinks)
+    o, l, _ = run(case, sinks=sinks)
+    s = compare(o, l, ref_o, ref_l, "sink fp32")
+    assert s["max_abs"] < 1e-4
+
+
+def test_sink_minus_inf_is_bit_identical_to_plain():
+    case = _case(3, 1, 128, [700, 64, 0], seed=78)
+    q, kv, bt, lens = to_device(case)
+    o0, l0, dec = run(case, tensors=(q, kv, bt, lens))
+    o1, l1, _ = run(case, tensors=(q, kv, bt, lens), decoder=dec, sinks=np.full(128, -np.inf, np.float32))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_sink_full_headline_sampled():
+    """The benchmark's workload and default plan, with sinks, on sampled rows."""
+    from mla_inputs import make_sinks
+    case = make_config(1)
+    sinks = make_sinks(case.num_heads, seed=1)
+    o, l, _ = run(case, sinks=sinks)
+    rows = sample_rows(case)
+    ref_o, ref_l = oracle_rows(case, rows=rows, sinks=sinks)
+    compare(o[rows], l[rows], ref_o, ref_l, "config1 sinks, %d rows" % rows.size)
