@@ -117,6 +117,10 @@ typedef struct {
   int32_t min_blocks_per_wg;   /* smallest share of 64-token blocks per workgroup (default 4) */
   int32_t row_split;           /* split each sequence's rows over this many workgroups: 1, 2 or 4 (default 1) */
   int32_t fixed_split_blocks;  /* > 0: batch-invariant plan (below); 0: balanced shares (default) */
+  int32_t split_rule;          /* 0: the cost model picks (default); 1: equal block shares;
+                                  2: cost-balanced shares (see mla_get_metadata) */
+  int32_t segment_cost;        /* cost model's per-segment overhead in quarter blocks
+                                  (0: from the traffic of a segment's rows, see below) */
 } mla_plan_options_t;
 
 /* Variants of the operation.  NULL (or every field NULL) = plain MLA decode. */
@@ -166,9 +170,15 @@ typedef struct {
 /*
  * Plan the split-KV work.  Reads cache_seqlens on the device, writes the plan
  * into plan->metadata: every sequence's 64-token blocks (times row_split) are
- * laid end to end and cut into num_workgroups contiguous, equal (+-1 block)
- * shares, so all CUs stream the same amount of KV; a sequence cut across k > 1
- * workgroups gets k partial results that mla_decode merges by log-sum-exp.
+ * laid end to end and cut into num_workgroups contiguous ranges; a sequence cut across
+ * k > 1 workgroups gets k partial results that mla_decode merges by log-sum-exp.
+ * Two cuts are ranked by a cost model (the TileLang notes' tile recommender ranks
+ * candidate configurations by traffic over bandwidth, "Key design 2: tile
+ * recommendation"): equal block shares, and equal shares of cost where every segment a
+ * workgroup decodes (a sequence's rows, or its slice of them) adds the traffic of its
+ * Q and output rows, segment_cost quarter blocks (default: the segment's rows times
+ * 2180 B, over 73,728 B per block, rounded; 15 for 128 rows).  The plan keeps the cut whose busiest workgroup costs less,
+ * equal block shares on a tie; split_rule forces either.
  * With options->fixed_split_blocks = C > 0 the plan is batch-invariant instead: every
  * sequence (row slice) is cut into chunks of C blocks from its own start, one chunk per
  * workgroup, so where a sequence is split -- and so every bit of its output -- does

@@ -48,7 +48,8 @@ class Problem(ctypes.Structure):
 
 class PlanOptions(ctypes.Structure):
     _fields_ = [("num_workgroups", ctypes.c_int32), ("min_blocks_per_wg", ctypes.c_int32),
-                ("row_split", ctypes.c_int32), ("fixed_split_blocks", ctypes.c_int32)]
+                ("row_split", ctypes.c_int32), ("fixed_split_blocks", ctypes.c_int32),
+                ("split_rule", ctypes.c_int32), ("segment_cost", ctypes.c_int32)]
 
 
 class Variant(ctypes.Structure):

@@ -51,8 +51,17 @@ int32_t resolve_cus(int32_t num_cus, int32_t* out) {
 }
 
 struct PlanShape {
-  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials, fixed_blocks;
+  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials, fixed_blocks, split_rule, seg_cost;
 };
+
+// Cost-model overhead of one segment (a unit's rows decoded by one workgroup) besides
+// its KV blocks, in quarter blocks: the traffic of its Q rows (1152 B each) and its
+// output or partial rows (1024 B + a 4 B LSE each) over a block's 73,728 B, rounded
+// to the nearest quarter.  128 rows give 15 (3.75 blocks).
+int segment_cost_quarters(int rows_per_wg) {
+  const int64_t bytes = (int64_t)rows_per_wg * (1152 + 1024 + 4);
+  return (int)((4 * bytes + mla::kPage * mla::kDqk * 2 / 2) / (mla::kPage * mla::kDqk * 2));
+}
 
 int32_t plan_shape(const mla_problem_t* p, const mla_plan_options_t* o, int32_t num_cus, PlanShape* s) {
   int32_t rc = check_problem(p);
@@ -80,6 +89,10 @@ int32_t plan_shape(const mla_problem_t* p, const mla_plan_options_t* o, int32_t 
   s->rows_per_wg = rows / rsplit;
   s->min_blocks = minb;
   s->fixed_blocks = fixed;
+  s->split_rule = o ? o->split_rule : 0;
+  if (s->split_rule < 0 || s->split_rule > 2) return MLA_ERR_UNSUPPORTED;
+  s->seg_cost = (o && o->segment_cost > 0) ? o->segment_cost : segment_cost_quarters(s->rows_per_wg);
+  if (s->seg_cost > (1 << 20)) return MLA_ERR_SHAPE;
   // each workgroup range holds at most one partial segment at each end (fixed chunks: one)
   s->max_partials = fixed > 0 ? grid : (int)(grid + (units < grid ? units : grid));
   return MLA_OK;
@@ -148,7 +161,8 @@ int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seql
   plan->rows = problem->q_len * problem->num_heads;
   if (mla_launch_plan(cache_seqlens, static_cast<int32_t*>(plan->metadata), problem->batch,
                       plan->rows, s.row_split, s.grid_wg, s.min_blocks, problem->max_blocks_per_seq,
-                      s.max_partials, s.fixed_blocks, static_cast<hipStream_t>(stream)) != hipSuccess)
+                      s.max_partials, s.fixed_blocks, s.split_rule, s.seg_cost,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }

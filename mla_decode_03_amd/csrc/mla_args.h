@@ -52,7 +52,8 @@ struct F32Args {
 
 extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32_t* meta, int batch, int rows,
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
-                                      int max_partials, int fixed_blocks, hipStream_t stream);
+                                      int max_partials, int fixed_blocks, int split_rule, int seg_cost,
+                                      hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_combine(const mla::CombineArgs* args, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_f32(const mla::F32Args* args, hipStream_t stream);

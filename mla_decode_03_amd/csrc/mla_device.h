@@ -42,8 +42,14 @@ enum MetaHdr {
   kHdrError = 9,         // device-side input fault flag
   kHdrMaxPartials = 10,  // partial slot capacity of the workspace
   kHdrMaxBlocks = 11,    // max_blocks_per_seq the plan was made for
+  kHdrRule = 12,         // partition rule used (PlanRule)
+  kHdrCostPages = 13,    // busiest workgroup's cost under the pages rule (auto only)
+  kHdrCostBalanced = 14, // ... under the cost rule (auto only)
+  kHdrSegCost = 15,      // per-segment overhead of the cost model, quarter blocks
   kHdrWords = 16,
 };
+// Partition rules of the planner (the split_rule option; the header's kHdrRule).
+enum PlanRule { kRuleAuto = 0, kRulePages = 1, kRuleCost = 2, kRuleFixed = 3 };
 // arrays follow the header: cu_blocks[B+1], num_splits[U], first_wg[U], part_off[U],
 // wg_begin[grid+1], with U = B * row_split units (unit u = b * row_split + g).
 struct MetaView {

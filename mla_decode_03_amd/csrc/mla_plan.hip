@@ -3,12 +3,21 @@
 // Every sequence b contributes row_split "units" (one per slice of its rows), each
 // holding nblk_b = ceil(L_b / 64) KV blocks.  Units are laid end to end (sequence-
 // major) and the concatenated block range [0, total) is cut into num_wg contiguous
-// shares [floor(w*total/num_wg), floor((w+1)*total/num_wg)), so every workgroup
-// streams the same number of blocks (+-1).  A unit cut across k > 1 workgroups gets
-// k partial results, merged later by log-sum-exp; their slots are numbered unit by
-// unit.  The pages give no scheduler for MLA; the nearest idea on them is the tile
-// recommender's warp partition matched to the machine's topology (TileLang notes,
-// "Key design 2: tile recommendation").  Deterministic, integer only.
+// workgroup ranges.  A unit cut across k > 1 workgroups gets k partial results,
+// merged later by log-sum-exp; their slots are numbered unit by unit.
+//
+// Two ways to cut, ranked by a cost model in the spirit of the TileLang notes' tile
+// recommender ("Key design 2: tile recommendation": time is traffic over bandwidth,
+// and candidate configurations are ranked by it):
+//   pages rule  equal block shares [floor(w*total/num_wg), floor((w+1)*total/num_wg));
+//   cost rule   equal shares of a cost axis on which each non-empty unit first takes
+//               `seg_cost` quarter-blocks (the traffic a segment adds besides its KV
+//               blocks: its Q rows and its output or partial rows) and then 4 quarters
+//               per block.  A cut in a unit's overhead moves to its first block, one
+//               inside its blocks rounds down to a block.
+// A workgroup's cost is 4 per block it streams plus seg_cost per unit it touches; the
+// planner keeps the rule whose busiest workgroup costs less (the pages rule on a tie,
+// so evenly sized batches keep their cut).  Deterministic, integer only.
 #include "mla_args.h"
 #include "mla_device.h"
 
@@ -36,6 +45,20 @@ __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s, int32_t* t
   return base + x - v;
 }
 
+// Block-wide maximum of one int64 per thread (256 threads); every thread gets it.
+__device__ inline int64_t block_max(int64_t x, int64_t* s) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int64_t y = __shfl_xor(x, off, 64);
+    x = x > y ? x : y;
+  }
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const int64_t r = max(max(s[0], s[1]), max(s[2], s[3]));
+  __syncthreads();  // s is reused by the next call
+  return r;
+}
+
 // floor(n / d) for 0 <= n < 2^53, 0 < d < 2^31: a double quotient, corrected to the
 // exact integer (the rounded quotient is off by at most one).
 __device__ inline int64_t floor_div(int64_t n, int64_t d) {
@@ -55,16 +78,21 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ meta, int batch,
                                                        int rows, int row_split, int grid_wg,
                                                        int min_blocks, int max_blocks,
-                                                       int max_partials, int fixed_blocks) {
+                                                       int max_partials, int fixed_blocks,
+                                                       int split_rule, int seg_cost) {
   __shared__ int32_t s_scan[256];
   __shared__ int32_t s_cu[kPlanLdsBatch + 1];   // cu_blocks, when the batch fits
+  __shared__ int32_t s_ne[kPlanLdsBatch + 1];   // non-empty sequences before b, likewise
+  __shared__ int64_t s_red[4];
   const int t = threadIdx.x;
   const bool cu_in_lds = batch <= kPlanLdsBatch;
   MetaView v = meta_view(meta, batch, row_split);
+  // Larger batches keep the non-empty prefix in first_wg (rewritten by the unit pass).
+  int32_t* ne_glob = v.first_wg;
   int err = 0;
 
-  // 1. blocks per sequence and their prefix sums
-  int32_t carry = 0;
+  // 1. blocks per sequence and their prefix sums; non-empty sequences before each
+  int32_t carry = 0, ne_carry = 0;
   for (int base = 0; base < batch; base += 256) {
     const int b = base + t;
     int32_t nb = 0;
@@ -75,24 +103,36 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       if (n > max_blocks) { n = max_blocks; err = 1; }
       nb = (int32_t)n;
     }
-    int32_t tot;
+    int32_t tot, ntot;
     const int32_t excl = block_exclusive_scan(nb, s_scan, &tot);
+    const int32_t nexcl = block_exclusive_scan(nb > 0 ? 1 : 0, s_scan, &ntot);
     if (b < batch) {
       v.cu_blocks[b] = carry + excl;
-      if (cu_in_lds) s_cu[b] = carry + excl;
+      if (cu_in_lds) {
+        s_cu[b] = carry + excl;
+        s_ne[b] = ne_carry + nexcl;
+      } else {
+        ne_glob[b] = ne_carry + nexcl;
+      }
     }
     carry += tot;
+    ne_carry += ntot;
   }
   if (t == 0) {
     v.cu_blocks[batch] = carry;
-    if (cu_in_lds) s_cu[batch] = carry;
+    if (cu_in_lds) {
+      s_cu[batch] = carry;
+      s_ne[batch] = ne_carry;
+    }
   }
-  __syncthreads();  // cu_blocks visible to the whole workgroup
+  __threadfence_block();
+  __syncthreads();  // cu_blocks and the non-empty prefix visible to the whole workgroup
 
   const int64_t total = (int64_t)row_split * carry;
   const int units = batch * row_split;
   int64_t num_wg = 0;
   int32_t pcarry = 0;
+  bool use_cost = false;
   if (fixed_blocks > 0) {
     // Batch-invariant plan: every unit cut into chunks of fixed_blocks blocks from its own
     // start, one chunk per workgroup, in unit order.
@@ -131,28 +171,107 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       if (num_wg > grid_wg) num_wg = grid_wg;
       if (num_wg < 1) num_wg = 1;
     }
+    const int rs = row_split;
+    const int64_t c = seg_cost;
+    const int64_t ctot = 4 * total + c * rs * (int64_t)ne_carry;   // length of the cost axis
+    auto cu_at = [&](int b) -> int64_t { return cu_in_lds ? s_cu[b] : v.cu_blocks[b]; };
+    auto ne_at = [&](int b) -> int64_t { return cu_in_lds ? s_ne[b] : (b < batch ? ne_glob[b] : ne_carry); };
+    auto cost_at = [&](int b) -> int64_t { return 4 * rs * cu_at(b) + c * rs * ne_at(b); };
+    // sequence holding block position p < total: the largest b with rs * cu[b] <= p
+    auto seq_of_block = [&](int64_t p) -> int {
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rs * cu_at(mid) <= p) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    };
+    // sequence holding cost position x < ctot: the largest b with cost_at(b) <= x
+    auto seq_of_cost = [&](int64_t x) -> int {
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cost_at(mid) <= x) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    };
+    // cost rule: block position of the cut at cost position x
+    auto block_at = [&](int64_t x) -> int64_t {
+      if (x >= ctot) return total;
+      const int b = seq_of_cost(x);
+      const int64_t nb = cu_at(b + 1) - cu_at(b);
+      const int64_t ucost = c + 4 * nb;
+      const int64_t g = (x - cost_at(b)) / ucost;
+      const int64_t off = x - cost_at(b) - g * ucost;
+      return rs * cu_at(b) + g * nb + (off < c ? 0 : (off - c) / 4);
+    };
+    // rank of the unit holding block p among the non-empty units
+    auto rank_of_block = [&](int64_t p) -> int64_t {
+      const int b = seq_of_block(p);
+      const int64_t nb = cu_at(b + 1) - cu_at(b);
+      return rs * ne_at(b) + (p - rs * cu_at(b)) / nb;
+    };
+    auto pages_begin = [&](int64_t w) -> int64_t { return floor_div(w * total, num_wg); };
+    auto cost_begin = [&](int64_t w) -> int64_t { return block_at(floor_div(w * ctot, num_wg)); };
+    auto range_cost = [&](int64_t lo, int64_t hi) -> int64_t {
+      return hi > lo ? 4 * (hi - lo) + c * (rank_of_block(hi - 1) - rank_of_block(lo) + 1) : 0;
+    };
 
-    // 2. workgroup shares
+    // 2. the busiest workgroup under each rule; keep the cheaper rule
+    int64_t worst_p = 0, worst_c = 0;
+    if (split_rule == kRuleAuto && num_wg > 0) {
+      for (int64_t w = t; w < num_wg; w += 256) {
+        worst_p = max(worst_p, range_cost(pages_begin(w), pages_begin(w + 1)));
+        worst_c = max(worst_c, range_cost(cost_begin(w), cost_begin(w + 1)));
+      }
+      worst_p = block_max(worst_p, s_red);
+      worst_c = block_max(worst_c, s_red);
+    }
+    use_cost = split_rule == kRuleCost || (split_rule == kRuleAuto && worst_c < worst_p);
+    if (t == 0) {
+      v.hdr[kHdrCostPages] = (int32_t)min<int64_t>(worst_p, INT32_MAX);
+      v.hdr[kHdrCostBalanced] = (int32_t)min<int64_t>(worst_c, INT32_MAX);
+    }
+
+    // 3. workgroup ranges
     for (int w = t; w <= grid_wg; w += 256)
-      v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)floor_div((int64_t)w * total, num_wg) : (int32_t)total;
-
-    // 3. units: which workgroups cover each, and the partial slots of the split ones
+      v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)(use_cost ? cost_begin(w) : pages_begin(w))
+                                                  : (int32_t)total;
+    // workgroup holding block p: the largest w < num_wg whose range starts at or before p.
+    // Cost rule: a cut at cost x lands at or before p exactly when x < Y, Y = the cost
+    // position just past block p, so the answer is the largest w with w*ctot < Y*num_wg.
+    auto holder = [&](int64_t p) -> int32_t {
+      if (!use_cost) return wg_of(p, total, num_wg);
+      const int b = seq_of_block(p);
+      const int64_t nb = cu_at(b + 1) - cu_at(b);
+      const int64_t g = (p - rs * cu_at(b)) / nb;
+      const int64_t y = cost_at(b) + g * (c + 4 * nb) + c + 4 * (p - rs * cu_at(b) - g * nb) + 4;
+      return (int32_t)min<int64_t>(floor_div(y * num_wg - 1, ctot), num_wg - 1);
+    };
+    // 4. units: which workgroups cover each, and the partial slots of the split ones.
+    // First every unit's first workgroup and split count (first_wg still holds the
+    // non-empty prefix of large batches, so the first workgroup waits in part_off) ...
+    for (int u = t; u < units; u += 256) {
+      int32_t ns = 0, first = -1;
+      const int b = u / rs, g = u % rs;
+      const int64_t nb = cu_at(b + 1) - cu_at(b);
+      if (nb > 0) {
+        const int64_t start = rs * cu_at(b) + g * nb;
+        first = holder(start);
+        ns = holder(start + nb - 1) - first + 1;
+      }
+      v.num_splits[u] = ns;
+      v.part_off[u] = first;
+    }
+    __threadfence_block();
+    __syncthreads();
+    // ... then, each unit by the thread that wrote it, the slots.
     for (int base = 0; base < units; base += 256) {
       const int u = base + t;
-      int32_t ns = 0, first = -1;
+      int32_t ns = 0;
       if (u < units) {
-        const int b = u / row_split, g = u % row_split;
-        const int32_t cb0 = cu_in_lds ? s_cu[b] : v.cu_blocks[b];
-        const int32_t cb1 = cu_in_lds ? s_cu[b + 1] : v.cu_blocks[b + 1];
-        const int32_t nb = cb1 - cb0;
-        if (nb > 0) {
-          const int64_t start = (int64_t)row_split * cb0 + (int64_t)g * nb;
-          first = wg_of(start, total, num_wg);
-          const int32_t last = wg_of(start + nb - 1, total, num_wg);
-          ns = last - first + 1;
-        }
-        v.num_splits[u] = ns;
-        v.first_wg[u] = first;
+        ns = v.num_splits[u];
+        v.first_wg[u] = v.part_off[u];
       }
       int32_t tot;
       const int32_t excl = block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &tot);
@@ -180,6 +299,12 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
     v.hdr[kHdrError] = (s_err || pcarry > max_partials) ? 1 : 0;
     v.hdr[kHdrMaxPartials] = max_partials;
     v.hdr[kHdrMaxBlocks] = max_blocks;
+    v.hdr[kHdrRule] = fixed_blocks > 0 ? kRuleFixed : (use_cost ? kRuleCost : kRulePages);
+    v.hdr[kHdrSegCost] = fixed_blocks > 0 ? 0 : seg_cost;
+    if (fixed_blocks > 0) {
+      v.hdr[kHdrCostPages] = 0;
+      v.hdr[kHdrCostBalanced] = 0;
+    }
     if (pcarry > max_partials || num_wg > grid_wg) v.hdr[kHdrNumWg] = 0;  // refuse to run a plan that overflows
   }
 }
@@ -188,8 +313,10 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
 
 extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32_t* meta, int batch, int rows,
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
-                                      int max_partials, int fixed_blocks, hipStream_t stream) {
+                                      int max_partials, int fixed_blocks, int split_rule, int seg_cost,
+                                      hipStream_t stream) {
   hipLaunchKernelGGL(mla::mla_plan_kernel, dim3(1), dim3(256), 0, stream, seqlens, meta, batch,
-                     rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks);
+                     rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks,
+                     split_rule, seg_cost);
   return hipGetLastError();
 }

@@ -100,6 +100,11 @@ def test_plan_sizes_and_workspace_checks():
     assert m.metadata_bytes(p, fo, 256) == 4 * (16 + 5 + 3 * 8 + grid + 1)
     assert m.workspace_bytes(p, fo, 256) == grid * 64 * (512 * 2 + 4)
     assert m.workspace_bytes(p, fo, 80) == m.workspace_bytes(p, fo, 256)   # no CU dependence
+    # partition rule: 0 (cost model), 1 (pages) or 2 (cost); anything else is refused
+    for rule in (0, 1, 2):
+        assert m.metadata_bytes(p, m.PlanOptions(split_rule=rule), 256) == mb
+    assert m.metadata_bytes(p, m.PlanOptions(split_rule=3), 256) == 0
+    assert m.metadata_bytes(p, m.PlanOptions(split_rule=-1), 256) == 0
     L = m.lib()
     a = ctypes.c_void_p(0x10000)
     # metadata buffer too small: refused before any launch

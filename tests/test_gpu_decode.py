@@ -47,7 +47,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["plan", "forced_splits", "unsplit", "fixed_splits"])
+@pytest.mark.parametrize("mode", ["plan", "forced_splits", "unsplit", "fixed_splits", "cost_rule"])
 @pytest.mark.parametrize("B,T,H,lens,causal", SMALL)
 def test_small_parity(B, T, H, lens, causal, mode):
     import mla_decode_03_amd as mla
@@ -61,6 +61,8 @@ def test_small_parity(B, T, H, lens, causal, mode):
         kw = dict(split=False)
     elif mode == "fixed_splits":
         kw = dict(options=mla.PlanOptions(fixed_split_blocks=2))
+    elif mode == "cost_rule":
+        kw = dict(options=mla.PlanOptions(num_workgroups=5, min_blocks_per_wg=1, split_rule=2))
     o, l, _ = run(case, **kw)
     compare(o, l, ref_o, ref_l, "small %s" % mode)
 
@@ -156,7 +158,37 @@ def test_device_plan_matches_mirror():
                         min_blocks=opts.min_blocks_per_wg)
         hdr, arrays = to_words(ref, opts.num_workgroups, 128, plan.max_partials,
                                case.block_table.shape[1])
-        assert list(words[:12]) == hdr
+        assert list(words[:16]) == hdr
+        assert list(words[16:16 + len(arrays)]) == arrays
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+def test_device_plan_rules_match_mirror(rule):
+    """Both partition rules and the cost model's choice, bit for bit against the mirror:
+    a ragged batch kept in LDS and a 5000-sequence batch (row_split 2) that is not."""
+    import torch
+    import mla_decode_03_amd as mla
+    from plan_mirror import RULES, make_plan, to_words
+    name = {v: k for k, v in RULES.items()}[rule]
+    rng = np.random.default_rng(9 + rule)
+    for B, rs, grid, hi, segq in ((61, 1, 256, 9000, 0), (5000, 2, 256, 300, 0), (40, 4, 100, 3000, 23)):
+        lens = [int(x) for x in rng.integers(0, hi, size=B)]
+        lens[3] = 0
+        maxb = (max(lens) + 63) // 64 + 1
+        prob = mla.Problem(batch=B, q_len=1, num_heads=128, causal=0, num_pages=1, block_table_stride=maxb,
+                           max_blocks_per_seq=maxb, dtype=mla.DTYPE_BF16)
+        opts = mla.PlanOptions(num_workgroups=grid, min_blocks_per_wg=1, row_split=rs, split_rule=rule,
+                               segment_cost=segq)
+        meta = torch.empty(mla.metadata_bytes(prob, opts, 256), dtype=torch.uint8, device="cuda")
+        lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        plan = mla.get_metadata(prob, lt, meta, opts, 256)
+        torch.cuda.synchronize()
+        words = meta.view(torch.int32).cpu().numpy()
+        ref = make_plan(lens, row_split=rs, grid_wg=grid, min_blocks=1, rule=name, seg_q=segq or None)
+        hdr, arrays = to_words(ref, grid, 128, plan.max_partials, maxb)
+        say("plan rule %s B=%d rs=%d: kept rule %d, worst pages %d cost %d" % (name, B, rs, ref["rule"],
+                                                                             ref["cost_pages"], ref["cost_balanced"]))
+        assert list(words[:16]) == hdr
         assert list(words[16:16 + len(arrays)]) == arrays
 
 
@@ -181,7 +213,7 @@ def test_device_fixed_plan_matches_mirror():
         ref = make_plan(lens, row_split=rs, grid_wg=grid, fixed_blocks=C)
         hdr, arrays = to_words(ref, grid, 128, plan.max_partials, maxb)
         say("fixed plan C=%d rs=%d: %d chunks of %d slots" % (C, rs, ref["num_wg"], grid))
-        assert list(words[:12]) == hdr
+        assert list(words[:16]) == hdr
         assert list(words[16:16 + len(arrays)]) == arrays
 
 

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from plan_mirror import make_plan, segments
+from plan_mirror import make_plan, plan_cost, segment_cost, segments
 
 
 def _check(plan, seqlens, rs, max_partials):
@@ -29,11 +29,20 @@ def _check(plan, seqlens, rs, max_partials):
                 assert slots == [-1]
             else:
                 assert slots == list(range(plan["part_off"][u], plan["part_off"][u] + len(parts)))
-    # shares are balanced to within one block
     shares = [plan["wg_begin"][w + 1] - plan["wg_begin"][w] for w in range(plan["num_wg"])]
     if shares:
-        assert max(shares) - min(shares) <= 1
-        assert sum(shares) == plan["total"]
+        assert min(shares) >= 0 and sum(shares) == plan["total"]
+        if plan["rule"] == 1:
+            # pages rule: shares balanced to within one block
+            assert max(shares) - min(shares) <= 1
+        elif plan["rule"] == 2:
+            # cost rule: no workgroup exceeds its share of the cost axis by more than one
+            # segment overhead plus one block (a cut rounds down by less than that)
+            c = plan["seg_cost"]
+            ne_units = sum(1 for L in seqlens if L > 0) * rs
+            ctot = 4 * plan["total"] + c * ne_units
+            n = plan["num_wg"]
+            assert plan_cost(plan, c) <= -(-ctot // n) + c + 3
     # partial slots are unique and fit the workspace bound
     used = [s for (*_, s) in segs if s >= 0]
     assert len(used) == len(set(used)) == plan["num_partials"] <= max_partials
@@ -51,6 +60,50 @@ def test_random_plans(seed):
     _check(plan, seqlens, rs, grid + min(grid, B * rs))
 
 
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("rule", ["pages", "cost"])
+def test_random_plans_each_rule(seed, rule):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 60))
+    seqlens = [int(x) for x in rng.integers(0, 5000, size=B)]
+    seqlens[int(rng.integers(0, B))] = 0
+    rs = [1, 2, 4][seed % 3]
+    grid = int(rng.integers(1, 300))
+    plan = make_plan(seqlens, row_split=rs, grid_wg=grid, min_blocks=int(rng.integers(1, 9)), rule=rule,
+                     seg_q=int(rng.integers(0, 30)) or None)
+    assert plan["rule"] == (1 if rule == "pages" else 2)
+    _check(plan, seqlens, rs, grid + min(grid, B * rs))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_auto_keeps_the_cheaper_rule(seed):
+    rng = np.random.default_rng(200 + seed)
+    B = int(rng.integers(2, 200))
+    seqlens = [int(x) for x in rng.integers(1, 8193, size=B)]
+    c = segment_cost(128)
+    auto = make_plan(seqlens, grid_wg=256)
+    pages = make_plan(seqlens, grid_wg=256, rule="pages")
+    cost = make_plan(seqlens, grid_wg=256, rule="cost")
+    wp, wc = plan_cost(pages, c), plan_cost(cost, c)
+    assert (auto["cost_pages"], auto["cost_balanced"]) == (wp, wc)
+    assert plan_cost(auto, c) == min(wp, wc)
+    assert auto["wg_begin"] == (cost if wc < wp else pages)["wg_begin"]
+
+
+def test_segment_cost_is_the_traffic_of_a_segments_rows():
+    # 128 rows move 128 * (1152 + 1024 + 4) B besides their KV: 3.78 blocks -> 15 quarters
+    assert segment_cost(128) == 15 and segment_cost(64) == 8 and segment_cost(32) == 4
+    assert segment_cost(16) == 2
+
+
+def test_even_batches_keep_the_pages_cut_and_ragged_ones_take_the_cost_cut():
+    even = make_plan([4096] * 64, grid_wg=256)
+    assert even["rule"] == 1 and even["cost_pages"] < even["cost_balanced"]
+    rng = np.random.default_rng(7)
+    ragged = make_plan([int(x) for x in rng.integers(1, 2049, size=256)], grid_wg=256)
+    assert ragged["rule"] == 2 and ragged["cost_balanced"] < ragged["cost_pages"]
+
+
 def test_headline_shape_splits_each_sequence_in_four():
     plan = make_plan([4096] * 64, grid_wg=256, min_blocks=4)
     assert plan["num_wg"] == 256 and set(plan["num_splits"]) == {4}
@@ -59,10 +112,15 @@ def test_headline_shape_splits_each_sequence_in_four():
 
 
 def test_small_problem_is_not_over_split_and_empty_batch():
-    # 2 + 4 blocks with at least 4 per workgroup: two workgroups; the contiguous cut at
-    # block 3 splits the second sequence in two
-    plan = make_plan([100, 200], grid_wg=256, min_blocks=4)
+    # 2 + 4 blocks with at least 4 per workgroup: two workgroups.  The pages rule cuts
+    # at block 3 and splits the second sequence in two (busiest workgroup: 3 blocks and
+    # 2 segments, 12 + 2*15 = 42 quarters); the cost rule gives each sequence its own
+    # workgroup (busiest: 4 blocks and 1 segment, 31), so the cost model keeps that.
+    plan = make_plan([100, 200], grid_wg=256, min_blocks=4, rule="pages")
     assert plan["num_wg"] == 2 and plan["num_splits"] == [1, 2] and plan["num_partials"] == 2
+    plan = make_plan([100, 200], grid_wg=256, min_blocks=4)
+    assert (plan["cost_pages"], plan["cost_balanced"]) == (42, 31)
+    assert plan["rule"] == 2 and plan["num_splits"] == [1, 1] and plan["num_partials"] == 0
     plan = make_plan([100, 200], grid_wg=256, min_blocks=8)
     assert plan["num_wg"] == 1 and plan["num_splits"] == [1, 1] and plan["num_partials"] == 0
     plan = make_plan([0, 0], grid_wg=8)
