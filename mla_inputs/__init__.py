@@ -171,6 +171,30 @@ def make_sinks(num_heads: int, seed: int, lo: float = -4.0, hi: float = 12.0) ->
     return rng.uniform(lo, hi, size=num_heads).astype(np.float32)
 
 
+def make_topk_indices(cache_seqlens, q_len: int, topk: int, seed: int, pad_frac: float = 0.0,
+                      dup_frac: float = 0.0) -> np.ndarray:
+    """Sparse token lists [B, q_len, topk] int32 standing in for a top-k indexer's output
+    (which needs trained weights): for each (b, t), min(topk, L_b) distinct positions
+    of [0, L_b) in random order, the rest -1.  pad_frac of the entries are then turned
+    into -1 and dup_frac into copies of another entry of the same list."""
+    rng = np.random.default_rng(seed)
+    B = len(cache_seqlens)
+    out = np.full((B, q_len, topk), -1, dtype=np.int32)
+    for b in range(B):
+        L = int(cache_seqlens[b])
+        for t in range(q_len):
+            k = min(topk, max(L, 0))
+            if k:
+                out[b, t, :k] = rng.choice(L, size=k, replace=False)
+            if pad_frac:
+                out[b, t, rng.random(topk) < pad_frac] = -1
+            if dup_frac and k:
+                src = out[b, t, rng.integers(0, k, size=topk)]
+                sel = rng.random(topk) < dup_frac
+                out[b, t, sel] = src[sel]
+    return out
+
+
 def poison_unused(case: Case, value=np.nan) -> None:
     """Overwrite every KV slot no query may read (tail slots of each sequence's last
     page and every page not named by a block table) with `value`, in place."""

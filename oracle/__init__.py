@@ -57,6 +57,7 @@ def _load():
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
         lib.mla_oracle_max_threads.restype = ctypes.c_int32
@@ -70,7 +71,7 @@ def max_threads() -> int:
 
 def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32",
            causal: bool = False, rows=None, d_v: int = 512, page: int | None = None,
-           threads: int = 0, sinks=None):
+           threads: int = 0, sinks=None, indices=None):
     """float64 MLA decode.
 
     q:  [B, T, H, d_qk] float32 values, or uint16 bf16 bits when dtype == "bf16"
@@ -79,6 +80,8 @@ def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32
     rows: optional flat row ids (b*T + t)*H + h to compute; default all rows.
     sinks: optional per-head sink logits [H] (an extra softmax term with a zero value
            row; see mla_oracle.c), taken as float64.
+    indices: optional sparse token lists [B, T, topk] int32 (-1 = unused entry); each
+           row then attends to exactly its (b, t) list.  Needs causal False.
     Returns (out [n_rows, d_v] float64, lse [n_rows] float64), rows in the order asked.
     """
     q = np.ascontiguousarray(q)
@@ -103,6 +106,11 @@ def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32
     if sinks is not None:
         sk = np.ascontiguousarray(sinks, dtype=np.float64)
         assert sk.shape == (H,), sk.shape
+    idx, topk = None, 0
+    if indices is not None:
+        idx = np.ascontiguousarray(indices, dtype=np.int32)
+        assert idx.ndim == 3 and idx.shape[:2] == (B, T), idx.shape
+        topk = idx.shape[2]
     out = np.empty((n_rows, d_v), dtype=np.float64)
     lse = np.empty((n_rows,), dtype=np.float64)
     rc = _load().mla_oracle_decode(
@@ -110,6 +118,7 @@ def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32
         bt.ctypes.data, bt.shape[1], lens.ctypes.data,
         B, T, H, npages, pg, d_qk, d_v, int(bool(causal)), float(scale),
         sk.ctypes.data if sk is not None else None,
+        idx.ctypes.data if idx is not None else None, topk,
         rows_arr.ctypes.data if rows_arr is not None else None, n_rows,
         out.ctypes.data, lse.ctypes.data, int(threads))
     if rc != 0:
@@ -117,8 +126,8 @@ def decode(q, kv, block_table, cache_seqlens, *, scale: float, dtype: str = "f32
     return out, lse
 
 
-def decode_case(case, rows=None, threads: int = 0, sinks=None):
+def decode_case(case, rows=None, threads: int = 0, sinks=None, indices=None):
     """decode() on a `mla_inputs.Case`."""
     return decode(case.q_array(), case.kv_array(), case.block_table, case.cache_seqlens,
                   scale=case.scale, dtype=case.dtype, causal=case.causal, rows=rows,
-                  threads=threads, sinks=sinks)
+                  threads=threads, sinks=sinks, indices=indices)

@@ -41,6 +41,13 @@
  * sum_q exp(s_q)), out is their sum over the real value rows, and lse is the natural
  * log of that whole denominator.  A row with no visible key then gets out = 0 and
  * lse = sigma_h; sigma_h = -inf is the plain decode.
+ *
+ * Sparse (top-k) decode (optional).  The DeepSeek-V4 TileLang note mentions the
+ * dynamic sparse attention of DeepSeek models (TileLang's limits on it) without the
+ * details.  Reading taken: each (b, t) has a list of topk logical token positions of
+ * sequence b, shared by all heads, with -1 marking an unused entry; the row attends to
+ * exactly the listed tokens, once per entry, in place of its causal range.  An entry
+ * below -1 or at or past cache_seqlens[b] is an input fault (ORACLE_ERR_PAGE).
  */
 #include <math.h>
 #include <stdint.h>
@@ -74,6 +81,7 @@ static int64_t visible(int64_t seqlen, int32_t q_len, int32_t t, int32_t causal)
 /*
  * Decode the requested rows.
  *   sinks        per-head sink logits [heads] (double), or NULL for none
+ *   indices      sparse token lists [batch, q_len, topk] int32, or NULL (dense); needs causal 0
  *   q            [batch, q_len, heads, d_qk]           (dtype)
  *   kv           [num_pages, page, d_qk]               (dtype)
  *   block_table  int32, row b at block_table + b*bt_stride
@@ -88,11 +96,13 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
                       int32_t batch, int32_t q_len, int32_t heads,
                       int64_t num_pages, int32_t page, int32_t d_qk, int32_t d_v,
                       int32_t causal, double scale, const double* sinks,
+                      const int32_t* indices, int32_t topk,
                       const int64_t* rows, int64_t n_rows,
                       double* out, double* lse, int32_t n_threads) {
   if (!q || !kv || !block_table || !cache_seqlens || !out || !lse) return ORACLE_ERR_ARG;
   if (dtype != 0 && dtype != 1) return ORACLE_ERR_ARG;
   if (batch < 0 || q_len < 1 || heads < 1 || page < 1 || d_v < 1 || d_v > d_qk) return ORACLE_ERR_ARG;
+  if (indices && (topk < 1 || causal)) return ORACLE_ERR_ARG;
   const int64_t total_rows = (int64_t)batch * q_len * heads;
   if (rows == NULL) n_rows = total_rows;
   int err = ORACLE_OK;
@@ -109,6 +119,7 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
     int64_t max_tokens = 0;
     for (int32_t b = 0; b < batch; ++b)
       if (cache_seqlens[b] > max_tokens) max_tokens = cache_seqlens[b];
+    if (indices && topk > max_tokens) max_tokens = topk;
     double* s = (double*)malloc(sizeof(double) * (size_t)(max_tokens > 0 ? max_tokens : 1));
     int64_t* kbase = (int64_t*)malloc(sizeof(int64_t) * (size_t)(max_tokens > 0 ? max_tokens : 1));
     double* acc = (double*)malloc(sizeof(double) * (size_t)d_v);
@@ -133,12 +144,25 @@ int mla_oracle_decode(const void* q, const void* kv, int32_t dtype,
       const int32_t h = (int32_t)(r % heads);
       const double sink = sinks ? sinks[h] : -INFINITY;
       const int has_sink = sink > -INFINITY || isnan(sink);
-      const int64_t n = visible(cache_seqlens[b], q_len, t, causal);
+      int64_t n = visible(cache_seqlens[b], q_len, t, causal);
       double* o = out + i * d_v;
 
-      /* gather: element offset of each visible key row inside kv */
+      /* gather: element offset of each visible key row inside kv (dense: positions
+         0 .. n-1; sparse: the listed positions, in list order) */
       int bad = 0;
-      for (int64_t p = 0; p < n; ++p) {
+      const int32_t* list = indices ? indices + ((int64_t)b * q_len + t) * topk : NULL;
+      if (list) {
+        n = 0;
+        for (int32_t k = 0; k < topk && !bad; ++k) {
+          const int64_t p = list[k];
+          if (p == -1) continue;
+          if (p < 0 || p >= cache_seqlens[b]) { bad = 1; break; }
+          const int64_t pg = block_table[b * bt_stride + p / page];
+          if (pg < 0 || pg >= num_pages) { bad = 1; break; }
+          kbase[n++] = (pg * page + p % page) * (int64_t)d_qk;
+        }
+      }
+      for (int64_t p = 0; p < n && !list; ++p) {
         const int64_t pg = block_table[b * bt_stride + p / page];
         if (pg < 0 || pg >= num_pages) { bad = 1; break; }
         kbase[p] = (pg * page + p % page) * (int64_t)d_qk;

@@ -299,3 +299,74 @@ def test_sink_minus_inf_is_the_plain_decode_and_empty_rows_take_the_sink():
     # b=0, t=0 sees no key: out 0, lse = its head's sink
     assert np.all(o2[0] == 0.0) and l2[0] == 1.5
     assert np.all(o2[1] == 0.0) and l2[1] == -3.0
+
+
+# ---- sparse (top-k) decode: each (b, t) attends to exactly its listed tokens ------------
+
+def _sparse_case(B, T, H, lens, seed):
+    return _f32_case(B, T, H, lens, seed=seed)
+
+
+def test_sparse_full_list_is_the_dense_decode():
+    """Listing every position 0 .. L-1 in order (unused entries -1) gathers the same keys
+    in the same order as the dense decode: bit-identical."""
+    case = _sparse_case(3, 2, 2, [70, 5, 128], seed=90)
+    topk = 130
+    idx = np.full((3, 2, topk), -1, np.int32)
+    for b, L in enumerate(case.cache_seqlens):
+        idx[b, :, :L] = np.arange(L)
+    o0, l0 = oracle.decode_case(case)
+    o1, l1 = oracle.decode_case(case, indices=idx)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_sparse_brute_force_tiny():
+    """Random lists with unused entries and repeats, against the brute force over the
+    listed keys gathered by plain indexing."""
+    from mla_inputs import make_topk_indices
+    case = _sparse_case(2, 2, 2, [150, 40], seed=91)
+    idx = make_topk_indices(case.cache_seqlens, 2, 70, seed=5, pad_frac=0.2, dup_frac=0.1)
+    out, lse = oracle.decode_case(case, indices=idx)
+    for b in range(2):
+        keys = _logical_keys(case, b)
+        for t in range(2):
+            sel = [list(keys[p]) for p in idx[b, t] if p != -1]
+            for h in range(2):
+                r = (b * 2 + t) * 2 + h
+                ref, ref_lse = brute.attend_row(list(case.q[b, t, h].astype(np.float64)), sel, case.scale, D_V)
+                np.testing.assert_allclose(out[r], ref, rtol=0, atol=1e-12)
+                assert abs(lse[r] - ref_lse) < 1e-12
+
+
+def test_sparse_unused_entries_order_and_repeats():
+    case = _sparse_case(1, 1, 3, [200], seed=92)
+    rng = np.random.default_rng(3)
+    base = rng.choice(200, size=50, replace=False).astype(np.int32)
+    o0, l0 = oracle.decode_case(case, indices=base.reshape(1, 1, -1))
+    # -1 entries anywhere change nothing, bit for bit
+    padded = np.insert(base, [0, 10, 10, 50], -1).reshape(1, 1, -1)
+    o1, l1 = oracle.decode_case(case, indices=padded)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # the list is a set of keys up to rounding order
+    o2, l2 = oracle.decode_case(case, indices=rng.permutation(base).reshape(1, 1, -1))
+    np.testing.assert_allclose(o2, o0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l0, rtol=0, atol=1e-13)
+    # listing every entry twice doubles every weight: same output, lse + ln 2
+    o3, l3 = oracle.decode_case(case, indices=np.concatenate([base, base]).reshape(1, 1, -1))
+    np.testing.assert_allclose(o3, o0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l3, l0 + math.log(2.0), rtol=0, atol=1e-13)
+    # an all-unused list is an empty row
+    o4, l4 = oracle.decode_case(case, indices=np.full((1, 1, 8), -1, np.int32))
+    assert np.all(o4 == 0.0) and np.all(l4 == -np.inf)
+
+
+def test_sparse_bad_entries_are_reported():
+    case = _sparse_case(2, 1, 1, [10, 64], seed=93)
+    for bad in (10, 64 + 5, -2):
+        idx = np.array([[[0, 1, 2]], [[3, 4, 5]]], np.int32)
+        idx[0, 0, 1] = bad                     # sequence 0 holds 10 tokens
+        with pytest.raises(RuntimeError, match="code 2"):
+            oracle.decode_case(case, indices=idx)
+    with pytest.raises(RuntimeError, match="code 1"):   # sparse lists replace the causal rule
+        c2 = _f32_case(1, 2, 1, [10], seed=94, causal=True)
+        oracle.decode_case(c2, indices=np.zeros((1, 2, 2), np.int32))
