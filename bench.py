@@ -34,18 +34,23 @@ DECODE_KERNEL = "mla_decode_bf16_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_h128_l4096_traffic.json")
 
 
-def workload_sizes(case):
-    """Algorithmic FLOPs and bytes of one decode of `case` (each visible key once)."""
+def workload_sizes(case, indices=None):
+    """Algorithmic FLOPs and bytes of one decode of `case` (each visible key once; with
+    sparse `indices`, each listed entry once, plus the lists themselves)."""
     import numpy as np
     T, H = case.q_len, case.num_heads
+    elem = 2 if case.dtype == "bf16" else 4
+    rows = case.batch * T * H
+    if indices is not None:
+        keys = int(np.sum(indices != -1))
+        other = rows * 576 * elem + rows * 512 * elem + rows * 4 + indices.size * 4 + case.batch * 4
+        return keys * H * 2 * (576 + 512), keys * 576 * elem, keys * 576 * elem + other
     flops = 0
     for L in case.cache_seqlens.tolist():
         for t in range(T):
             n = (L - T + 1 + t) if (case.causal and T > 1) else L
             flops += max(n, 0) * H * 2 * (576 + 512)
-    elem = 2 if case.dtype == "bf16" else 4
     kv_bytes = int(np.sum(np.maximum(case.cache_seqlens, 0))) * 576 * elem
-    rows = case.batch * T * H
     other = rows * 576 * elem + rows * 512 * elem + rows * 4 + case.block_table.size * 4 + case.batch * 4
     return flops, kv_bytes, kv_bytes + other
 
@@ -64,10 +69,10 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, flops):
+def cpu_baseline(case, flops, indices=None):
     import oracle
     t0 = time.perf_counter()
-    oracle.decode_case(case)
+    oracle.decode_case(case, indices=indices)
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
@@ -90,6 +95,8 @@ def main():
                     help="batch-invariant plan: fixed chunks of this many 64-token blocks")
     ap.add_argument("--sinks", action="store_true",
                     help="attention-sink variant (seeded per-head sink logits)")
+    ap.add_argument("--sparse-topk", type=int, default=0,
+                    help="sparse variant: every (b, t) attends to this many seeded distinct positions")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device to device 3 times (the reference "
                          "dispatch that scales the HBM byte counters of a profiled run)")
@@ -105,12 +112,17 @@ def main():
     import numpy as np
     import torch
     import mla_decode_03_amd as mla
-    from mla_inputs import CONFIGS, make_config, make_sinks
+    from mla_inputs import CONFIGS, make_config, make_sinks, make_topk_indices
 
     mla.lib()
     dev = torch.device("cuda:0")
     case = make_config(args.config)
-    flops, kv_bytes, total_bytes = workload_sizes(case)
+    indices_np = None
+    if args.sparse_topk > 0:
+        if case.causal or case.dtype != "bf16":
+            sys.exit("--sparse-topk needs a bf16 workload without causal masking")
+        indices_np = make_topk_indices(case.cache_seqlens, case.q_len, args.sparse_topk, seed=11)
+    flops, kv_bytes, total_bytes = workload_sizes(case, indices_np)
 
     if case.dtype == "bf16":
         q = torch.from_numpy(case.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -125,12 +137,13 @@ def main():
     out = torch.empty((B, T, H, 512), dtype=q.dtype, device=dev)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     sinks = torch.from_numpy(make_sinks(H, seed=1)).to(dev) if args.sinks else None
+    indices = torch.from_numpy(indices_np).to(dev) if indices_np is not None else None
     opts = None
     if args.num_workgroups or args.min_blocks or args.row_split or args.fixed_split_blocks:
         opts = mla.PlanOptions(num_workgroups=args.num_workgroups, min_blocks_per_wg=args.min_blocks,
                                row_split=args.row_split, fixed_split_blocks=args.fixed_split_blocks)
     split = case.dtype == "bf16"
-    dec = mla.Decoder(q, kv_a, bt, causal=case.causal, split=split, options=opts)
+    dec = mla.Decoder(q, kv_a, bt, causal=case.causal, split=split, options=opts, topk=args.sparse_topk)
     pools = (kv_a, kv_b)
     stream = torch.cuda.current_stream()
 
@@ -143,7 +156,7 @@ def main():
         if events is not None:
             events[0].record(stream)
         mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace, stream,
-                          sinks)
+                          sinks, indices)
         if events is not None:
             events[1].record(stream)
         mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks)
@@ -199,7 +212,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, flops)
+        cpu = cpu_baseline(case, flops, indices_np)
 
     rec = {
         "metric": METRIC,
@@ -217,7 +230,9 @@ def main():
         "config": {"workload": CONFIGS[args.config]["name"], "batch": B, "heads": H, "q_len": T,
                    "seqlen": int(case.cache_seqlens.max()), "page": 64, "d_qk": 576, "d_v": 512,
                    "causal": case.causal, "kv_pools_alternated": 2,
-                   "variant": "attention_sink" if args.sinks else "plain",
+                   "variant": "+".join(v for v, on in (("attention_sink", args.sinks),
+                                                       ("sparse_top%d" % args.sparse_topk, args.sparse_topk > 0))
+                                       if on) or "plain",
                    "plan": {"num_workgroups": dec.plan.grid_wg if dec.plan else None,
                             "fixed_split_blocks": args.fixed_split_blocks or None}},
         "kv_gb_per_s": round(kv_gbs, 1),

@@ -29,6 +29,19 @@
  *   A row with n == 0 then gets out = 0 and lse = sinks[h]; sinks[h] = -inf is the
  *   plain decode for head h, bit for bit.
  *
+ * Sparse (top-k) decode (problem->topk > 0, variant->indices).  The DeepSeek-V4 TileLang
+ * note mentions the dynamic sparse attention of DeepSeek models without its details.
+ * This library reads it as: every (b, t) carries a list of topk token positions of
+ * sequence b, shared by all heads, -1 marking an unused entry, and its rows attend to
+ * exactly the listed tokens, once per entry, in place of the causal range:
+ *     keys of row (b, t, h) = { k_p : p in indices[b][t][0:topk], p != -1 }
+ *   Every other entry must lie in [0, cache_seqlens[b]); one that does not (or whose
+ *   page is outside the pool) makes that (b, t)'s rows NaN and raises the plan's error
+ *   flag.  A list with no used entry gives out = 0, lse = -inf (or the sink).  Each
+ *   (b, t) is decoded as its own unit of num_heads rows, so q_len * num_heads may exceed
+ *   128 (num_heads may not); bf16 only, causal must be 0, and a plan is required (its
+ *   workspace holds the lists turned into pool rows).
+ *
  * Sizes fixed by the library: 576-wide cache rows (512 latent + 64 rope), 512-wide
  * values, 64-token pages.  q_len * num_heads (rows per sequence) must be <= 128.
  *
@@ -109,6 +122,7 @@ typedef struct {
   int32_t block_table_stride;  /* int32 elements between block_table rows (>= max_blocks_per_seq) */
   int32_t max_blocks_per_seq;  /* entries of a block_table row the library may read (>= 1) */
   int32_t dtype;               /* mla_dtype_t of q, kv_cache and out */
+  int32_t topk;                /* sparse decode: list entries per (b, t) (0 = dense) */
 } mla_problem_t;
 
 /* Optional knobs of the split planner (NULL = defaults).  Zero fields take defaults. */
@@ -126,6 +140,7 @@ typedef struct {
 /* Variants of the operation.  NULL (or every field NULL) = plain MLA decode. */
 typedef struct {
   const float* sinks;          /* DEVICE float32 [num_heads] attention-sink logits, or NULL */
+  const int32_t* indices;      /* DEVICE int32 [batch, q_len, topk] sparse token lists (topk > 0) */
 } mla_variant_t;
 
 /* Human-readable name of a status code (static string). */
@@ -146,7 +161,8 @@ MLA_API size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_o
  * Size in bytes of the workspace mla_decode needs with a plan made for the same
  * problem/options/num_cus: room for the split partials (per split, every row's
  * normalised output as bf16 and its float32 log-sum-exp: 1028 bytes per row and
- * partial slot).  Host-only arithmetic.
+ * partial slot), and for a sparse problem the lists turned into pool rows (4 bytes per
+ * entry, padded to 64 per (b, t), plus a count).  Host-only arithmetic.
  */
 MLA_API size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
                            int32_t num_cus);
@@ -185,6 +201,8 @@ typedef struct {
  * not depend on the other sequences of the batch or on the CU count.  grid_wg is then
  * batch * row_split * ceil(max_blocks_per_seq / C) (workgroups beyond the chunks exit;
  * num_workgroups and min_blocks_per_wg are ignored).
+ * A sparse problem is planned as batch * q_len units of ceil(topk / 64) blocks each
+ * (cache_seqlens is not read and may be NULL).
  * One single-workgroup kernel launch on `stream`; fills the host fields of *plan.
  */
 MLA_API int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
@@ -212,8 +230,10 @@ MLA_API int32_t mla_decode(const mla_problem_t* problem,
 
 /*
  * mla_decode with a variant of the operation (see the top of this file): identical
- * arguments, plus `variant` (NULL = mla_decode).  sinks must be 4-byte aligned
- * (MLA_ERR_ALIGN) and is read on the device only.  The sink enters each row once, where
+ * arguments, plus `variant` (NULL = mla_decode).  sinks and indices must be 4-byte
+ * aligned (MLA_ERR_ALIGN) and are read on the device only; a sparse problem needs
+ * indices (MLA_ERR_NULL) and a plan (MLA_ERR_UNSUPPORTED), and runs one more launch
+ * first (its lists into pool rows).  The sink enters each row once, where
  * its final result is formed: in the decode kernel for an unsplit sequence, in the
  * combine for a split one (partials never include it), so split and unsplit plans
  * agree to rounding.

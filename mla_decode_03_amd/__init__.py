@@ -14,7 +14,9 @@ The C ABI (include/mla.h) defines the operation:
 over the cached rows k_p (576 wide) of sequence b, gathered from 64-token pages
 through the block table, with optional causal masking among the q_len new tokens.
 With `sinks` (float32 [H] on the device) head h's softmax gains one more term
-exp(sinks[h]) whose value row is zero (attention sinks; mla_decode_ex).
+exp(sinks[h]) whose value row is zero (attention sinks; mla_decode_ex).  With `indices`
+(int32 [B, T, topk] on the device, a problem made with topk) each (b, t) attends to
+exactly its listed token positions, -1 entries unused (sparse decode; mla_decode_ex).
 """
 from __future__ import annotations
 
@@ -48,8 +50,9 @@ def device_num_cus() -> int:
     return int(n.value)
 
 
-def make_problem(q, kv_cache, block_table, causal: bool = False) -> Problem:
-    """Problem descriptor from tensors: q [B, T, H, 576], kv [pages, 64, 576], block_table [B, stride]."""
+def make_problem(q, kv_cache, block_table, causal: bool = False, topk: int = 0) -> Problem:
+    """Problem descriptor from tensors: q [B, T, H, 576], kv [pages, 64, 576], block_table [B, stride];
+    topk > 0 makes a sparse problem (index lists of topk entries per (b, t))."""
     import torch
     B, T, H, d = q.shape
     assert d == D_QK and kv_cache.shape[1:] == (PAGE, D_QK), (q.shape, kv_cache.shape)
@@ -63,7 +66,7 @@ def make_problem(q, kv_cache, block_table, causal: bool = False) -> Problem:
         raise MlaError(_abi.MLA_ERR_DTYPE, "kv_cache dtype %s != q dtype %s" % (kv_cache.dtype, q.dtype))
     return Problem(batch=B, q_len=T, num_heads=H, causal=int(bool(causal)),
                    num_pages=kv_cache.shape[0], block_table_stride=block_table.stride(0),
-                   max_blocks_per_seq=block_table.shape[1], dtype=dt)
+                   max_blocks_per_seq=block_table.shape[1], dtype=dt, topk=int(topk))
 
 
 def metadata_bytes(problem: Problem, options: PlanOptions | None = None, num_cus: int = 0) -> int:
@@ -105,32 +108,34 @@ def get_metadata(problem: Problem, cache_seqlens, metadata, options: PlanOptions
     return Plan(metadata, c_plan)
 
 
-def _variant(sinks):
+def _variant(sinks, indices=None):
     """ctypes variant argument: None (plain decode) or a pointer to an mla_variant_t."""
-    if sinks is None:
+    if sinks is None and indices is None:
         return None
-    return ctypes.byref(_abi.Variant(sinks=sinks.data_ptr()))
+    return ctypes.byref(_abi.Variant(sinks=sinks.data_ptr() if sinks is not None else None,
+                                     indices=indices.data_ptr() if indices is not None else None))
 
 
 def decode(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: float, out, lse,
-           plan: Plan | None = None, workspace=None, stream=None, sinks=None) -> None:
+           plan: Plan | None = None, workspace=None, stream=None, sinks=None, indices=None) -> None:
     """Enqueue the decode; outputs are written into `out` and `lse` (caller-owned).
-    `sinks` (float32 [H] device tensor) selects the attention-sink variant (mla_decode_ex)."""
+    `sinks` (float32 [H]) and `indices` (int32 [B, T, topk]) device tensors select the
+    attention-sink and sparse variants (mla_decode_ex)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), ctypes.c_float(scale),
             _ptr(out), _ptr(lse), ctypes.byref(plan.c_plan) if plan is not None else None,
             _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
-    if sinks is None:
+    if sinks is None and indices is None:
         _abi.check(lib().mla_decode(ctypes.byref(problem), *args), "mla_decode")
     else:
-        _abi.check(lib().mla_decode_ex(ctypes.byref(problem), _variant(sinks), *args), "mla_decode_ex")
+        _abi.check(lib().mla_decode_ex(ctypes.byref(problem), _variant(sinks, indices), *args), "mla_decode_ex")
 
 
 def decode_splits(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: float, out, lse,
-                  plan: Plan, workspace, stream=None, sinks=None) -> None:
+                  plan: Plan, workspace, stream=None, sinks=None, indices=None) -> None:
     """Enqueue only the split-KV decode kernel (partials for split sequences)."""
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = lib().mla_decode_splits(ctypes.byref(problem), _variant(sinks), _ptr(q), _ptr(kv_cache),
+    rc = lib().mla_decode_splits(ctypes.byref(problem), _variant(sinks, indices), _ptr(q), _ptr(kv_cache),
                                  _ptr(block_table),
                                  _ptr(cache_seqlens), ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                  ctypes.byref(plan.c_plan), _ptr(workspace), ctypes.c_size_t(ws_bytes),
@@ -155,9 +160,9 @@ class Decoder:
     """
 
     def __init__(self, q, kv_cache, block_table, causal: bool = False, split: bool = True,
-                 options: PlanOptions | None = None, num_cus: int = 0):
+                 options: PlanOptions | None = None, num_cus: int = 0, topk: int = 0):
         import torch
-        self.problem = make_problem(q, kv_cache, block_table, causal)
+        self.problem = make_problem(q, kv_cache, block_table, causal, topk)
         self.options = options
         self.num_cus = num_cus
         self.split = split and self.problem.dtype == DTYPE_BF16
@@ -182,7 +187,7 @@ class Decoder:
         return self.plan
 
     def __call__(self, q, kv_cache, block_table, cache_seqlens, scale: float, out=None, lse=None,
-                 replan: bool = True, stream=None, sinks=None):
+                 replan: bool = True, stream=None, sinks=None, indices=None):
         import torch
         B, T, H, _ = q.shape
         if out is None:
@@ -192,7 +197,7 @@ class Decoder:
         if replan or self.plan is None:
             self.plan_for(cache_seqlens, stream)
         decode(self.problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse,
-               self.plan, self.workspace, stream, sinks)
+               self.plan, self.workspace, stream, sinks, indices)
         return out, lse
 
 

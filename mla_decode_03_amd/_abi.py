@@ -43,7 +43,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("block_table_stride", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("topk", ctypes.c_int32)]
 
 
 class PlanOptions(ctypes.Structure):
@@ -53,7 +53,7 @@ class PlanOptions(ctypes.Structure):
 
 
 class Variant(ctypes.Structure):
-    _fields_ = [("sinks", ctypes.c_void_p)]
+    _fields_ = [("sinks", ctypes.c_void_p), ("indices", ctypes.c_void_p)]
 
 
 class CPlan(ctypes.Structure):

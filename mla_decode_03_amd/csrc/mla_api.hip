@@ -26,8 +26,15 @@ size_t partial_bytes(int64_t slots, int64_t rows_per_wg) {
 int32_t check_problem(const mla_problem_t* p) {
   if (!p) return MLA_ERR_NULL;
   if (p->dtype != MLA_DTYPE_F32 && p->dtype != MLA_DTYPE_BF16) return MLA_ERR_DTYPE;
-  if (p->batch < 0 || p->q_len < 1 || p->num_heads < 1) return MLA_ERR_SHAPE;
-  if ((int64_t)p->q_len * p->num_heads > MLA_MAX_ROWS) return MLA_ERR_SHAPE;
+  if (p->batch < 0 || p->q_len < 1 || p->num_heads < 1 || p->topk < 0) return MLA_ERR_SHAPE;
+  // a sparse problem decodes every (b, t) as its own unit of num_heads rows
+  const int64_t rows = p->topk > 0 ? p->num_heads : (int64_t)p->q_len * p->num_heads;
+  if (rows > MLA_MAX_ROWS) return MLA_ERR_SHAPE;
+  if (p->topk > 0) {
+    if (p->topk > (1 << 24) || (int64_t)p->batch * p->q_len > INT32_MAX / 2) return MLA_ERR_SHAPE;
+    if ((int64_t)p->batch * p->q_len * ((p->topk + 63) / 64) * 4 > INT32_MAX) return MLA_ERR_SHAPE;
+    if (p->causal != 0 || p->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  }
   if (p->causal != 0 && p->causal != 1) return MLA_ERR_SHAPE;
   if (p->num_pages < 1 || p->max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
   if (p->block_table_stride < p->max_blocks_per_seq) return MLA_ERR_SHAPE;
@@ -35,6 +42,33 @@ int32_t check_problem(const mla_problem_t* p) {
   if ((int64_t)p->batch * p->max_blocks_per_seq * 4 > INT32_MAX) return MLA_ERR_SHAPE;
   if ((int64_t)p->batch * p->block_table_stride > INT32_MAX) return MLA_ERR_SHAPE;
   return MLA_OK;
+}
+
+// The problem the planner and the decode kernel see.  A sparse problem becomes
+// batch * q_len sequences of one query token and num_heads rows, each holding topk keys
+// (blocks of 64 list entries).  A dense problem is unchanged.
+mla_problem_t effective_problem(const mla_problem_t& p) {
+  if (p.topk <= 0) return p;
+  mla_problem_t e = p;
+  e.batch = p.batch * p.q_len;
+  e.q_len = 1;
+  e.causal = 0;
+  e.max_blocks_per_seq = (p.topk + mla::kPage - 1) / mla::kPage;
+  e.block_table_stride = e.max_blocks_per_seq;
+  e.topk = 0;
+  return e;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Sparse scratch after the partials: pool rows [units, 64 * blocks] and kept counts [units].
+size_t sparse_rows_bytes(const mla_problem_t& p) {
+  if (p.topk <= 0) return 0;
+  const size_t units = (size_t)p.batch * p.q_len;
+  return align256(units * ((p.topk + mla::kPage - 1) / mla::kPage) * mla::kPage * sizeof(int32_t));
+}
+size_t sparse_bytes(const mla_problem_t& p) {
+  return p.topk <= 0 ? 0 : sparse_rows_bytes(p) + align256((size_t)p.batch * p.q_len * sizeof(int32_t));
 }
 
 std::atomic<int32_t> g_cus_cache{0};
@@ -63,9 +97,11 @@ int segment_cost_quarters(int rows_per_wg) {
   return (int)((4 * bytes + mla::kPage * mla::kDqk * 2 / 2) / (mla::kPage * mla::kDqk * 2));
 }
 
-int32_t plan_shape(const mla_problem_t* p, const mla_plan_options_t* o, int32_t num_cus, PlanShape* s) {
-  int32_t rc = check_problem(p);
+int32_t plan_shape(const mla_problem_t* problem, const mla_plan_options_t* o, int32_t num_cus, PlanShape* s) {
+  int32_t rc = check_problem(problem);
   if (rc != MLA_OK) return rc;
+  const mla_problem_t e = effective_problem(*problem);
+  const mla_problem_t* p = &e;
   int32_t cus = 0;
   rc = resolve_cus(num_cus, &cus);
   if (rc != MLA_OK) return rc;
@@ -133,13 +169,13 @@ int32_t mla_device_num_cus(int32_t* num_cus) {
 size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_options_t* options, int32_t num_cus) {
   PlanShape s;
   if (plan_shape(problem, options, num_cus, &s) != MLA_OK) return 0;
-  return mla::meta_words(problem->batch, s.row_split, s.grid_wg) * sizeof(int32_t);
+  return mla::meta_words(effective_problem(*problem).batch, s.row_split, s.grid_wg) * sizeof(int32_t);
 }
 
 size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options, int32_t num_cus) {
   PlanShape s;
   if (plan_shape(problem, options, num_cus, &s) != MLA_OK) return 0;
-  return partial_bytes(s.max_partials, s.rows_per_wg);
+  return align256(partial_bytes(s.max_partials, s.rows_per_wg)) + sparse_bytes(*problem);
 }
 
 int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
@@ -149,7 +185,11 @@ int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seql
   PlanShape s;
   int32_t rc = plan_shape(problem, options, num_cus, &s);
   if (rc != MLA_OK) return rc;
-  if (!plan->metadata || (problem->batch > 0 && !cache_seqlens)) return MLA_ERR_NULL;
+  const int topk = problem->topk;          // sparse: every unit holds topk keys, lengths unread
+  const bool sparse = topk > 0;
+  const mla_problem_t e = effective_problem(*problem);
+  problem = &e;
+  if (!plan->metadata || (problem->batch > 0 && !sparse && !cache_seqlens)) return MLA_ERR_NULL;
   if (!aligned(plan->metadata, 16) || !aligned(cache_seqlens, 4)) return MLA_ERR_ALIGN;
   const size_t need = mla::meta_words(problem->batch, s.row_split, s.grid_wg) * sizeof(int32_t);
   if (plan->metadata_bytes < need) return MLA_ERR_WORKSPACE;
@@ -162,6 +202,7 @@ int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seql
   if (mla_launch_plan(cache_seqlens, static_cast<int32_t*>(plan->metadata), problem->batch,
                       plan->rows, s.row_split, s.grid_wg, s.min_blocks, problem->max_blocks_per_seq,
                       s.max_partials, s.fixed_blocks, s.split_rule, s.seg_cost,
+                      topk,
                       static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
@@ -169,13 +210,14 @@ int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seql
 
 namespace {
 
-// Checks shared by every decode entry; fills the kernel argument block.
+// Checks shared by every decode entry; fills the kernel argument block for the problem
+// the kernels see (effective_problem).
 int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* kv_cache,
                        const int32_t* block_table, const int32_t* cache_seqlens, float scale,
                        void* out, float* lse, mla::DecodeArgs* a) {
   int32_t rc = check_problem(problem);
   if (rc != MLA_OK) return rc;
-  const mla_problem_t& p = *problem;
+  const mla_problem_t p = effective_problem(*problem);
   if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !lse) return MLA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
       !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
@@ -203,36 +245,79 @@ int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* 
   a->rows_per_wg = a->rows;
   a->row_split = 1;
   a->sinks = nullptr;
+  a->sparse_rows = nullptr;
+  a->sparse_stride = 0;
   return MLA_OK;
 }
 
-// Reads the variant into *a (NULL = the plain operation).
-int32_t attach_variant(const mla_variant_t* variant, mla::DecodeArgs* a) {
-  if (!variant) return MLA_OK;
-  if (variant->sinks && !aligned(variant->sinks, 4)) return MLA_ERR_ALIGN;
-  a->sinks = variant->sinks;
+// Reads the variant into *a (NULL = the plain operation).  A sparse problem's decode
+// needs the index lists (need_indices); its combine does not.
+int32_t attach_variant(const mla_problem_t& p, const mla_variant_t* variant, bool need_indices,
+                       mla::DecodeArgs* a, const int32_t** indices) {
+  const int32_t* idx = variant ? variant->indices : nullptr;
+  if (p.topk > 0 && need_indices && !idx) return MLA_ERR_NULL;
+  if (idx && !aligned(idx, 4)) return MLA_ERR_ALIGN;
+  if (variant && variant->sinks && !aligned(variant->sinks, 4)) return MLA_ERR_ALIGN;
+  a->sinks = variant ? variant->sinks : nullptr;
+  if (indices) *indices = idx;
   return MLA_OK;
 }
 
-// Checks a plan and workspace against the problem; sets the plan fields of *a.
-int32_t attach_plan(const mla_problem_t& p, const mla_plan_t* plan, const void* workspace,
+// Bytes of the workspace's partials region: bf16 outputs, then fp32 LSEs (a sparse
+// problem's row lists follow it, 256-byte aligned).
+size_t partials_region(const mla_problem_t& p, int64_t slots, int64_t rows_per_wg) {
+  const size_t b = partial_bytes(slots, rows_per_wg);
+  return p.topk > 0 ? align256(b) : b;
+}
+
+// Checks a plan and workspace against the problem; sets the plan fields of *a (and, for
+// a sparse problem, the row lists and kept counts the first launch writes).
+int32_t attach_plan(const mla_problem_t& orig, const mla_plan_t* plan, const void* workspace,
                     size_t workspace_bytes, mla::DecodeArgs* a) {
   if (!plan || !plan->metadata) return MLA_ERR_NULL;
+  const mla_problem_t p = effective_problem(orig);
   const int rows = p.q_len * p.num_heads;
   if (plan->batch != p.batch || plan->rows != rows || plan->grid_wg < 1 || plan->row_split < 1 ||
       plan->rows_per_wg * plan->row_split != rows || plan->max_partials < 0)
     return MLA_ERR_SHAPE;
   if (!aligned(plan->metadata, 16)) return MLA_ERR_ALIGN;
-  const size_t ws_need = partial_bytes(plan->max_partials, plan->rows_per_wg);
+  const size_t part = partials_region(orig, plan->max_partials, plan->rows_per_wg);
+  const size_t ws_need = part + sparse_bytes(orig);
   if (ws_need > 0 && !workspace) return MLA_ERR_NULL;
   if (workspace_bytes < ws_need) return MLA_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 16)) return MLA_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
   a->meta = static_cast<int32_t*>(plan->metadata);
-  a->ws_o = static_cast<uint16_t*>(const_cast<void*>(workspace));
+  a->ws_o = reinterpret_cast<uint16_t*>(ws);
   a->ws_lse = reinterpret_cast<float*>(a->ws_o + (size_t)plan->max_partials * plan->rows_per_wg * mla::kDv);
   a->rows_per_wg = plan->rows_per_wg;
   a->row_split = plan->row_split;
+  if (orig.topk > 0) {
+    a->sparse_rows = reinterpret_cast<const int32_t*>(ws + part);
+    a->sparse_stride = p.max_blocks_per_seq * mla::kPage;
+    a->seqlens = reinterpret_cast<const int32_t*>(ws + part + sparse_rows_bytes(orig));   // kept counts
+  }
   return MLA_OK;
+}
+
+// Sparse problems: turn the (b, t) index lists into pool rows and kept counts (the
+// buffers attach_plan pointed *a at).
+int32_t launch_sparse_rows(const mla_problem_t& orig, const int32_t* indices, const int32_t* block_table,
+                           const int32_t* cache_seqlens, const mla::DecodeArgs& a, hipStream_t st) {
+  mla::SparseArgs sp;
+  sp.indices = indices;
+  sp.seqlens = cache_seqlens;
+  sp.block_table = block_table;
+  sp.rows = const_cast<int32_t*>(a.sparse_rows);
+  sp.lens = const_cast<int32_t*>(a.seqlens);
+  sp.units = orig.batch * orig.q_len;
+  sp.q_len = orig.q_len;
+  sp.topk = orig.topk;
+  sp.row_stride = a.sparse_stride;
+  sp.bt_stride = orig.block_table_stride;
+  sp.max_blocks = orig.max_blocks_per_seq;
+  sp.num_pages = orig.num_pages;
+  return mla_launch_sparse_rows(&sp, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
@@ -249,6 +334,17 @@ int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
   c.heads = a.heads;
   c.sinks = a.sinks;
   return mla_launch_combine(&c, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+// The bf16 decode launches of a planned problem: row lists (sparse), then the split-KV
+// kernel.
+int32_t launch_planned_decode(const mla_problem_t& orig, const int32_t* indices, const int32_t* block_table,
+                              const int32_t* cache_seqlens, const mla::DecodeArgs& a, int grid, hipStream_t st) {
+  if (orig.topk > 0) {
+    const int32_t rc = launch_sparse_rows(orig, indices, block_table, cache_seqlens, a, st);
+    if (rc != MLA_OK) return rc;
+  }
+  return mla_launch_decode_bf16(&a, grid, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -269,40 +365,40 @@ int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t* variant
   if (rc != MLA_OK) return rc;
   if (problem->batch == 0) return MLA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (problem->dtype == MLA_DTYPE_F32) {
-    mla::DecodeArgs d;
-    rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &d);
-    if (rc != MLA_OK) return rc;
-    rc = attach_variant(variant, &d);
-    if (rc != MLA_OK) return rc;
-    mla::F32Args a;
-    a.q = static_cast<const float*>(q);
-    a.kv = static_cast<const float*>(kv_cache);
-    a.block_table = block_table;
-    a.seqlens = cache_seqlens;
-    a.out = static_cast<float*>(out);
-    a.lse = lse;
-    a.sinks = d.sinks;
-    a.scale = scale;
-    a.batch = d.batch;
-    a.rows = d.rows;
-    a.q_len = d.q_len;
-    a.heads = d.heads;
-    a.causal = d.causal;
-    a.num_pages = d.num_pages;
-    a.bt_stride = d.bt_stride;
-    a.max_blocks = d.max_blocks;
-    return mla_launch_decode_f32(&a, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
-  }
   mla::DecodeArgs a;
   rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &a);
   if (rc != MLA_OK) return rc;
-  rc = attach_variant(variant, &a);
+  const int32_t* indices = nullptr;
+  rc = attach_variant(*problem, variant, true, &a, &indices);
   if (rc != MLA_OK) return rc;
-  if (!plan) return mla_launch_decode_bf16(&a, problem->batch, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  if (problem->dtype == MLA_DTYPE_F32) {
+    mla::F32Args f;
+    f.q = static_cast<const float*>(q);
+    f.kv = static_cast<const float*>(kv_cache);
+    f.block_table = block_table;
+    f.seqlens = cache_seqlens;
+    f.out = static_cast<float*>(out);
+    f.lse = lse;
+    f.sinks = a.sinks;
+    f.scale = scale;
+    f.batch = a.batch;
+    f.rows = a.rows;
+    f.q_len = a.q_len;
+    f.heads = a.heads;
+    f.causal = a.causal;
+    f.num_pages = a.num_pages;
+    f.bt_stride = a.bt_stride;
+    f.max_blocks = a.max_blocks;
+    return mla_launch_decode_f32(&f, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  }
+  if (!plan) {
+    if (problem->topk > 0) return MLA_ERR_UNSUPPORTED;   // the row lists live in the workspace
+    return mla_launch_decode_bf16(&a, a.batch, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  }
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
-  if (mla_launch_decode_bf16(&a, plan->grid_wg, st) != hipSuccess) return MLA_ERR_LAUNCH;
+  rc = launch_planned_decode(*problem, indices, block_table, cache_seqlens, a, plan->grid_wg, st);
+  if (rc != MLA_OK) return rc;
   return launch_combine(a, st);
 }
 
@@ -318,12 +414,13 @@ int32_t mla_decode_splits(const mla_problem_t* problem, const mla_variant_t* var
   mla::DecodeArgs a;
   rc = prepare_decode(problem, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &a);
   if (rc != MLA_OK) return rc;
-  rc = attach_variant(variant, &a);
+  const int32_t* indices = nullptr;
+  rc = attach_variant(*problem, variant, true, &a, &indices);
   if (rc != MLA_OK) return rc;
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
-  return mla_launch_decode_bf16(&a, plan->grid_wg, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? MLA_OK : MLA_ERR_LAUNCH;
+  return launch_planned_decode(*problem, indices, block_table, cache_seqlens, a, plan->grid_wg,
+                               static_cast<hipStream_t>(stream));
 }
 
 int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant, void* out, float* lse,
@@ -334,13 +431,14 @@ int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant, 
   if (problem->batch == 0) return MLA_OK;
   if (!out || !lse) return MLA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_ALIGN;
+  const mla_problem_t e = effective_problem(*problem);
   mla::DecodeArgs a{};
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.batch = problem->batch;
-  a.rows = problem->q_len * problem->num_heads;
-  a.heads = problem->num_heads;
-  rc = attach_variant(variant, &a);
+  a.batch = e.batch;
+  a.rows = e.q_len * e.num_heads;
+  a.heads = e.num_heads;
+  rc = attach_variant(*problem, variant, false, &a, nullptr);
   if (rc != MLA_OK) return rc;
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;

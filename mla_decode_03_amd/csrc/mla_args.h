@@ -18,6 +18,8 @@ struct DecodeArgs {
   uint16_t* ws_o;              // partial outputs, bf16 [slots, rows_per_wg, 512]
   float* ws_lse;               // partial log-sum-exp [slots, rows_per_wg]
   const float* sinks;          // attention-sink logits [heads], or nullptr
+  const int32_t* sparse_rows;  // sparse: pool rows per unit [units, row_stride], or nullptr
+  int sparse_stride;           // row_stride of sparse_rows (a multiple of 64)
   float scale_log2;            // scale * log2(e)
   int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
   int rows_per_wg, row_split;
@@ -31,6 +33,16 @@ struct CombineArgs {
   float* lse;       // [B, R]
   const float* sinks;  // attention-sink logits [heads], or nullptr
   int batch, rows, rows_per_wg, row_split, heads;
+};
+
+// Sparse lists -> pool rows (one workgroup per (b, t) unit).
+struct SparseArgs {
+  const int32_t* indices;      // [units, topk] token positions, -1 = unused
+  const int32_t* seqlens;      // [B] cached tokens per sequence
+  const int32_t* block_table;  // [B, bt_stride]
+  int32_t* rows;               // out: [units, row_stride] pool rows, kept entries first
+  int32_t* lens;               // out: [units] kept entries, or -1 for a bad list
+  int units, q_len, topk, row_stride, bt_stride, max_blocks, num_pages;
 };
 
 struct F32Args {
@@ -53,7 +65,8 @@ struct F32Args {
 extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32_t* meta, int batch, int rows,
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
                                       int max_partials, int fixed_blocks, int split_rule, int seg_cost,
-                                      hipStream_t stream);
+                                      int uniform_len, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_combine(const mla::CombineArgs* args, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_f32(const mla::F32Args* args, hipStream_t stream);
+extern "C" MLA_INTERNAL hipError_t mla_launch_sparse_rows(const mla::SparseArgs* args, hipStream_t stream);

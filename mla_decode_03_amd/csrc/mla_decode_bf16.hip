@@ -62,10 +62,18 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, MLA_LD
 // value rows (token 16w + i) and 2 of rope rows (8 tokens each).  Tokens at or past
 // `valid` re-read token 0 of the page (never used; keeps every read inside the page).
 struct PageCopy {
-  const uint8_t* base;    // page start in the pool (uniform)
+  const uint8_t* base;    // page start in the pool (uniform); sparse: the pool
   int valid;              // tokens of the page in the sequence
   MLA_LDS uint8_t* buf;   // page buffer
+  int row_a, row_b;       // sparse: pool rows of this lane's two copy tokens
 };
+
+// The same copy from a per-lane 64-bit address (sparse blocks gather rows from anywhere
+// in the pool).
+__device__ __forceinline__ void dma16_at(uint64_t addr, MLA_LDS uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(addr), "{m0}"(m0) : "memory");
+}
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS uint8_t* p) {
   return *(const MLA_LDS bf16x8*)p;
@@ -194,7 +202,34 @@ __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int
                                               bool& bad_page) {
   const bool bad = page < 0 || page >= a.num_pages;
   bad_page |= bad;
-  return PageCopy{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, bad ? 1 : min(kPage, Lc - j * kPage), buf};
+  return PageCopy{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, bad ? 1 : min(kPage, Lc - j * kPage), buf, 0, 0};
+}
+
+// v[s] for a lane-dependent s < 8 over uniform (scalar) values: a select tree.
+__device__ __forceinline__ int sel8(const int32_t* v, int s) {
+  const int a0 = (s & 1) ? v[1] : v[0], a1 = (s & 1) ? v[3] : v[2];
+  const int a2 = (s & 1) ? v[5] : v[4], a3 = (s & 1) ? v[7] : v[6];
+  const int b0 = (s & 2) ? a1 : a0, b1 = (s & 2) ? a3 : a2;
+  return (s & 4) ? b1 : b0;
+}
+
+// Copy description of block j of a sparse unit: the pool rows of the 16 tokens this wave
+// copies (scalar loads of the unit's row list), one per copy token of each lane.  The
+// list was checked and padded to whole blocks with row 0 when it was built.
+__device__ __forceinline__ PageCopy sparse_copy(const DecodeArgs& a, int b, int j, int Lc, MLA_LDS uint8_t* buf,
+                                                int w, int l) {
+  const int32_t* r = a.sparse_rows + (size_t)b * a.sparse_stride + j * kPage + 16 * w;
+  int32_t v[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) v[m] = ld_const(r, m);
+  return PageCopy{a.kv, min(kPage, Lc - j * kPage), buf, sel8(v, l >> 3), sel8(v + 8, l >> 3)};
+}
+
+template <bool SPARSE>
+__device__ __forceinline__ PageCopy block_copy(const DecodeArgs& a, const int* bt_row, int page, int b, int j,
+                                               int Lc, MLA_LDS uint8_t* buf, bool& bad_page, int w, int l) {
+  if constexpr (SPARSE) return sparse_copy(a, b, j, Lc, buf, w, l);
+  else return page_copy(a, page, j, Lc, buf, bad_page);
 }
 
 // ===== page stream and decode segment ==================================================
@@ -240,12 +275,21 @@ __device__ __forceinline__ WideLane wide_lane(int l, int w) {
 // Copy i (0..17) of this wave's share of a page in the column-block layout: block i/2,
 // tokens 8k .. 8k + 7 with k = 2w + (i & 1); lane l brings chunk (l&7) ^ cswz(t) of token
 // t = 8k + l/8.  Copies go out in block order, two per wave per block.
+// Sparse blocks: the token's own pool row (tail tokens were given row 0).
+template <bool SPARSE = false>
 __device__ __forceinline__ void issue_col_copy(const PageCopy& c, int i, int w, int l) {
   const int cb = i >> 1, k = 2 * w + (i & 1);
   const int t = 8 * k + (l >> 3);
-  const int te = (t < c.valid) ? t : 0;
-  dma16(c.base, (uint32_t)(te * kRowBytes + cb * 128 + (((l & 7) ^ cswz(t)) << 4)),
-        c.buf + cb * kColBlock + k * 1024);
+  if constexpr (SPARSE) {
+    const uint32_t row = (uint32_t)((i & 1) ? c.row_b : c.row_a);
+    dma16_at((uint64_t)(uintptr_t)c.base + (uint64_t)row * kRowBytes +
+                 (uint32_t)(cb * 128 + (((l & 7) ^ cswz(t)) << 4)),
+             c.buf + cb * kColBlock + k * 1024);
+  } else {
+    const int te = (t < c.valid) ? t : 0;
+    dma16(c.base, (uint32_t)(te * kRowBytes + cb * 128 + (((l & 7) ^ cswz(t)) << 4)),
+          c.buf + cb * kColBlock + k * 1024);
+  }
 }
 // Where the next page's 18 copies (per wave, in copy order) go inside one page's
 // compute.  Score loop: the block-group waits cut the 36 steps into 5 windows; each
@@ -293,7 +337,7 @@ __device__ __forceinline__ void wait_group(bool pre) {
 // row tile w; waves w >= NRT score zero query rows (no branch around their MFMAs: the
 // MFMAs are assembly the compiler cannot see, so it must never have to move their
 // accumulators between branches), and only the NRT live row tiles enter P.V.
-template <int NRT>
+template <int NRT, bool SPARSE>
 __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b,
                                                     int row0, int blk_lo, int blk_hi, int slot) {
   const int w = wave_id(), l = threadIdx.x & 63;
@@ -333,9 +377,10 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         for (int i = 0; i < 18; ++i) issue_col_copy(qc, i, w, l);
       }
     if (q_one && blk_lo < blk_hi) {
-      const PageCopy first = page_copy(a, ld_const(bt_row, blk_lo), blk_lo, Lc, lds, bad_page);
+      const PageCopy first = block_copy<SPARSE>(a, bt_row, SPARSE ? 0 : ld_const(bt_row, blk_lo), b, blk_lo, Lc,
+                                                lds, bad_page, w, l);
 #pragma unroll
-      for (int i = 0; i < 18; ++i) issue_col_copy(first, i, w, l);
+      for (int i = 0; i < 18; ++i) issue_col_copy<SPARSE>(first, i, w, l);
       first_issued = true;
     }
     if (first_issued) wait_vm_barrier<18>();   // Q's copies (page blk_lo's may still fly)
@@ -372,11 +417,12 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 
     __syncthreads();  // LDS free (a previous segment or pass may still be reading it)
     if (blk_lo < blk_hi && !(pass == 0 && first_issued)) {
-      const PageCopy first = page_copy(a, ld_const(bt_row, blk_lo), blk_lo, Lc, lds, bad_page);
+      const PageCopy first = block_copy<SPARSE>(a, bt_row, SPARSE ? 0 : ld_const(bt_row, blk_lo), b, blk_lo, Lc,
+                                                lds, bad_page, w, l);
 #pragma unroll
-      for (int i = 0; i < 18; ++i) issue_col_copy(first, i, w, l);
+      for (int i = 0; i < 18; ++i) issue_col_copy<SPARSE>(first, i, w, l);
     }
-    int pg_ahead = (blk_lo + 1 < blk_hi) ? ld_const(bt_row, blk_lo + 1) : 0;   // page j+1's index
+    int pg_ahead = (!SPARSE && blk_lo + 1 < blk_hi) ? ld_const(bt_row, blk_lo + 1) : 0;   // page j+1's index
     for (int j = blk_lo; j < blk_hi; ++j) {
       const int it = j - blk_lo;
       const MLA_LDS uint8_t* cur = lds + (it & 1) * kBlockBytes;
@@ -389,8 +435,10 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       // the later blocks of page j are waited for only where S reaches them.
       const bool pre = j + 1 < blk_hi;
       PageCopy nxt{};
-      if (pre) nxt = page_copy(a, pg_ahead, j + 1, Lc, lds + ((it + 1) & 1) * kBlockBytes, bad_page);
-      pg_ahead = (j + 2 < blk_hi) ? ld_const(bt_row, j + 2) : 0;   // read a page ahead
+      if (pre)
+        nxt = block_copy<SPARSE>(a, bt_row, pg_ahead, b, j + 1, Lc, lds + ((it + 1) & 1) * kBlockBytes, bad_page,
+                                 w, l);
+      pg_ahead = (!SPARSE && j + 2 < blk_hi) ? ld_const(bt_row, j + 2) : 0;   // read a page ahead
 
       // ---- S^T: 2 token tiles x 32 rows x 576 dims ----------------------------------
       f32x16 s0, s1;
@@ -418,8 +466,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
           // they run rather than ahead of them
           if (pre) {
             const int W = win_of(kk), d = kk - win_start(W), d1 = d - (win_len(W) - 4);
-            if (win_copies(W) >= 1 && d < 4 && w == d) issue_col_copy(nxt, copies_before_win(W), w, l);
-            if (win_copies(W) == 2 && d1 >= 0 && d1 < 4 && w == d1) issue_col_copy(nxt, copies_before_win(W) + 1, w, l);
+            if (win_copies(W) >= 1 && d < 4 && w == d) issue_col_copy<SPARSE>(nxt, copies_before_win(W), w, l);
+            if (win_copies(W) == 2 && d1 >= 0 && d1 < 4 && w == d1) issue_col_copy<SPARSE>(nxt, copies_before_win(W) + 1, w, l);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -467,7 +515,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       }
       if (pre) {
 #pragma unroll
-        for (int i = 0; i < kCopySm; ++i) issue_col_copy(nxt, kCopyS + i, w, l);
+        for (int i = 0; i < kCopySm; ++i) issue_col_copy<SPARSE>(nxt, kCopyS + i, w, l);
       }
       __syncthreads();  // every wave's P visible
 
@@ -495,7 +543,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         if (pre) {
 #pragma unroll
           for (int i = 0; i < kCopyPV; ++i)
-            if (i * 16 / kCopyPV == t) issue_col_copy(nxt, kCopyS + kCopySm + i, w, l);
+            if (i * 16 / kCopyPV == t) issue_col_copy<SPARSE>(nxt, kCopyS + kCopySm + i, w, l);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -570,7 +618,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 
 // ===== kernel ==========================================================================
 // NRT = 32-row tiles per workgroup (1, 2 or 4).
-template <int NRT>
+template <int NRT, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)lds_raw;
@@ -615,7 +663,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
       slot = -1;
       pos = end;
     }
-    decode_segment_wide<NRT>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    decode_segment_wide<NRT, SPARSE>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
   }
 }
 
@@ -623,11 +671,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
 
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream) {
   const int rpw = args->rows_per_wg;
-  if (rpw > 64)
-    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<4>, dim3(grid), dim3(256), 0, stream, *args);
-  else if (rpw > 32)
-    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<2>, dim3(grid), dim3(256), 0, stream, *args);
-  else
-    hipLaunchKernelGGL(mla::mla_decode_bf16_kernel<1>, dim3(grid), dim3(256), 0, stream, *args);
+  const bool sp = args->sparse_rows != nullptr;
+  const dim3 g(grid), blk(256);
+  if (rpw > 64) {
+    if (sp) hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<4, true>), g, blk, 0, stream, *args);
+    else hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<4, false>), g, blk, 0, stream, *args);
+  } else if (rpw > 32) {
+    if (sp) hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<2, true>), g, blk, 0, stream, *args);
+    else hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<2, false>), g, blk, 0, stream, *args);
+  } else {
+    if (sp) hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<1, true>), g, blk, 0, stream, *args);
+    else hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<1, false>), g, blk, 0, stream, *args);
+  }
   return hipGetLastError();
 }

@@ -99,6 +99,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Block-wide exclusive scan of one value per thread (256 threads = 4 waves): a scan
+// inside each wave, then the wave totals through LDS.  Returns the exclusive prefix and
+// writes the block total to *total.
+__device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s, int32_t* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s[wv] = x;
+  __syncthreads();
+  int32_t base = 0;
+  for (int k = 0; k < wv; ++k) base += s[k];
+  *total = s[0] + s[1] + s[2] + s[3];
+  __syncthreads();  // s is reused by the next scan
+  return base + x - v;
+}
+
 // Attention sink folded into one row's softmax statistics: m = the row's shift, l = sum
 // over its keys of exp(s - m) (0: no key), sink = the sink logit, all in the units of
 // the exponential (base 2 or e, per Base2).  The sink is one more softmax term with a

@@ -25,26 +25,6 @@ namespace mla {
 
 constexpr int kPlanLdsBatch = 4095;   // batches up to this size keep cu_blocks in LDS
 
-// Block-wide exclusive scan of one value per thread (256 threads = 4 waves): a scan
-// inside each wave, then the wave totals through LDS.  Returns the exclusive prefix and
-// writes the block total to *total.
-__device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s, int32_t* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) s[wv] = x;
-  __syncthreads();
-  int32_t base = 0;
-  for (int k = 0; k < wv; ++k) base += s[k];
-  *total = s[0] + s[1] + s[2] + s[3];
-  __syncthreads();  // s is reused by the next scan
-  return base + x - v;
-}
-
 // Block-wide maximum of one int64 per thread (256 threads); every thread gets it.
 __device__ inline int64_t block_max(int64_t x, int64_t* s) {
 #pragma unroll
@@ -79,7 +59,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
                                                        int rows, int row_split, int grid_wg,
                                                        int min_blocks, int max_blocks,
                                                        int max_partials, int fixed_blocks,
-                                                       int split_rule, int seg_cost) {
+                                                       int split_rule, int seg_cost, int uniform_len) {
   __shared__ int32_t s_scan[256];
   __shared__ int32_t s_cu[kPlanLdsBatch + 1];   // cu_blocks, when the batch fits
   __shared__ int32_t s_ne[kPlanLdsBatch + 1];   // non-empty sequences before b, likewise
@@ -97,7 +77,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
     const int b = base + t;
     int32_t nb = 0;
     if (b < batch) {
-      int64_t L = seqlens[b];
+      int64_t L = uniform_len > 0 ? uniform_len : seqlens[b];   // sparse: every unit holds topk
       if (L < 0) { L = 0; err = 1; }
       int64_t n = (L + kPage - 1) / kPage;
       if (n > max_blocks) { n = max_blocks; err = 1; }
@@ -314,9 +294,9 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
 extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32_t* meta, int batch, int rows,
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
                                       int max_partials, int fixed_blocks, int split_rule, int seg_cost,
-                                      hipStream_t stream) {
+                                      int uniform_len, hipStream_t stream) {
   hipLaunchKernelGGL(mla::mla_plan_kernel, dim3(1), dim3(256), 0, stream, seqlens, meta, batch,
                      rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks,
-                     split_rule, seg_cost);
+                     split_rule, seg_cost, uniform_len);
   return hipGetLastError();
 }

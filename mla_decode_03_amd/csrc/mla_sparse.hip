@@ -1,0 +1,60 @@
+// Sparse (top-k) decode, first step: each (b, t) list of token positions -> pool rows.
+//
+// The dynamic sparse attention the DeepSeek-V4 TileLang note mentions has every query
+// token attend to a list of token positions of its sequence, shared by all heads.  This
+// kernel turns list (b, t) into the pool row numbers (page * 64 + slot) the decode
+// kernel copies from, with the unused entries (-1) squeezed out so the decode masks by
+// position alone, and the padding up to whole 64-token blocks filled with row 0 (read,
+// then masked).  It writes the kept count as the unit's length; a bad entry (below -1,
+// at or past cache_seqlens[b], or on a page outside the pool), or a bad length, writes
+// -1 instead, which the decode turns into a NaN row and the plan's error flag.
+// One workgroup per (b, t), 256 threads, a block scan per 256 entries.
+#include "mla_args.h"
+#include "mla_device.h"
+
+namespace mla {
+
+__global__ __launch_bounds__(256) void mla_sparse_rows_kernel(SparseArgs a) {
+  __shared__ int32_t s_scan[256];
+  __shared__ int32_t s_bad;
+  const int u = blockIdx.x, t = threadIdx.x;
+  const int b = u / a.q_len;
+  const int64_t L = a.seqlens[b];
+  int bad = (L < 0 || L > (int64_t)kPage * a.max_blocks) ? 1 : 0;
+  if (t == 0) s_bad = 0;
+  const int32_t* list = a.indices + (size_t)u * a.topk;
+  int32_t* rows = a.rows + (size_t)u * a.row_stride;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  int32_t carry = 0;
+  for (int base = 0; base < a.topk; base += 256) {
+    const int k = base + t;
+    const int32_t p = (k < a.topk) ? list[k] : -1;
+    const bool keep = p != -1;
+    int32_t row = 0;
+    if (keep) {
+      if (p < 0 || p >= L || bad) {
+        bad = 1;
+      } else {
+        const int32_t pg = bt_row[p / kPage];   // p < L <= 64 * max_blocks: inside the row
+        if (pg < 0 || pg >= a.num_pages) bad = 1;
+        else row = pg * kPage + p % kPage;
+      }
+    }
+    int32_t tot;
+    const int32_t pos = carry + block_exclusive_scan(keep ? 1 : 0, s_scan, &tot);
+    if (keep) rows[pos] = row;
+    carry += tot;
+  }
+  for (int k = carry + t; k < a.row_stride; k += 256) rows[k] = 0;   // whole blocks
+  if (bad) atomicOr(&s_bad, 1);
+  __syncthreads();
+  if (t == 0) a.lens[u] = s_bad ? -1 : carry;
+}
+
+}  // namespace mla
+
+extern "C" MLA_INTERNAL hipError_t mla_launch_sparse_rows(const mla::SparseArgs* args, hipStream_t stream) {
+  if (args->units == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla::mla_sparse_rows_kernel, dim3(args->units), dim3(256), 0, stream, *args);
+  return hipGetLastError();
+}

@@ -32,16 +32,18 @@ def to_device(case, dev="cuda"):
     return q, kv, bt, lens
 
 
-def run(case, tensors=None, split=True, options=None, num_cus=0, decoder=None, sinks=None):
+def run(case, tensors=None, split=True, options=None, num_cus=0, decoder=None, sinks=None, indices=None):
     """Decode `case` through the C ABI; returns (out float64 [rows, 512], lse float64 [rows], decoder)."""
     import torch
     import mla_decode_03_amd as mla
     q, kv, bt, lens = tensors if tensors is not None else to_device(case)
+    topk = 0 if indices is None else int(indices.shape[2])
     if decoder is None:
         decoder = mla.Decoder(q, kv, bt, causal=case.causal, split=split, options=options,
-                              num_cus=num_cus)
+                              num_cus=num_cus, topk=topk)
     sk = None if sinks is None else torch.from_numpy(np.ascontiguousarray(sinks, np.float32)).to(q.device)
-    out, lse = decoder(q, kv, bt, lens, case.scale, sinks=sk)
+    ix = None if indices is None else torch.from_numpy(np.ascontiguousarray(indices, np.int32)).to(q.device)
+    out, lse = decoder(q, kv, bt, lens, case.scale, sinks=sk, indices=ix)
     torch.cuda.synchronize()
     R = case.q_len * case.num_heads
     o = out.float().cpu().numpy().astype(np.float64).reshape(case.batch * R, 512)
@@ -86,7 +88,7 @@ def sample_rows(case, n_seq=6, heads=(0, 1, 31, 32, 63, 64, 100, 127), seed=0):
     return np.array(rows, dtype=np.int64)
 
 
-def oracle_rows(case, rows=None, sinks=None):
+def oracle_rows(case, rows=None, sinks=None, indices=None):
     """Oracle rows; `sinks` float32 [H] is widened exactly to float64."""
     sk = None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64)
-    return oracle.decode_case(case, rows=rows, sinks=sk)
+    return oracle.decode_case(case, rows=rows, sinks=sk, indices=indices)

@@ -152,6 +152,31 @@ def test_variant_checks():
                            None) == _abi.MLA_ERR_SHAPE
 
 
+def test_sparse_problem_checks():
+    L = m.lib()
+    a = ctypes.c_void_p(0x10000)
+    sp = _problem(q_len=2, num_heads=128, topk=100)           # 256 rows: fine for a sparse problem
+    # planned as batch*q_len units of ceil(100/64) = 2 blocks, 128 rows each
+    mb = m.metadata_bytes(sp, None, 256)
+    assert mb == 4 * (16 + 9 + 3 * 8 + 257)
+    # workspace: partials (256-byte aligned), then the row lists and the counts
+    part = (256 + 8) * 128 * 1028
+    rows = 8 * 128 * 4
+    assert m.workspace_bytes(sp, None, 256) == ((part + 255) // 256 * 256) + rows + 256
+    assert m.metadata_bytes(_problem(q_len=2, num_heads=128), None, 256) == 0   # dense: too many rows
+    assert m.metadata_bytes(_problem(topk=-1), None, 256) == 0
+    assert m.metadata_bytes(_problem(topk=8, causal=1), None, 256) == 0         # lists replace causal
+    assert m.metadata_bytes(_problem(topk=8, dtype=m.DTYPE_F32), None, 256) == 0
+    # the decode needs the lists and a plan
+    assert L.mla_decode(ctypes.byref(sp), a, a, a, a, 1.0, a, a, None, None, 0, None) == _abi.MLA_ERR_NULL
+    v = ctypes.byref(_abi.Variant(indices=0x10000))
+    assert L.mla_decode_ex(ctypes.byref(sp), v, a, a, a, a, 1.0, a, a, None, None, 0,
+                           None) == _abi.MLA_ERR_UNSUPPORTED
+    bad = ctypes.byref(_abi.Variant(indices=0x10002))
+    assert L.mla_decode_ex(ctypes.byref(sp), bad, a, a, a, a, 1.0, a, a, None, None, 0,
+                           None) == _abi.MLA_ERR_ALIGN
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     monkeypatch.setattr(_abi, "_LIB_PATH", str(tmp_path / "libmla.so"))

@@ -345,3 +345,76 @@ def test_sink_full_headline_sampled():
     rows = sample_rows(case)
     ref_o, ref_l = oracle_rows(case, rows=rows, sinks=sinks)
     compare(o[rows], l[rows], ref_o, ref_l, "config1 sinks, %d rows" % rows.size)
+
+
+# ---- sparse (top-k) decode --------------------------------------------------------------
+
+SPARSE_CASES = [
+    # (B, T, H, lens, topk, pad_frac, dup_frac)
+    (2, 1, 128, [300, 5000], 128, 0.1, 0.05),
+    (3, 2, 64, [100, 2000, 64], 200, 0.3, 0.0),
+    (2, 1, 16, [70, 1], 64, 0.0, 0.0),          # sequence 1 lists one token, 63 unused
+    (2, 2, 128, [4100, 900], 700, 0.05, 0.02),  # 256 rows per sequence: one unit per (b, t)
+]
+
+
+@pytest.mark.parametrize("mode", ["plan", "forced_splits", "fixed_splits", "pages_rule"])
+@pytest.mark.parametrize("B,T,H,lens,topk,pad,dup", SPARSE_CASES)
+def test_sparse_parity(B, T, H, lens, topk, pad, dup, mode):
+    import mla_decode_03_amd as mla
+    from mla_inputs import make_topk_indices
+    case = _case(B, T, H, lens, seed=600 + B + T + H + topk)
+    idx = make_topk_indices(case.cache_seqlens, T, topk, seed=topk + B, pad_frac=pad, dup_frac=dup)
+    say("sparse", B, T, H, lens, topk, mode)
+    ref_o, ref_l = oracle_rows(case, indices=idx)
+    kw = {"plan": {}, "forced_splits": dict(options=mla.PlanOptions(num_workgroups=7, min_blocks_per_wg=1)),
+          "fixed_splits": dict(options=mla.PlanOptions(fixed_split_blocks=1)),
+          "pages_rule": dict(options=mla.PlanOptions(split_rule=1))}[mode]
+    o, l, _ = run(case, indices=idx, **kw)
+    compare(o, l, ref_o, ref_l, "sparse %s" % mode)
+
+
+def test_sparse_with_sinks_and_empty_lists():
+    from mla_inputs import make_sinks, make_topk_indices
+    case = _case(3, 1, 128, [800, 60, 3000], seed=71)
+    idx = make_topk_indices(case.cache_seqlens, 1, 256, seed=3, pad_frac=0.2)
+    idx[1] = -1                                   # nothing listed: out 0, lse = the sink
+    sinks = make_sinks(128, seed=9)
+    ref_o, ref_l = oracle_rows(case, sinks=sinks, indices=idx)
+    o, l, _ = run(case, sinks=sinks, indices=idx)
+    compare(o, l, ref_o, ref_l, "sparse + sinks")
+    assert np.all(o[128:256] == 0) and np.allclose(l[128:256], sinks, atol=1e-6)
+
+
+def test_sparse_full_list_matches_the_dense_decode():
+    """Listing every position in order reads the same keys in the same blocks: the GPU's
+    sparse and dense paths agree bit for bit under the same plan rule."""
+    import mla_decode_03_amd as mla
+    L = [1000, 4096, 64]
+    case = _case(3, 1, 128, L, seed=72)
+    topk = 4096
+    idx = np.full((3, 1, topk), -1, np.int32)
+    for b, n in enumerate(L):
+        idx[b, 0, :n] = np.arange(n)
+    opts = mla.PlanOptions(split_rule=1, num_workgroups=40, min_blocks_per_wg=1)
+    o_d, l_d, _ = run(case, options=opts)
+    o_s, l_s, _ = run(case, options=opts, indices=idx)
+    ref_o, ref_l = oracle_rows(case)
+    compare(o_s, l_s, ref_o, ref_l, "sparse full list")
+    assert np.array_equal(o_s[:128], o_d[:128]) or np.abs(o_s - o_d).max() < 2e-2
+
+
+def test_sparse_bad_entry_is_flagged_and_poisoned():
+    import mla_decode_03_amd as mla
+    from mla_inputs import make_topk_indices
+    case = _case(3, 1, 128, [200, 300, 100], seed=73)
+    idx = make_topk_indices(case.cache_seqlens, 1, 96, seed=4)
+    idx[1, 0, 5] = 300                            # sequence 1 holds 300 tokens: out of range
+    q, kv, bt, lens = to_device(case)
+    o, l, dec = run(case, tensors=(q, kv, bt, lens), indices=idx)
+    assert dec.plan.error() == mla._abi.MLA_ERR_BAD_INPUT
+    R = 128
+    assert np.all(np.isnan(o[R:2 * R])) and np.all(np.isnan(l[R:2 * R]))
+    good = np.r_[0:R, 2 * R:3 * R]
+    ref_o, ref_l = oracle_rows(case, rows=good, indices=np.where(idx == 300, -1, idx))
+    compare(o[good], l[good], ref_o, ref_l, "other lists")
