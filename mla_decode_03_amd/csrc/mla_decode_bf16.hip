@@ -65,7 +65,7 @@ struct PageCopy {
   const uint8_t* base;    // page start in the pool (uniform); sparse: the pool
   int valid;              // tokens of the page in the sequence
   MLA_LDS uint8_t* buf;   // page buffer
-  int row_a, row_b;       // sparse: pool rows of this lane's two copy tokens
+  int row_a, row_b;       // sparse: 9 x the pool rows of this lane's two copy tokens
 };
 
 // The same copy from a per-lane 64-bit address (sparse blocks gather rows from anywhere
@@ -222,7 +222,7 @@ __device__ __forceinline__ PageCopy sparse_copy(const DecodeArgs& a, int b, int 
   int32_t v[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m) v[m] = ld_const(r, m);
-  return PageCopy{a.kv, min(kPage, Lc - j * kPage), buf, sel8(v, l >> 3), sel8(v + 8, l >> 3)};
+  return PageCopy{a.kv, min(kPage, Lc - j * kPage), buf, 9 * sel8(v, l >> 3), 9 * sel8(v + 8, l >> 3)};
 }
 
 template <bool SPARSE>
@@ -275,16 +275,19 @@ __device__ __forceinline__ WideLane wide_lane(int l, int w) {
 // Copy i (0..17) of this wave's share of a page in the column-block layout: block i/2,
 // tokens 8k .. 8k + 7 with k = 2w + (i & 1); lane l brings chunk (l&7) ^ cswz(t) of token
 // t = 8k + l/8.  Copies go out in block order, two per wave per block.
-// Sparse blocks: the token's own pool row (tail tokens were given row 0).
+// Sparse blocks: the token's own pool row (tail tokens were given row 0).  A row is
+// 9 lines of 128 B, so the chunk's address is pool + ((9 row + cb) << 7) + its 16-byte
+// slot: one 32-bit add and one 64-bit shift-add per copy, with only the two per-parity
+// lane bases (pool + slot) loop-invariant (the 64-bit per-copy offsets would otherwise
+// be hoisted out of the loop and spilled).
 template <bool SPARSE = false>
 __device__ __forceinline__ void issue_col_copy(const PageCopy& c, int i, int w, int l) {
   const int cb = i >> 1, k = 2 * w + (i & 1);
   const int t = 8 * k + (l >> 3);
   if constexpr (SPARSE) {
-    const uint32_t row = (uint32_t)((i & 1) ? c.row_b : c.row_a);
-    dma16_at((uint64_t)(uintptr_t)c.base + (uint64_t)row * kRowBytes +
-                 (uint32_t)(cb * 128 + (((l & 7) ^ cswz(t)) << 4)),
-             c.buf + cb * kColBlock + k * 1024);
+    const uint32_t line = (uint32_t)((i & 1) ? c.row_b : c.row_a) + (uint32_t)cb;
+    const uint64_t lane_base = (uint64_t)(uintptr_t)c.base + (uint32_t)(((l & 7) ^ cswz(t)) << 4);
+    dma16_at(((uint64_t)line << 7) + lane_base, c.buf + cb * kColBlock + k * 1024);
   } else {
     const int te = (t < c.valid) ? t : 0;
     dma16(c.base, (uint32_t)(te * kRowBytes + cb * 128 + (((l & 7) ^ cswz(t)) << 4)),
@@ -448,20 +451,23 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
           k0 = lds_read_b128(p);
           k1 = lds_read_b128(p + 32 * 128);
         };
-        bf16x8 kr0[kPrefK + 1], kr1[kPrefK + 1];
+        // Sparse blocks hold two more per-lane values (their copy rows) through the page;
+        // a one-step K prefetch there frees the registers.  The block-group waits stay
+        // where the two-step schedule puts them (one step early for the one-step loads).
+        constexpr int PK = SPARSE ? 1 : kPrefK;
+        bf16x8 kr0[PK + 1], kr1[PK + 1];
 #pragma unroll
-        for (int kk = 0; kk < kPrefK; ++kk) load_k(kk, kr0[kk], kr1[kk]);
+        for (int kk = 0; kk < PK; ++kk) load_k(kk, kr0[kk], kr1[kk]);
 #pragma unroll
         for (int kk = 0; kk < 36; ++kk) {
           // before the first read of blocks 2G, 2G+1: wait for them
-          const int kl = kk + kPrefK;
+          const int kl = kk + kPrefK;            // the wait schedule's load step
           if (kl == 8) wait_group<1>(pre);
           if (kl == 16) wait_group<2>(pre);
           if (kl == 24) wait_group<3>(pre);
           if (kl == 32) wait_group<4>(pre);
-          if (kl < 36)
-            load_k(kl, kr0[kl % (kPrefK + 1)], kr1[kl % (kPrefK + 1)]);
-          mfma32_s_step(s0, s1, kr0[kk % (kPrefK + 1)], kr1[kk % (kPrefK + 1)], qf[kk], kk);
+          if (kk + PK < 36) load_k(kk + PK, kr0[(kk + PK) % (PK + 1)], kr1[(kk + PK) % (PK + 1)]);
+          mfma32_s_step(s0, s1, kr0[kk % (PK + 1)], kr1[kk % (PK + 1)], qf[kk], kk);
           // a copy issued behind the step's MFMAs stalls (on a full memory queue) while
           // they run rather than ahead of them
           if (pre) {

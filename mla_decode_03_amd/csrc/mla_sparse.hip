@@ -8,7 +8,7 @@
 // then masked).  It writes the kept count as the unit's length; a bad entry (below -1,
 // at or past cache_seqlens[b], or on a page outside the pool), or a bad length, writes
 // -1 instead, which the decode turns into a NaN row and the plan's error flag.
-// One workgroup per (b, t), 256 threads, a block scan per 256 entries.
+// One workgroup per (b, t), 256 threads, a block scan per 2048 entries.
 #include "mla_args.h"
 #include "mla_device.h"
 
@@ -25,24 +25,37 @@ __global__ __launch_bounds__(256) void mla_sparse_rows_kernel(SparseArgs a) {
   const int32_t* list = a.indices + (size_t)u * a.topk;
   int32_t* rows = a.rows + (size_t)u * a.row_stride;
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  // 8 consecutive entries per thread and round, every load of a round in flight at once
+  // (index, then its block-table entry), then one scan of the per-thread counts keeps
+  // the list order.
+  constexpr int kPer = 8;
   int32_t carry = 0;
-  for (int base = 0; base < a.topk; base += 256) {
-    const int k = base + t;
-    const int32_t p = (k < a.topk) ? list[k] : -1;
-    const bool keep = p != -1;
-    int32_t row = 0;
-    if (keep) {
-      if (p < 0 || p >= L || bad) {
+  for (int base = 0; base < a.topk; base += 256 * kPer) {
+    int32_t p[kPer], row[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int k = base + kPer * t + e;
+      p[e] = (k < a.topk) ? list[k] : -1;
+    }
+    int32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      row[e] = 0;
+      if (p[e] == -1) continue;
+      ++cnt;
+      if (p[e] < 0 || p[e] >= L || bad) {
         bad = 1;
       } else {
-        const int32_t pg = bt_row[p / kPage];   // p < L <= 64 * max_blocks: inside the row
+        const int32_t pg = bt_row[p[e] / kPage];   // p < L <= 64 * max_blocks: inside the row
         if (pg < 0 || pg >= a.num_pages) bad = 1;
-        else row = pg * kPage + p % kPage;
+        else row[e] = pg * kPage + p[e] % kPage;
       }
     }
     int32_t tot;
-    const int32_t pos = carry + block_exclusive_scan(keep ? 1 : 0, s_scan, &tot);
-    if (keep) rows[pos] = row;
+    int32_t pos = carry + block_exclusive_scan(cnt, s_scan, &tot);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (p[e] != -1) rows[pos++] = row[e];
     carry += tot;
   }
   for (int k = carry + t; k < a.row_stride; k += 256) rows[k] = 0;   // whole blocks
