@@ -24,6 +24,7 @@
 namespace mla {
 
 constexpr int kPlanLdsBatch = 4095;   // batches up to this size keep cu_blocks in LDS
+constexpr int kPlanLdsWg = 1024;      // plans up to this many workgroups keep both cuts in LDS
 
 // Block-wide maximum of one int64 per thread (256 threads); every thread gets it.
 __device__ inline int64_t block_max(int64_t x, int64_t* s) {
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
   __shared__ int32_t s_cu[kPlanLdsBatch + 1];   // cu_blocks, when the batch fits
   __shared__ int32_t s_ne[kPlanLdsBatch + 1];   // non-empty sequences before b, likewise
   __shared__ int64_t s_red[4];
+  __shared__ int32_t s_bp[kPlanLdsWg + 1], s_bc[kPlanLdsWg + 1];   // the two rules' cuts
   const int t = threadIdx.x;
   const bool cu_in_lds = batch <= kPlanLdsBatch;
   MetaView v = meta_view(meta, batch, row_split);
@@ -71,8 +73,10 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
   int32_t* ne_glob = v.first_wg;
   int err = 0;
 
-  // 1. blocks per sequence and their prefix sums; non-empty sequences before each
+  // 1. blocks per sequence and their prefix sums; non-empty sequences before each; the
+  // largest sequence
   int32_t carry = 0, ne_carry = 0;
+  int64_t nb_max = 0;
   for (int base = 0; base < batch; base += 256) {
     const int b = base + t;
     int32_t nb = 0;
@@ -82,6 +86,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       int64_t n = (L + kPage - 1) / kPage;
       if (n > max_blocks) { n = max_blocks; err = 1; }
       nb = (int32_t)n;
+      nb_max = max<int64_t>(nb_max, n);
     }
     int32_t tot, ntot;
     const int32_t excl = block_exclusive_scan(nb, s_scan, &tot);
@@ -181,15 +186,15 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       const int b = seq_of_cost(x);
       const int64_t nb = cu_at(b + 1) - cu_at(b);
       const int64_t ucost = c + 4 * nb;
-      const int64_t g = (x - cost_at(b)) / ucost;
+      const int64_t g = rs == 1 ? 0 : floor_div(x - cost_at(b), ucost);
       const int64_t off = x - cost_at(b) - g * ucost;
-      return rs * cu_at(b) + g * nb + (off < c ? 0 : (off - c) / 4);
+      return rs * cu_at(b) + g * nb + (off < c ? 0 : (off - c) >> 2);
     };
     // rank of the unit holding block p among the non-empty units
     auto rank_of_block = [&](int64_t p) -> int64_t {
       const int b = seq_of_block(p);
       const int64_t nb = cu_at(b + 1) - cu_at(b);
-      return rs * ne_at(b) + (p - rs * cu_at(b)) / nb;
+      return rs * ne_at(b) + (rs == 1 ? 0 : floor_div(p - rs * cu_at(b), nb));
     };
     auto pages_begin = [&](int64_t w) -> int64_t { return floor_div(w * total, num_wg); };
     auto cost_begin = [&](int64_t w) -> int64_t { return block_at(floor_div(w * ctot, num_wg)); };
@@ -197,12 +202,35 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       return hi > lo ? 4 * (hi - lo) + c * (rank_of_block(hi - 1) - rank_of_block(lo) + 1) : 0;
     };
 
-    // 2. the busiest workgroup under each rule; keep the cheaper rule
+    // 2. the busiest workgroup under each rule; keep the cheaper rule.  When every
+    // non-empty unit holds the same nb blocks and the equal shares line up with the
+    // units (share a multiple of nb, or nb of share), every workgroup of the pages rule
+    // costs exactly the average, which no cut's busiest workgroup can beat: keep it
+    // without evaluating.  Otherwise each cut is computed once (kept in LDS when the plan
+    // fits).
     int64_t worst_p = 0, worst_c = 0;
-    if (split_rule == kRuleAuto && num_wg > 0) {
+    bool evaluate = split_rule == kRuleAuto && num_wg > 0;
+    if (evaluate) {
+      const int64_t nbm = block_max(nb_max, s_red);
+      const int64_t share = total / num_wg;
+      if ((int64_t)carry == nbm * ne_carry && share * num_wg == total && nbm > 0 &&
+          (share % nbm == 0 || nbm % share == 0))
+        evaluate = false;
+    }
+    const bool cuts_in_lds = evaluate && num_wg <= kPlanLdsWg;
+    if (cuts_in_lds) {
+      for (int w = t; w <= num_wg; w += 256) {
+        s_bp[w] = (int32_t)pages_begin(w);
+        s_bc[w] = (int32_t)cost_begin(w);
+      }
+      __syncthreads();
+    }
+    auto cut_p = [&](int64_t w) -> int64_t { return cuts_in_lds ? s_bp[w] : pages_begin(w); };
+    auto cut_c = [&](int64_t w) -> int64_t { return cuts_in_lds ? s_bc[w] : cost_begin(w); };
+    if (evaluate) {
       for (int64_t w = t; w < num_wg; w += 256) {
-        worst_p = max(worst_p, range_cost(pages_begin(w), pages_begin(w + 1)));
-        worst_c = max(worst_c, range_cost(cost_begin(w), cost_begin(w + 1)));
+        worst_p = max(worst_p, range_cost(cut_p(w), cut_p(w + 1)));
+        worst_c = max(worst_c, range_cost(cut_c(w), cut_c(w + 1)));
       }
       worst_p = block_max(worst_p, s_red);
       worst_c = block_max(worst_c, s_red);
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
 
     // 3. workgroup ranges
     for (int w = t; w <= grid_wg; w += 256)
-      v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)(use_cost ? cost_begin(w) : pages_begin(w))
+      v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)(use_cost ? cut_c(w) : cut_p(w))
                                                   : (int32_t)total;
     // workgroup holding block p: the largest w < num_wg whose range starts at or before p.
     // Cost rule: a cut at cost x lands at or before p exactly when x < Y, Y = the cost
@@ -224,39 +252,57 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       if (!use_cost) return wg_of(p, total, num_wg);
       const int b = seq_of_block(p);
       const int64_t nb = cu_at(b + 1) - cu_at(b);
-      const int64_t g = (p - rs * cu_at(b)) / nb;
+      const int64_t g = rs == 1 ? 0 : floor_div(p - rs * cu_at(b), nb);
       const int64_t y = cost_at(b) + g * (c + 4 * nb) + c + 4 * (p - rs * cu_at(b) - g * nb) + 4;
       return (int32_t)min<int64_t>(floor_div(y * num_wg - 1, ctot), num_wg - 1);
     };
     // 4. units: which workgroups cover each, and the partial slots of the split ones.
-    // First every unit's first workgroup and split count (first_wg still holds the
-    // non-empty prefix of large batches, so the first workgroup waits in part_off) ...
-    for (int u = t; u < units; u += 256) {
-      int32_t ns = 0, first = -1;
+    auto unit_span = [&](int u, int32_t& first) -> int32_t {
       const int b = u / rs, g = u % rs;
       const int64_t nb = cu_at(b + 1) - cu_at(b);
-      if (nb > 0) {
-        const int64_t start = rs * cu_at(b) + g * nb;
-        first = holder(start);
-        ns = holder(start + nb - 1) - first + 1;
+      first = -1;
+      if (nb == 0) return 0;
+      const int64_t start = rs * cu_at(b) + g * nb;
+      first = holder(start);
+      return holder(start + nb - 1) - first + 1;
+    };
+    if (cu_in_lds) {
+      for (int base = 0; base < units; base += 256) {
+        const int u = base + t;
+        int32_t ns = 0, first = -1;
+        if (u < units) {
+          ns = unit_span(u, first);
+          v.num_splits[u] = ns;
+          v.first_wg[u] = first;
+        }
+        int32_t tot;
+        const int32_t excl = block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &tot);
+        if (u < units) v.part_off[u] = pcarry + excl;
+        pcarry += tot;
       }
-      v.num_splits[u] = ns;
-      v.part_off[u] = first;
-    }
-    __threadfence_block();
-    __syncthreads();
-    // ... then, each unit by the thread that wrote it, the slots.
-    for (int base = 0; base < units; base += 256) {
-      const int u = base + t;
-      int32_t ns = 0;
-      if (u < units) {
-        ns = v.num_splits[u];
-        v.first_wg[u] = v.part_off[u];
+    } else {
+      // first_wg still holds the non-empty prefix: first every unit's span (the first
+      // workgroup waits in part_off) ...
+      for (int u = t; u < units; u += 256) {
+        int32_t first;
+        v.num_splits[u] = unit_span(u, first);
+        v.part_off[u] = first;
       }
-      int32_t tot;
-      const int32_t excl = block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &tot);
-      if (u < units) v.part_off[u] = pcarry + excl;
-      pcarry += tot;
+      __threadfence_block();
+      __syncthreads();
+      // ... then, each unit by the thread that wrote it, the slots.
+      for (int base = 0; base < units; base += 256) {
+        const int u = base + t;
+        int32_t ns = 0;
+        if (u < units) {
+          ns = v.num_splits[u];
+          v.first_wg[u] = v.part_off[u];
+        }
+        int32_t tot;
+        const int32_t excl = block_exclusive_scan(ns > 1 ? ns : 0, s_scan, &tot);
+        if (u < units) v.part_off[u] = pcarry + excl;
+        pcarry += tot;
+      }
     }
   }
 

@@ -9,7 +9,9 @@ units are laid end to end (sequence-major, then row slice) and the block range
          blocks of segment overhead and then 4 quarters per block (cuts in an
          overhead move to the unit's first block, cuts in its blocks round down).
 A workgroup costs 4 per block plus c per unit it touches; rule "auto" keeps the rule
-whose busiest workgroup costs less, pages on a tie.  c defaults to the traffic of a
+whose busiest workgroup costs less, pages on a tie.  It skips the comparison (and keeps
+pages, header costs 0) when every non-empty unit holds the same nb blocks and the equal
+shares line up with them (share a multiple of nb or nb of share).  c defaults to the traffic of a
 segment's rows: rows * 2180 B over 73,728 B per block, in quarters, rounded.  A unit cut
 across k > 1 workgroups owns k consecutive partial slots, numbered unit by unit.
 
@@ -51,7 +53,12 @@ def make_plan(seqlens, *, row_split=1, grid_wg=256, min_blocks=4, max_blocks=1 <
     costed = (_cost_bounds(nblk, cu, total, row_split, num_wg, c) + [total] * (grid_wg - num_wg)
               if num_wg > 0 else pages)
     worst_p = worst_c = 0
-    if rule == "auto" and num_wg > 0:
+    used = [n for n in nblk if n > 0]
+    aligned_even = False
+    if used and num_wg > 0 and min(used) == max(used) and total % num_wg == 0:
+        share, nbm = total // num_wg, max(used)
+        aligned_even = share % nbm == 0 or nbm % share == 0
+    if rule == "auto" and num_wg > 0 and not aligned_even:
         base = dict(cu_blocks=cu, num_wg=num_wg, row_split=row_split, batch=B)
         worst_p = plan_cost(dict(base, wg_begin=pages), c)
         worst_c = plan_cost(dict(base, wg_begin=costed), c)

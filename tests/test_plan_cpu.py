@@ -90,6 +90,28 @@ def test_auto_keeps_the_cheaper_rule(seed):
     assert auto["wg_begin"] == (cost if wc < wp else pages)["wg_begin"]
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_aligned_even_batches_need_no_comparison(seed):
+    """The shortcut's claim: with equal units and shares lined up with them, no cut of
+    either rule (nor any seg cost) beats the pages rule's busiest workgroup."""
+    rng = np.random.default_rng(300 + seed)
+    nb = int(rng.choice([1, 2, 4, 8, 16, 64]))
+    B = int(rng.integers(1, 80))
+    rs = [1, 2, 4][seed % 3]
+    lens = [nb * 64 if rng.random() < 0.8 else 0 for _ in range(B)]
+    if not any(lens):
+        lens[0] = nb * 64
+    total = rs * nb * sum(1 for L in lens if L)
+    shares = [d for d in range(1, total + 1) if total % d == 0 and (d % nb == 0 or nb % d == 0)]
+    share = int(rng.choice(shares))
+    grid = total // share
+    c = int(rng.integers(1, 40))
+    auto = make_plan(lens, row_split=rs, grid_wg=grid, min_blocks=1, seg_q=c)
+    assert auto["rule"] == 1 and auto["num_wg"] == grid
+    cost = make_plan(lens, row_split=rs, grid_wg=grid, min_blocks=1, rule="cost", seg_q=c)
+    assert plan_cost(auto, c) <= plan_cost(cost, c)
+
+
 def test_segment_cost_is_the_traffic_of_a_segments_rows():
     # 128 rows move 128 * (1152 + 1024 + 4) B besides their KV: 3.78 blocks -> 15 quarters
     assert segment_cost(128) == 15 and segment_cost(64) == 8 and segment_cost(32) == 4
@@ -98,7 +120,10 @@ def test_segment_cost_is_the_traffic_of_a_segments_rows():
 
 def test_even_batches_keep_the_pages_cut_and_ragged_ones_take_the_cost_cut():
     even = make_plan([4096] * 64, grid_wg=256)
-    assert even["rule"] == 1 and even["cost_pages"] < even["cost_balanced"]
+    assert even["rule"] == 1 and (even["cost_pages"], even["cost_balanced"]) == (0, 0)   # not compared
+    c = segment_cost(128)
+    assert plan_cost(make_plan([4096] * 64, grid_wg=256, rule="pages"), c) < \
+        plan_cost(make_plan([4096] * 64, grid_wg=256, rule="cost"), c)
     rng = np.random.default_rng(7)
     ragged = make_plan([int(x) for x in rng.integers(1, 2049, size=256)], grid_wg=256)
     assert ragged["rule"] == 2 and ragged["cost_balanced"] < ragged["cost_pages"]
