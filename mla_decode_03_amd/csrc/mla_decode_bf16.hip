@@ -329,11 +329,31 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
   __syncthreads();
 }
-template <int G>
-__device__ __forceinline__ void wait_group(bool pre) {
-  constexpr int kk = 8 * G - kPrefK;   // the step that first loads block 2G
-  if (pre) wait_vm_barrier<copies_after_group(G) + s_copies_before(kk)>();
-  else wait_vm_barrier<copies_after_group(G)>();
+// Which block group each wait point covers: point 0 is the page head, point S (1..4) the
+// score step that first loads block group S.  A point covers a group at or past its own
+// (loads complete in order, so covering a later group covers the earlier ones too);
+// -1 = no wait there, which needs an earlier point to have covered that group.
+constexpr int kWaitCover[5] = {0, 1, 2, 3, 4};
+constexpr bool wait_plan_ok() {
+  int covered = kWaitCover[0];
+  if (covered < 0) return false;
+  for (int S = 1; S <= 4; ++S) {
+    if (kWaitCover[S] >= 0) {
+      if (kWaitCover[S] < S || kWaitCover[S] <= covered) return false;
+      covered = kWaitCover[S];
+    }
+    if (covered < S) return false;
+  }
+  return true;
+}
+static_assert(wait_plan_ok(), "every block group is waited for before it is read");
+template <int S>
+__device__ __forceinline__ void wait_point(bool pre) {
+  if constexpr (kWaitCover[S] >= 0) {
+    constexpr int kk = 8 * S - kPrefK;   // the step that first loads block group S
+    if (pre) wait_vm_barrier<copies_after_group(kWaitCover[S]) + s_copies_before(kk)>();
+    else wait_vm_barrier<copies_after_group(kWaitCover[S])>();
+  }
 }
 
 // NRT = row tiles of 32 rows the workgroup holds (rows_per_wg <= 32 NRT).  Wave w scores
@@ -429,8 +449,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
     for (int j = blk_lo; j < blk_hi; ++j) {
       const int it = j - blk_lo;
       const MLA_LDS uint8_t* cur = lds + (it & 1) * kBlockBytes;
-      // blocks 0-1 of page j have landed (all waves); page j-1 and its P are consumed
-      wait_vm_barrier<14>();
+      // page j's first block groups have landed (all waves); page j-1 and its P are consumed
+      wait_vm_barrier<copies_after_group(kWaitCover[0])>();
       // Page j+1 streams into the other buffer while this page is computed: its 18 copies
       // per wave go out in block order, spread over the MFMA loops below (the copy
       // schedule above; the waits in S count on it),
@@ -462,10 +482,10 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         for (int kk = 0; kk < 36; ++kk) {
           // before the first read of blocks 2G, 2G+1: wait for them
           const int kl = kk + kPrefK;            // the wait schedule's load step
-          if (kl == 8) wait_group<1>(pre);
-          if (kl == 16) wait_group<2>(pre);
-          if (kl == 24) wait_group<3>(pre);
-          if (kl == 32) wait_group<4>(pre);
+          if (kl == 8) wait_point<1>(pre);
+          if (kl == 16) wait_point<2>(pre);
+          if (kl == 24) wait_point<3>(pre);
+          if (kl == 32) wait_point<4>(pre);
           if (kk + PK < 36) load_k(kk + PK, kr0[(kk + PK) % (PK + 1)], kr1[(kk + PK) % (PK + 1)]);
           mfma32_s_step(s0, s1, kr0[kk % (PK + 1)], kr1[kk % (PK + 1)], qf[kk], kk);
           // a copy issued behind the step's MFMAs stalls (on a full memory queue) while
