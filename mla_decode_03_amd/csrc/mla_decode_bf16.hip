@@ -296,16 +296,16 @@ __device__ __forceinline__ void issue_col_copy(const PageCopy& c, int i, int w, 
 }
 // Where the next page's 18 copies (per wave, in copy order) go inside one page's
 // compute.  Score loop: the block-group waits cut the 36 steps into 5 windows; each
-// window carries up to 2 copies per wave, wave w issuing its copies w steps after the window's
-// copy slots, so the four waves do not queue their copies behind each other at the
-// same step (every wave still issues the same copies before each wait, which keeps the
-// wait counts compile-time).  Then kCopySm after the softmax and the rest spread over
-// the 16 P.V steps.
+// window carries up to 2 copies per wave, at fixed steps (the first step of the window
+// and 4 steps before its end), the same for every wave, so the copy sites are
+// compile-time and every wave issues the same copies before each wait.  Then kCopySm
+// after the softmax and the rest spread over the 16 P.V steps.  (Staggering the waves'
+// copy steps by wave id needed a runtime condition at every step and was 5% slower.)
 constexpr int win_start(int W) { return W == 0 ? 0 : 8 * W - kPrefK; }
 constexpr int win_end(int W) { return W == 4 ? 36 : 8 * (W + 1) - kPrefK; }
 constexpr int win_of(int kk) { return kk < win_start(1) ? 0 : kk < win_start(2) ? 1 : kk < win_start(3) ? 2 : kk < win_start(4) ? 3 : 4; }
 constexpr int win_len(int W) { return win_end(W) - win_start(W); }
-// copies per window: wave w issues slot 0 at step start+w and slot 1 at step end-4+w
+// copies per window: slot 0 at the window's first step, slot 1 four steps before its end
 constexpr int win_copies(int W) { return win_len(W) >= 6 ? 2 : win_len(W) >= 4 ? 1 : 0; }
 // windows 1-3 are 8 steps long (2 copies each)
 constexpr int copies_before_win(int W) {
@@ -492,8 +492,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
           // they run rather than ahead of them
           if (pre) {
             const int W = win_of(kk), d = kk - win_start(W), d1 = d - (win_len(W) - 4);
-            if (win_copies(W) >= 1 && d < 4 && w == d) issue_col_copy<SPARSE>(nxt, copies_before_win(W), w, l);
-            if (win_copies(W) == 2 && d1 >= 0 && d1 < 4 && w == d1) issue_col_copy<SPARSE>(nxt, copies_before_win(W) + 1, w, l);
+            if (win_copies(W) >= 1 && d == 0) issue_col_copy<SPARSE>(nxt, copies_before_win(W), w, l);
+            if (win_copies(W) == 2 && d1 == 0) issue_col_copy<SPARSE>(nxt, copies_before_win(W) + 1, w, l);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
