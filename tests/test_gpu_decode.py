@@ -418,3 +418,72 @@ def test_sparse_bad_entry_is_flagged_and_poisoned():
     good = np.r_[0:R, 2 * R:3 * R]
     ref_o, ref_l = oracle_rows(case, rows=good, indices=np.where(idx == 300, -1, idx))
     compare(o[good], l[good], ref_o, ref_l, "other lists")
+
+
+# ---- capture, large batches, capacity edges -----------------------------------------------
+
+def test_graph_capture_replays_match_eager():
+    """Planner + decode (+ combine) captured in a HIP graph: nothing allocates or
+    synchronises, so every replay reproduces the eager result bit for bit, with eager
+    work on the stream between replays."""
+    import torch
+    import mla_decode_03_amd as mla
+    case = _case(4, 1, 128, [700, 64, 1, 3000], seed=81)
+    q, kv, bt, lens = to_device(case)
+    dec = mla.Decoder(q, kv, bt, num_cus=256)
+    out = torch.empty((4, 1, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((4, 1, 128), dtype=torch.float32, device="cuda")
+    dec(q, kv, bt, lens, case.scale, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        dec(q, kv, bt, lens, case.scale, out, lse)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda") * r     # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), r
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), r
+        del scratch
+    o = ref_o.float().cpu().numpy().astype(np.float64).reshape(-1, 512)
+    l = ref_l.cpu().numpy().astype(np.float64).reshape(-1)
+    ref = oracle_rows(case)
+    compare(o, l, ref[0], ref[1], "graph")
+
+
+def test_batch_beyond_the_planners_lds_path():
+    """4200 sequences (the planner keeps its prefix sums in global memory past 4095),
+    cost-model plan, decoded end to end; sampled rows against the oracle."""
+    rng = np.random.default_rng(82)
+    lens = [int(x) for x in rng.integers(0, 130, size=4200)]
+    case = _case(4200, 1, 16, lens, seed=82)
+    say("batch 4200, pages", case.num_pages)
+    o, l, dec = run(case)
+    assert dec.plan.error() == 0
+    rows = np.r_[np.arange(0, 64), np.arange(4200 * 16 - 64, 4200 * 16), rng.integers(0, 4200 * 16, 256)]
+    ref_o, ref_l = oracle_rows(case, rows=rows)
+    compare(o[rows], l[rows], ref_o, ref_l, "batch 4200 sampled")
+
+
+def test_lengths_at_and_past_the_block_table():
+    """L = 64 * max_blocks_per_seq is served; one token more is an input fault: that
+    sequence's rows are NaN, the flag is raised, the other sequences are untouched."""
+    import mla_decode_03_amd as mla
+    case = _case(3, 1, 128, [320, 100, 7], seed=83)      # block table: 5 columns
+    assert case.block_table.shape[1] == 5
+    ref_o, ref_l = oracle_rows(case)
+    o, l, dec = run(case)
+    assert dec.plan.error() == 0
+    compare(o, l, ref_o, ref_l, "L at capacity")
+    case.cache_seqlens[0] = 321
+    q, kv, bt, lens = to_device(case)
+    o2, l2, dec2 = run(case, tensors=(q, kv, bt, lens))
+    assert dec2.plan.error() == mla._abi.MLA_ERR_BAD_INPUT
+    assert np.all(np.isnan(o2[:128])) and np.all(np.isnan(l2[:128]))
+    compare(o2[128:], l2[128:], ref_o[128:], ref_l[128:], "others")
