@@ -370,3 +370,15 @@ def test_sparse_bad_entries_are_reported():
     with pytest.raises(RuntimeError, match="code 1"):   # sparse lists replace the causal rule
         c2 = _f32_case(1, 2, 1, [10], seed=94, causal=True)
         oracle.decode_case(c2, indices=np.zeros((1, 2, 2), np.int32))
+
+
+def test_sink_far_above_every_score_keeps_the_max_shift():
+    """A sink 800 above the scores: the softmax is all sink.  Without the sink in the
+    max shift, exp(800 - max score) overflows float64 and lse comes out infinite."""
+    case = _f32_case(1, 1, 2, [70], seed=84)
+    o, l = oracle.decode_case(case, sinks=[800.0, -800.0])
+    plain_o, plain_l = oracle.decode_case(case)
+    assert abs(l[0] - 800.0) < 1e-12 and np.all(np.abs(o[0]) < 1e-300)
+    # a sink far below changes nothing measurable
+    np.testing.assert_allclose(o[1], plain_o[1], rtol=1e-15, atol=0)
+    assert l[1] == plain_l[1]
