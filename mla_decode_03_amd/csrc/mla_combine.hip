@@ -9,7 +9,9 @@
 // lse = -inf.  Units decoded by one workgroup were written directly and are skipped.
 // With attention sinks the merged row takes its head's sink here (one more softmax term
 // with a zero value row): the partials never include it.
-// Memory-bound: 8 rows per workgroup, 32 threads per row, 16 output dims per thread.
+// Memory-bound: 8 rows per workgroup, 32 threads per row; thread t of a row owns dims
+// 8t .. 8t+7 and 256+8t .. 256+8t+7, so each 16-byte load or store instruction of a wave
+// covers whole 512-byte runs.  One pass over the partials (see the loop).
 #include "mla_args.h"
 #include "mla_device.h"
 
@@ -29,10 +31,10 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   const int b = u / a.row_split, g = u % a.row_split;
   const int r = g * a.rows_per_wg + rl;
   const int t = threadIdx.x & 31;
-  uint16_t* orow = a.out + ((size_t)b * a.rows + r) * kDv + 16 * t;
+  uint16_t* orow = a.out + ((size_t)b * a.rows + r) * kDv + 8 * t;
   if (ns == 0) {
     *(u32x4*)orow = u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)(orow + 8) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(orow + kDv / 2) = u32x4{0u, 0u, 0u, 0u};
     if (t == 0) a.lse[(size_t)b * a.rows + r] = a.sinks ? a.sinks[r % a.heads] : -INFINITY;
     return;
   }
@@ -40,45 +42,53 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  float tot = 0.f, Ms = 0.f;
-  // o_s rows of this thread: 16 bf16 = two 16-byte loads per split
-  auto part = [&](int sidx) { return (const u32x4*)(a.ws_o + ((size_t)(s0 + sidx) * a.rows_per_wg + rl) * kDv + 16 * t); };
-  auto accumulate = [&](float wgt, u32x4 x0, u32x4 x1) {
-    tot += wgt;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += wgt * __uint_as_float(x0[j] << 16);
-      acc[2 * j + 1] += wgt * __uint_as_float(x0[j] & 0xffff0000u);
-      acc[8 + 2 * j] += wgt * __uint_as_float(x1[j] << 16);
-      acc[8 + 2 * j + 1] += wgt * __uint_as_float(x1[j] & 0xffff0000u);
-    }
-  };
-  // M = the largest partial LSE (8 loads in flight per step)
-  float M = -INFINITY;
-  for (int base = 0; base < ns; base += 8) {
-    float ls[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      ls[k] = (base + k < ns) ? a.ws_lse[(size_t)(s0 + base + k) * a.rows_per_wg + rl] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) M = fmaxf(M, ls[k]);
-  }
-  Ms = (M == -INFINITY) ? 0.f : M;
-  // weighted sum, 4 splits per step with all their loads issued before any is used
+  // One pass over the splits, 4 at a time with every load of a group issued before any
+  // is used: a running shift Ms (the largest partial LSE so far, 0 while there is none)
+  // and the sums rescaled whenever it grows, so the partials are read once and no load
+  // waits on an earlier group's LSE.
+  float tot = 0.f, Ms = 0.f, M = -INFINITY;
+  auto part = [&](int sidx) { return a.ws_o + ((size_t)(s0 + sidx) * a.rows_per_wg + rl) * kDv + 8 * t; };
   for (int base = 0; base < ns; base += 4) {
     float ls[4];
     u32x4 x[4][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      ls[k] = -INFINITY;
       if (base + k < ns) {
         ls[k] = a.ws_lse[(size_t)(s0 + base + k) * a.rows_per_wg + rl];
-        x[k][0] = part(base + k)[0];
-        x[k][1] = part(base + k)[1];
+        x[k][0] = *(const u32x4*)part(base + k);
+        x[k][1] = *(const u32x4*)(part(base + k) + kDv / 2);
       }
     }
+    float Mn = M;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (base + k < ns) accumulate(expf(ls[k] - Ms), x[k][0], x[k][1]);
+    for (int k = 0; k < 4; ++k) Mn = fmaxf(Mn, ls[k]);
+    const float Msn = (Mn == -INFINITY) ? 0.f : Mn;
+    // Rescale once a finite shift grows (uniform over the row's 32 threads).  While M is
+    // -inf every weight so far was 0 (or NaN, which stays NaN), so nothing to rescale;
+    // a finite M never exceeds Mn, so r <= 1 here.
+    if (M != -INFINITY && Msn != Ms) {
+      const float r = expf(Ms - Msn);
+      tot *= r;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] *= r;
+    }
+    M = Mn;
+    Ms = Msn;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (base + k < ns) {
+        const float wgt = expf(ls[k] - Ms);
+        tot += wgt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += wgt * __uint_as_float(x[k][0][j] << 16);
+          acc[2 * j + 1] += wgt * __uint_as_float(x[k][0][j] & 0xffff0000u);
+          acc[8 + 2 * j] += wgt * __uint_as_float(x[k][1][j] << 16);
+          acc[8 + 2 * j + 1] += wgt * __uint_as_float(x[k][1][j] & 0xffff0000u);
+        }
+      }
+    }
   }
   const bool empty = tot == 0.f;  // NaN (a poisoned split) propagates
   float inv = empty ? 0.f : 1.f / tot;
@@ -93,7 +103,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   for (int i = 0; i < 8; ++i)
     packed[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   *(u32x4*)orow = u32x4{packed[0], packed[1], packed[2], packed[3]};
-  *(u32x4*)(orow + 8) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+  *(u32x4*)(orow + kDv / 2) = u32x4{packed[4], packed[5], packed[6], packed[7]};
   if (t == 0) a.lse[(size_t)b * a.rows + r] = lse_v;
 }
 

@@ -2,6 +2,7 @@
 import numpy as np
 import pytest
 
+import oracle
 from gpu_util import ATOL, compare, oracle_rows, run, sample_rows, say, to_device
 from mla_inputs import make_case, make_config, poison_unused
 
@@ -102,6 +103,41 @@ def test_split_counts_agree():
         assert np.all(np.abs(o - o0) <= 2 ** -7 * np.abs(o0) + 2e-3)
         # two independent roundings (output and P, ~2e-3 relative L2 each vs the oracle)
         assert np.linalg.norm(o - o0) / np.linalg.norm(o0) < 5e-3
+
+
+def test_merge_rescales_as_the_largest_partial_grows():
+    """Keys whose rope dims grow block by block (values untouched) make the largest LSE
+    seen by the merge rise at every group of four one-block partials, by under one unit
+    early and by tens late, so the running sums are rescaled at every group and the early
+    groups still carry weight (32 and 40 partials per sequence); the merged rows must meet
+    the oracle.  (Scaling whole rows would scale the values too: then rows whose merge
+    cancels large partials miss the absolute bound by the bf16 rounding of the partials
+    alone, in exact arithmetic as on the GPU.)"""
+    import mla_decode_03_amd as mla
+    from mla_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    case = _case(2, 1, 128, [2048, 2560], seed=77)
+    for b in range(case.batch):
+        for j in range((int(case.cache_seqlens[b]) + 63) // 64):
+            pg = int(case.block_table[b, j])
+            x = case.kv[pg].copy()
+            x[:, 512:] *= np.float32(2.0 ** (j / 6.0))
+            bits = f32_to_bf16_bits(x).reshape(x.shape)
+            case.kv_bits[pg] = bits
+            case.kv[pg] = bf16_bits_to_f32(bits).reshape(bits.shape)
+    say("merge rescale", case.cache_seqlens.tolist())
+    ref_o, ref_l = oracle_rows(case)
+    # the partial LSEs really climb: the whole sequence's LSE is far above its first block's
+    first = oracle.decode_case(_first_blocks(case, 1))[1]
+    assert np.all(ref_l - first > 5.0)
+    o, l, _ = run(case, options=mla.PlanOptions(fixed_split_blocks=1))
+    compare(o, l, ref_o, ref_l, "merge rescale")
+
+
+def _first_blocks(case, n):
+    """The same case cut to each sequence's first n blocks."""
+    import dataclasses
+    lens = np.minimum(case.cache_seqlens, 64 * n).astype(np.int32)
+    return dataclasses.replace(case, cache_seqlens=lens)
 
 
 @pytest.mark.parametrize("rs", [2, 4])
