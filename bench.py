@@ -179,6 +179,7 @@ def main():
 
     # the decode kernel alone, with HIP events on the stream it is launched on
     kernel_ms = None
+    kernel_us_pct = None
     if split:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
@@ -186,7 +187,10 @@ def main():
         for i in range(args.steps):
             step(i, evs[i])
         torch.cuda.synchronize()
-        kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        per_launch = sorted(a.elapsed_time(b) for a, b in evs)
+        kernel_ms = sum(per_launch) / args.steps
+        pct = lambda f: per_launch[min(len(per_launch) - 1, int(f * len(per_launch)))] * 1e3
+        kernel_us_pct = {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
 
     t = ms_per_step * 1e-3
     tflops = flops / t / 1e12
@@ -199,7 +203,7 @@ def main():
         achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                    "kernel": DECODE_KERNEL, "kernel_ms": round(kernel_ms, 5),
+                    "kernel": DECODE_KERNEL, "kernel_ms": round(kernel_ms, 5), "kernel_us_per_launch": kernel_us_pct,
                     "algorithmic_bytes_per_launch": total_bytes}
 
     if args.calibrate_copy > 0:
