@@ -26,8 +26,9 @@
 // page's V is read from LDS once, not four times).  Everything runs on 32x32x16 MFMA
 // tiles; pages stream in as column blocks (see the copies below).
 // O is never rescaled inside the loop: each row fixes its reference max at its first
-// visible keys and accumulates exp2(x - m_ref) <= 2^kRefSlack; if a later score exceeds
-// that, the segment is decoded again with m_ref = the row's true running max (exact).
+// visible keys and accumulates exp2(x - m_ref) <= 2^kRefSlack; if a later page's sum
+// exceeds that, the segment is decoded again with m_ref at or above every score of the
+// row (exact: no term can overflow, and the row's largest term is at least 2^-kRefSlack).
 #include "mla_args.h"
 #include "mla_device.h"
 
@@ -41,6 +42,7 @@ constexpr int kPBufBytes = 16384;                 // P of one page
 constexpr int kLdsBytes = kPBufOff + kPBufBytes;   // 163840 = all of it
 
 constexpr float kRefSlack = 16.0f;  // scores may exceed the reference max by 2^16
+constexpr float kSumCap = 65536.0f; // 2^kRefSlack: a half-row page sum above it flags
 constexpr int kPrefK = 2;           // K-fragment prefetch distance (32-dim steps)
 constexpr int kPrefV = 4;           // V-fragment prefetch distance (16-wide value tiles)
 
@@ -512,13 +514,16 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
           s1[e] = (t0 + 32 < lim) ? s1[e] : -INFINITY;
         }
       }
-      float mr = -INFINITY;
+      // A row takes its reference max from the first page where it sees a key (both
+      // lane halves of the row agree on it).  Only while some row of the wave has none
+      // does the wave take the page's row maxima.
+      if (__builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0) {
+        float mr = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mr = fmaxf(mr, fmaxf(s0[e], s1[e]));
-      const float mx = wave_max_xor(mr, 32) * a.scale_log2;
-      mtrue = fmaxf(mtrue, mx);
-      if (m_ref == -INFINITY) m_ref = mx;        // nothing accumulated yet: exact
-      over |= mx > m_ref + kRefSlack;
+        for (int e = 0; e < 16; ++e) mr = fmaxf(mr, fmaxf(s0[e], s1[e]));
+        const float mx = wave_max_xor(mr, 32) * a.scale_log2;
+        if (m_ref == -INFINITY) m_ref = mx;      // nothing accumulated yet: exact
+      }
       const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
       float rs = 0.f;
       f32x16 p0, p1;
@@ -528,8 +533,18 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         p1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], a.scale_log2, -msub));
         rs += p0[e] + p1[e];
       }
-      rs += __shfl_xor(rs, 32, 64);
+      // lsum holds this lane's half of the row (its 32 of the page's 64 keys); the halves
+      // are added once, in the epilogue.  Every term is at most the half-row sum, so
+      // no term exceeds 2^kRefSlack unless that sum does (an overflow to inf included);
+      // only then does the wave take this page's maxima, for the second pass's max.
       lsum += rs;
+      if (__builtin_amdgcn_ballot_w64(rs > kSumCap) != 0) {
+        over |= rs > kSumCap;
+        float mr = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mr = fmaxf(mr, fmaxf(s0[e], s1[e]));
+        mtrue = fmaxf(mtrue, mr * a.scale_log2);
+      }
       // B operands per 16-token K step: ks -> tile ks/2, C indices 8(ks&1) .. +7
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -576,7 +591,12 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
     }
     // the page buffers and P buffer are idle until the next pass starts
     if (!wg_or(over, (MLA_LDS int*)pbuf)) break;
-    mref_init = mtrue;
+    // Second pass from an upper bound of every score of the row: pages that did not flag
+    // stayed within m_ref + kRefSlack, the flagged ones gave their maxima.
+    {
+      const float mt = fmaxf(mtrue, m_ref + kRefSlack);
+      mref_init = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    }
   }
 
   // ---- epilogue: every wave needs the row statistics of all 128 rows ---------------------
@@ -586,6 +606,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   // sink enters a row once, where its final result is formed: here for an unsplit range,
   // in the combine for the partials of a split one.
   MLA_LDS float* stats = (MLA_LDS float*)pbuf;   // [row][scale_o, lse]
+  lsum += __shfl_xor(lsum, 32, 64);              // the row's two halves
   const float nanv = __builtin_nanf("");
   if (g == 0) {
     const int rr = 32 * w + lr;

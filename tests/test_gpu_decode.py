@@ -133,6 +133,35 @@ def test_merge_rescales_as_the_largest_partial_grows():
     compare(o, l, ref_o, ref_l, "merge rescale")
 
 
+@pytest.mark.parametrize("mode", ["unsplit", "split2"])
+def test_late_score_spike_takes_the_second_pass(mode):
+    """One page in the middle of each sequence gets its keys' rope dims scaled by 40
+    (values untouched): its scores sit tens of log2 units above the first page's maxima,
+    so the page sums pass 2^16 and the workgroup decodes its range again from an upper
+    bound of every row's scores.  Some rows' sums pass the cap through many large terms
+    rather than one.  Out and lse must still meet the oracle."""
+    import mla_decode_03_amd as mla
+    from mla_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    case = _case(3, 1, 128, [1000, 300, 64 * 5], seed=91)
+    for b, j in [(0, 7), (1, 2), (2, 4)]:
+        pg = int(case.block_table[b, j])
+        x = case.kv[pg].copy()
+        x[:, 512:] *= np.float32(40.0)
+        bits = f32_to_bf16_bits(x).reshape(x.shape)
+        case.kv_bits[pg] = bits
+        case.kv[pg] = bf16_bits_to_f32(bits).reshape(bits.shape)
+    say("score spike", mode, case.cache_seqlens.tolist())
+    ref_o, ref_l = oracle_rows(case)
+    # the spike dominates: each sequence's lse is far above its first block's
+    first = oracle.decode_case(_first_blocks(case, 1))[1]
+    assert np.all(ref_l - first > 16.0 * np.log(2.0))
+    if mode == "unsplit":
+        o, l, _ = run(case, split=False)
+    else:
+        o, l, _ = run(case, options=mla.PlanOptions(fixed_split_blocks=2))
+    compare(o, l, ref_o, ref_l, "score spike " + mode)
+
+
 def _first_blocks(case, n):
     """The same case cut to each sequence's first n blocks."""
     import dataclasses
