@@ -207,12 +207,16 @@ __device__ __forceinline__ PageCopy page_copy(const DecodeArgs& a, int page, int
   return PageCopy{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, bad ? 1 : min(kPage, Lc - j * kPage), buf, 0, 0};
 }
 
-// v[s] for a lane-dependent s < 8 over uniform (scalar) values: a select tree.
+// v[s] for a lane-dependent s < 8 over uniform (scalar) values: a select tree written
+// with bit masks.  (Written as conditionals, the first level of the tree was turned into
+// an indexed load from a scratch copy of the values, whose wait drained every copy in
+// flight, at each block.)
+__device__ __forceinline__ int pick(int a, int b, int m) { return (a & ~m) | (b & m); }   // m: 0 or -1
 __device__ __forceinline__ int sel8(const int32_t* v, int s) {
-  const int a0 = (s & 1) ? v[1] : v[0], a1 = (s & 1) ? v[3] : v[2];
-  const int a2 = (s & 1) ? v[5] : v[4], a3 = (s & 1) ? v[7] : v[6];
-  const int b0 = (s & 2) ? a1 : a0, b1 = (s & 2) ? a3 : a2;
-  return (s & 4) ? b1 : b0;
+  const int m0 = -(s & 1), m1 = -((s >> 1) & 1), m2 = -((s >> 2) & 1);
+  const int a0 = pick(v[0], v[1], m0), a1 = pick(v[2], v[3], m0);
+  const int a2 = pick(v[4], v[5], m0), a3 = pick(v[6], v[7], m0);
+  return pick(pick(a0, a1, m1), pick(a2, a3, m1), m2);
 }
 
 // Copy description of block j of a sparse unit: the pool rows of the 16 tokens this wave
