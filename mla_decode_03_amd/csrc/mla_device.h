@@ -99,6 +99,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Workgroup barrier for communication through LDS only: it orders LDS accesses and
+// does not wait for global stores in flight (__syncthreads also waits for those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Block-wide exclusive scan of one value per thread (256 threads = 4 waves): a scan
 // inside each wave, then the wave totals through LDS.  Returns the exclusive prefix and
 // writes the block total to *total.
@@ -111,11 +119,11 @@ __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s, int32_t* t
     if (lane >= off) x += y;
   }
   if (lane == 63) s[wv] = x;
-  __syncthreads();
+  lds_barrier();
   int32_t base = 0;
   for (int k = 0; k < wv; ++k) base += s[k];
   *total = s[0] + s[1] + s[2] + s[3];
-  __syncthreads();  // s is reused by the next scan
+  lds_barrier();  // s is reused by the next scan
   return base + x - v;
 }
 

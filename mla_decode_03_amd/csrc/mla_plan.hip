@@ -34,9 +34,9 @@ __device__ inline int64_t block_max(int64_t x, int64_t* s) {
     x = x > y ? x : y;
   }
   if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_barrier();
   const int64_t r = max(max(s[0], s[1]), max(s[2], s[3]));
-  __syncthreads();  // s is reused by the next call
+  lds_barrier();  // s is reused by the next call
   return r;
 }
 
@@ -55,6 +55,10 @@ __device__ inline int32_t wg_of(int64_t x, int64_t total, int64_t num_wg) {
   return (int32_t)floor_div((x + 1) * num_wg - 1, total);
 }
 
+// CU_IN_LDS: the batch fits kPlanLdsBatch, so cu_blocks and the non-empty prefix are kept
+// in LDS (a compile-time choice: selecting the array at run time made every read a generic
+// load that waits on both LDS and global memory).
+template <bool CU_IN_LDS>
 __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict__ seqlens,
                                                        int32_t* __restrict__ meta, int batch,
                                                        int rows, int row_split, int grid_wg,
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
   __shared__ int64_t s_red[4];
   __shared__ int32_t s_bp[kPlanLdsWg + 1], s_bc[kPlanLdsWg + 1];   // the two rules' cuts
   const int t = threadIdx.x;
-  const bool cu_in_lds = batch <= kPlanLdsBatch;
+  constexpr bool cu_in_lds = CU_IN_LDS;
   MetaView v = meta_view(meta, batch, row_split);
   // Larger batches keep the non-empty prefix in first_wg (rewritten by the unit pass).
   int32_t* ne_glob = v.first_wg;
@@ -110,8 +114,15 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       s_ne[batch] = ne_carry;
     }
   }
-  __threadfence_block();
-  __syncthreads();  // cu_blocks and the non-empty prefix visible to the whole workgroup
+  // cu_blocks and the non-empty prefix visible to the whole workgroup.  Larger batches
+  // read them back from global memory, so their stores must have landed; batches that fit
+  // keep them in LDS, and the barrier need not wait for the stores.
+  if constexpr (!cu_in_lds) {
+    __threadfence_block();
+    __syncthreads();
+  } else {
+    lds_barrier();
+  }
 
   const int64_t total = (int64_t)row_split * carry;
   const int units = batch * row_split;
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
         s_bp[w] = (int32_t)pages_begin(w);
         s_bc[w] = (int32_t)cost_begin(w);
       }
-      __syncthreads();
+      lds_barrier();
     }
     auto cut_p = [&](int64_t w) -> int64_t { return cuts_in_lds ? s_bp[w] : pages_begin(w); };
     auto cut_c = [&](int64_t w) -> int64_t { return cuts_in_lds ? s_bc[w] : cost_begin(w); };
@@ -309,9 +320,9 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
   // 4. header (the error flag is the OR over threads)
   __shared__ int32_t s_err;
   if (t == 0) s_err = 0;
-  __syncthreads();
+  lds_barrier();
   if (err) atomicOr(&s_err, 1);
-  __syncthreads();
+  lds_barrier();
   if (t == 0) {
     v.hdr[kHdrMagic] = kMetaMagic;
     v.hdr[kHdrBatch] = batch;
@@ -341,8 +352,13 @@ extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
                                       int max_partials, int fixed_blocks, int split_rule, int seg_cost,
                                       int uniform_len, hipStream_t stream) {
-  hipLaunchKernelGGL(mla::mla_plan_kernel, dim3(1), dim3(256), 0, stream, seqlens, meta, batch,
-                     rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks,
-                     split_rule, seg_cost, uniform_len);
+  if (batch <= mla::kPlanLdsBatch)
+    hipLaunchKernelGGL(mla::mla_plan_kernel<true>, dim3(1), dim3(256), 0, stream, seqlens, meta, batch,
+                       rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks,
+                       split_rule, seg_cost, uniform_len);
+  else
+    hipLaunchKernelGGL(mla::mla_plan_kernel<false>, dim3(1), dim3(256), 0, stream, seqlens, meta, batch,
+                       rows, row_split, grid_wg, min_blocks, max_blocks, max_partials, fixed_blocks,
+                       split_rule, seg_cost, uniform_len);
   return hipGetLastError();
 }
