@@ -133,8 +133,9 @@ def test_merge_rescales_as_the_largest_partial_grows():
     compare(o, l, ref_o, ref_l, "merge rescale")
 
 
+@pytest.mark.parametrize("H", [128, 16])
 @pytest.mark.parametrize("mode", ["unsplit", "split2"])
-def test_late_score_spike_takes_the_second_pass(mode):
+def test_late_score_spike_takes_the_second_pass(mode, H):
     """One page in the middle of each sequence gets its keys' rope dims scaled by 40
     (values untouched): its scores sit tens of log2 units above the first page's maxima,
     so the page sums pass 2^16 and the workgroup decodes its range again from an upper
@@ -142,7 +143,7 @@ def test_late_score_spike_takes_the_second_pass(mode):
     rather than one.  Out and lse must still meet the oracle."""
     import mla_decode_03_amd as mla
     from mla_inputs import bf16_bits_to_f32, f32_to_bf16_bits
-    case = _case(3, 1, 128, [1000, 300, 64 * 5], seed=91)
+    case = _case(3, 1, H, [1000, 300, 64 * 5], seed=91)
     for b, j in [(0, 7), (1, 2), (2, 4)]:
         pg = int(case.block_table[b, j])
         x = case.kv[pg].copy()
@@ -150,7 +151,7 @@ def test_late_score_spike_takes_the_second_pass(mode):
         bits = f32_to_bf16_bits(x).reshape(x.shape)
         case.kv_bits[pg] = bits
         case.kv[pg] = bf16_bits_to_f32(bits).reshape(bits.shape)
-    say("score spike", mode, case.cache_seqlens.tolist())
+    say("score spike", mode, H, case.cache_seqlens.tolist())
     ref_o, ref_l = oracle_rows(case)
     # the spike dominates: each sequence's lse is far above its first block's
     first = oracle.decode_case(_first_blocks(case, 1))[1]
