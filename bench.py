@@ -13,7 +13,8 @@ step before it.
 
 Prints one JSON line: throughput in TFLOP/s (algorithmic FLOPs: 2*(576+512) per
 visible key per query row), KV GB/s, roofline fractions, the decode kernel's own
-duration from HIP events, and the CPU oracle's rate on the host as a reported baseline.
+duration from HIP events, the device's streaming-read rate from the library's probe
+(context for the roofline), and the CPU oracle's rate on the host as a reported baseline.
 """
 from __future__ import annotations
 
@@ -69,6 +70,27 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
+def hbm_probe(torch, mla, dev, nbytes=512 << 20, reps=10):
+    """The device's streaming-read rate, as context for the roofline fraction: 512 MiB (twice
+    the 256 MB memory-side cache, so the passes stream from HBM) read once per pass by the
+    library's probe, with plain vector loads and with the decode's global->LDS copies."""
+    src = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    res = {"bytes": nbytes}
+    for mode, key in ((0, "vector_loads_gbs"), (1, "lds_copies_gbs")):
+        for _ in range(3):
+            mla.hbm_read_probe(src, mode, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            mla.hbm_read_probe(src, mode, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        res[key] = round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, sink
+    return res
+
+
 def cpu_baseline(case, flops, indices=None):
     import oracle
     t0 = time.perf_counter()
@@ -97,6 +119,8 @@ def main():
                     help="attention-sink variant (seeded per-head sink logits)")
     ap.add_argument("--sparse-topk", type=int, default=0,
                     help="sparse variant: every (b, t) attends to this many seeded distinct positions")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the HBM streaming-read probe (reported as context beside the roofline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device to device 3 times (the reference "
                          "dispatch that scales the HBM byte counters of a profiled run)")
@@ -206,6 +230,12 @@ def main():
                     "kernel": DECODE_KERNEL, "kernel_ms": round(kernel_ms, 5), "kernel_us_per_launch": kernel_us_pct,
                     "algorithmic_bytes_per_launch": total_bytes}
 
+    probe = None
+    if not args.no_probe:
+        probe = hbm_probe(torch, mla, dev)
+        if roofline is not None:
+            probe["decode_frac_of_lds_copies"] = round(roofline["achieved"] / probe["lds_copies_gbs"], 4)
+
     if args.calibrate_copy > 0:
         src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -245,6 +275,7 @@ def main():
         "frac_roofline": round(max(frac_hbm, frac_mfma), 4),
         "algorithmic": {"flop": flops, "kv_bytes": kv_bytes, "total_bytes": total_bytes},
         "roofline": roofline,
+        "hbm_probe": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

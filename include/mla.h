@@ -273,6 +273,26 @@ MLA_API int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* v
  */
 MLA_API int32_t mla_plan_error(const mla_plan_t* plan, void* stream);
 
+/*
+ * HBM streaming-read probe, a measurement aid outside the decode path: the read
+ * bandwidth the device delivers to a plain stream, the ceiling the decode's bytes per
+ * second are read against (the TileLang notes rank candidate kernels by traffic over
+ * bandwidth, "Key design 2: tile recommendation"; this measures the bandwidth term).
+ *
+ * Reads `bytes` of DEVICE memory at `src` (16-byte aligned) exactly once, split into
+ * equal contiguous chunks over `num_workgroups` workgroups of 256 threads (<= 0: 4 per
+ * CU for mode 0, 1 per CU for mode 1), either
+ *   mode 0: with 16-byte vector loads into registers, or
+ *   mode 1: with the decode's wave-wide global->LDS copies (1 KB each) into an LDS ring.
+ * `sink` (DEVICE uint32 [num_workgroups], 4-byte aligned) keeps the loads live; its
+ * contents are unspecified.  Each chunk (bytes / workgroups) must be a positive multiple
+ * of 16 KiB below 4 GiB (MLA_ERR_SHAPE otherwise); NULL pointers give MLA_ERR_NULL, a
+ * mode other than 0 or 1 MLA_ERR_UNSUPPORTED, misalignment MLA_ERR_ALIGN, all before
+ * anything is enqueued.  Enqueues one kernel on `stream`; time it with events there.
+ */
+MLA_API int32_t mla_hbm_read_probe(const void* src, size_t bytes, int32_t mode, int32_t num_workgroups,
+                                   uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ from ._abi import (D_QK, D_V, DTYPE_BF16, DTYPE_F32, MAX_ROWS, PAGE, MlaError, P
 __all__ = ["D_QK", "D_V", "PAGE", "MAX_ROWS", "DTYPE_BF16", "DTYPE_F32", "MlaError", "Problem",
            "PlanOptions", "Plan", "lib", "lib_path", "metadata_bytes", "workspace_bytes",
            "get_metadata", "decode", "decode_splits", "combine", "make_problem", "Decoder",
-           "device_num_cus"]
+           "device_num_cus", "hbm_read_probe"]
 
 
 def _stream_handle(stream):
@@ -150,6 +150,16 @@ def combine(problem: Problem, out, lse, plan: Plan, workspace, stream=None, sink
                            ctypes.byref(plan.c_plan),
                            _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
     _abi.check(rc, "mla_combine")
+
+
+def hbm_read_probe(src, mode: int, sink, num_workgroups: int = 0, nbytes: int | None = None, stream=None) -> None:
+    """Enqueue the HBM streaming-read probe over `src` (a device tensor; `nbytes` of it,
+    default all): mode 0 = vector loads, mode 1 = the decode's global->LDS copies.
+    `sink` is a device uint32/int32 tensor with at least one element per workgroup."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    rc = lib().mla_hbm_read_probe(_ptr(src), ctypes.c_size_t(n), int(mode), int(num_workgroups), _ptr(sink),
+                                  _stream_handle(stream))
+    _abi.check(rc, "mla_hbm_read_probe")
 
 
 class Decoder:

@@ -460,4 +460,31 @@ int32_t mla_plan_error(const mla_plan_t* plan, void* stream) {
   return MLA_OK;
 }
 
+// the probe's launcher (mla_probe.hip); declared here, the probe is no part of the decode
+MLA_INTERNAL hipError_t mla_launch_probe(const void* src, size_t bytes, int mode, int num_wg, uint32_t* sink,
+                                         hipStream_t stream);
+
+int32_t mla_hbm_read_probe(const void* src, size_t bytes, int32_t mode, int32_t num_workgroups, uint32_t* sink,
+                           void* stream) {
+  if (!src || !sink) return MLA_ERR_NULL;
+  if (mode != 0 && mode != 1) return MLA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
+    return MLA_ERR_ALIGN;
+  int32_t nwg = num_workgroups;
+  if (nwg <= 0) {
+    if (bytes == 0) return MLA_ERR_SHAPE;
+    int32_t cus = 0;
+    const int32_t rc = mla_device_num_cus(&cus);
+    if (rc != MLA_OK) return rc;
+    nwg = mode == 0 ? 4 * cus : cus;
+  }
+  // every workgroup reads an equal chunk, a multiple of 16 KiB below 4 GiB
+  if (bytes == 0 || bytes % (size_t)nwg != 0) return MLA_ERR_SHAPE;
+  const size_t chunk = bytes / (size_t)nwg;
+  if (chunk % 16384 != 0 || chunk >= ((size_t)1 << 32)) return MLA_ERR_SHAPE;
+  return mla_launch_probe(src, bytes, mode, nwg, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_LAUNCH;
+}
+
 }  // extern "C"

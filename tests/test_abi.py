@@ -182,3 +182,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_LIB_PATH", str(tmp_path / "libmla.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         _abi.lib()
+
+
+def test_hbm_probe_argument_checks():
+    """Every host-checkable fault of the streaming-read probe returns its status before
+    anything is enqueued (an explicit workgroup count: no device query)."""
+    L = m.lib()
+    src, sink = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    mib = 1 << 20
+    assert L.mla_hbm_read_probe(None, mib, 0, 4, sink, None) == _abi.MLA_ERR_NULL
+    assert L.mla_hbm_read_probe(src, mib, 0, 4, None, None) == _abi.MLA_ERR_NULL
+    assert L.mla_hbm_read_probe(src, mib, 2, 4, sink, None) == _abi.MLA_ERR_UNSUPPORTED
+    assert L.mla_hbm_read_probe(src, mib, -1, 4, sink, None) == _abi.MLA_ERR_UNSUPPORTED
+    assert L.mla_hbm_read_probe(ctypes.c_void_p(0x100008), mib, 0, 4, sink, None) == _abi.MLA_ERR_ALIGN
+    assert L.mla_hbm_read_probe(src, mib, 1, 4, ctypes.c_void_p(0x200002), None) == _abi.MLA_ERR_ALIGN
+    # chunks: equal, a positive multiple of 16 KiB, below 4 GiB
+    assert L.mla_hbm_read_probe(src, 0, 0, 4, sink, None) == _abi.MLA_ERR_SHAPE
+    assert L.mla_hbm_read_probe(src, mib + 16384, 0, 4, sink, None) == _abi.MLA_ERR_SHAPE   # not divisible by 4 x 16 KiB
+    assert L.mla_hbm_read_probe(src, 3 * 16384, 1, 2, sink, None) == _abi.MLA_ERR_SHAPE    # 24 KiB chunks
+    assert L.mla_hbm_read_probe(src, 1 << 33, 0, 2, sink, None) == _abi.MLA_ERR_SHAPE      # 4 GiB chunks

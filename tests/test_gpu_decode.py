@@ -553,3 +553,27 @@ def test_lengths_at_and_past_the_block_table():
     assert dec2.plan.error() == mla._abi.MLA_ERR_BAD_INPUT
     assert np.all(np.isnan(o2[:128])) and np.all(np.isnan(l2[:128]))
     compare(o2[128:], l2[128:], ref_o[128:], ref_l[128:], "others")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_hbm_read_probe_streams(mode):
+    """The streaming-read probe runs in both modes (vector loads; the decode's global->LDS
+    copies) over 64 MiB with the default workgroup count and with an explicit one, and
+    reports a plausible rate.  Its sink is never the thing checked (unspecified)."""
+    import torch
+    import mla_decode_03_amd as mla
+    say("hbm probe", mode)
+    src = torch.arange(16 << 20, dtype=torch.int32, device="cuda")   # 64 MiB
+    sink = torch.zeros(4 * 1024, dtype=torch.int32, device="cuda")
+    mla.hbm_read_probe(src, mode, sink)
+    mla.hbm_read_probe(src, mode, sink, num_workgroups=64)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        mla.hbm_read_probe(src, mode, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    say("  %.0f GB/s" % gbs)
+    assert gbs > 200.0
