@@ -2,7 +2,8 @@
 //
 // Serves float32 problems, where speed is not the point: every step is the
 // definition done directly on the vector ALUs.  Per 64-token page, lane j scores
-// token p0 + j (a 576-long dot product against the q row held in LDS), the wave
+// token p0 + j (a 576-long dot product against the q row held in LDS, in four
+// interleaved partial sums), the wave
 // takes the running max / sum by shuffles (online softmax, natural exp), and then
 // every lane accumulates 8 of the 512 value dims over the page's tokens.
 #include "mla_args.h"
@@ -23,7 +24,7 @@ __device__ inline float wave_max(float v) {
 }
 
 __global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
-  __shared__ float qs[4][kDqk];
+  __shared__ __attribute__((aligned(16))) float qs[4][kDqk];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int chunks = (a.rows + 3) / 4;
   const int b = blockIdx.x / chunks;
@@ -50,10 +51,20 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
     const bool valid = p0 + l < n;
     float s = -INFINITY;
     if (valid) {
-      const float* krow = pbase + (size_t)l * kDqk;
-      float dot = 0.f;
-      for (int d = 0; d < kDqk; ++d) dot = fmaf(qs[w][d], krow[d], dot);
-      s = dot * a.scale;
+      // 16-byte loads and four independent partial sums (one per vector component), so
+      // the 576-term dot product is not one dependent chain of scalar loads and FMAs
+      const f32x4* krow = (const f32x4*)(pbase + (size_t)l * kDqk);
+      const f32x4* qv = (const f32x4*)qs[w];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int d = 0; d < kDqk / 4; ++d) {
+        const f32x4 kq = krow[d], qq = qv[d];
+        acc[0] = fmaf(qq[0], kq[0], acc[0]);
+        acc[1] = fmaf(qq[1], kq[1], acc[1]);
+        acc[2] = fmaf(qq[2], kq[2], acc[2]);
+        acc[3] = fmaf(qq[3], kq[3], acc[3]);
+      }
+      s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale;
     }
     const float mn = fmaxf(m, wave_max(s));
     const float alpha = expf(m - mn);
@@ -63,8 +74,22 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= alpha;
     const int cnt = min(kPage, n - p0);
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __shfl(pw, k, 64);
+    // token k's weight from lane k (a scalar read: k is uniform); eight tokens at a time,
+    // so that their value rows are in flight together
+    int k = 0;
+    for (; k + 8 <= cnt; k += 8) {
+      float wk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) wk[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), k + u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* vrow = pbase + (size_t)(k + u) * kDqk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(wk[u], vrow[l + 64 * i], o[i]);
+      }
+    }
+    for (; k < cnt; ++k) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), k));
       const float* vrow = pbase + (size_t)k * kDqk;
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = fmaf(wk, vrow[l + 64 * i], o[i]);
