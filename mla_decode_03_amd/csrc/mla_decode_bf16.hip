@@ -612,8 +612,14 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   MLA_LDS float* stats = (MLA_LDS float*)pbuf;   // [row][scale_o, lse]
   lsum += __shfl_xor(lsum, 32, 64);              // the row's two halves
   const float nanv = __builtin_nanf("");
-  if (g == 0) {
-    const int rr = 32 * w + lr;
+  // The epilogue's lane indices, formed here from an opaque copy of the thread index, so
+  // that the addresses derived from them are not computed before the page loop and kept
+  // (spilled) across it.
+  int tid_e = threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  const int l_e = tid_e & 63, g_e = l_e >> 5, lr_e = l_e & 31;
+  if (g_e == 0) {
+    const int rr = 32 * w + lr_e;
     float so, lse_v;
     if (poison) {
       so = nanv;
@@ -637,7 +643,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   MLA_LDS uint8_t* ob = lds;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const int rr = 32 * rt + lr;
+    const int rr = 32 * rt + lr_e;
     const float scale_o = stats[2 * rr];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -647,17 +653,17 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         const uint32_t lo2 = pack_bf16x2(t[4 * i] * scale_o, t[4 * i + 1] * scale_o);
         const uint32_t hi2 = pack_bf16x2(t[4 * i + 2] * scale_o, t[4 * i + 3] * scale_o);
         const int c = 16 * w + 4 * dt + i;
-        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g) = u32x2{lo2, hi2};
+        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) = u32x2{lo2, hi2};
       }
   }
   __syncthreads();
   for (int k = 0; k < 32; ++k) {                  // the wave's rows 32w .. 32w+31
     const int rr = 32 * w + k;
     if (row0 + rr >= row_end) break;              // uniform
-    const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l ^ (rr & 15)) << 4));
+    const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
     uint16_t* dst = (slot < 0) ? a.out + ((size_t)b * R + row0 + rr) * kDv
                                : a.ws_o + ((size_t)slot * a.rows_per_wg + rr) * kDv;
-    *(u32x4*)(dst + 8 * l) = v;
+    *(u32x4*)(dst + 8 * l_e) = v;
   }
   if (threadIdx.x < 128 && row0 + (int)threadIdx.x < row_end) {
     const int rr = threadIdx.x;
