@@ -436,11 +436,16 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
     mtrue = -INFINITY;
     lsum = 0.f;
     over = false;
+    // Zeros from an opaque scalar formed in this pass: a plain zero vector is one value the
+    // compiler keeps (and spills) from the kernel's start to every pass.
+    int zi = 0;
+    asm volatile("" : "+s"(zi));
+    const float zf = __int_as_float(zi);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        o[dt][rt] = f32x16{};
+        o[dt][rt] = f32x16{zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf};
         asm volatile("" : "+a"(o[dt][rt]));
       }
 
