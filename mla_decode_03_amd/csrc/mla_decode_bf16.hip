@@ -376,7 +376,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   const int myrow = row0 + 32 * w + lr;
 
   const int L = ld_const(a.seqlens, b);
-  const bool bad_len = (L < 0) || ((int64_t)L > (int64_t)kPage * a.max_blocks);
+  // more keys than the block table's row can hold: ceil(L / kPage) > max_blocks, in 32 bits
+  const bool bad_len = (L < 0) || (L > 0 && (L - 1) / kPage >= a.max_blocks);
   const int Lc = bad_len ? 0 : L;
   int nvis = Lc;
   if (a.causal && a.q_len > 1) nvis = Lc - a.q_len + 1 + min(myrow, R - 1) / a.heads;
@@ -670,8 +671,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
                                : a.ws_o + ((size_t)slot * a.rows_per_wg + rr) * kDv;
     *(u32x4*)(dst + 8 * l_e) = v;
   }
-  if (threadIdx.x < 128 && row0 + (int)threadIdx.x < row_end) {
-    const int rr = threadIdx.x;
+  if (tid_e < 128 && row0 + tid_e < row_end) {
+    const int rr = tid_e;
     const float lse_v = stats[2 * rr + 1];
     if (slot < 0) a.lse[(size_t)b * R + row0 + rr] = lse_v;
     else a.ws_lse[(size_t)slot * a.rows_per_wg + rr] = lse_v;
