@@ -11,6 +11,13 @@ before timing starts.  Two KV pools with identical contents are alternated step 
 step, so no step can be served from the 256 MB memory-side cache left warm by the
 step before it.
 
+Timed passes hold the stream with a short spin kernel while the host enqueues the
+whole pass, so the device runs the steps back to back: the figures are device time,
+with no host enqueue gaps inside them (a serving loop gets the same by enqueueing
+ahead or replaying a captured graph).  A second pass, after its own settling steps,
+records events around each launch of every step for the per-kernel durations (plan,
+decode, combine).
+
 Prints one JSON line: throughput in TFLOP/s (algorithmic FLOPs: 2*(576+512) per
 visible key per query row), KV GB/s, roofline fractions, the decode kernel's own
 duration from HIP events, the device's streaming-read rate from the library's probe
@@ -91,13 +98,24 @@ def hbm_probe(torch, mla, dev, nbytes=512 << 20, reps=10):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, flops, indices=None):
     import oracle
     t0 = time.perf_counter()
     oracle.decode_case(case, indices=indices)
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
             "sample": "the whole workload once: all %d query rows x %d keys, float64 two-pass "
                       "softmax on the host" % (case.batch * case.q_len * case.num_heads,
                                                int(case.cache_seqlens.max()))}
@@ -171,28 +189,51 @@ def main():
     pools = (kv_a, kv_b)
     stream = torch.cuda.current_stream()
 
-    def step(i, events=None):
+    def step(i, ev=None):
         kv = pools[i & 1]
         if not split:
+            if ev is not None:
+                ev[1].record(stream)
             mla.decode(dec.problem, q, kv, bt, lens, case.scale, out, lse, None, None, stream, sinks)
+            if ev is not None:
+                ev[2].record(stream)
             return
+        if ev is not None:
+            ev[0].record(stream)
         plan = dec.plan_for(lens, stream)
-        if events is not None:
-            events[0].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace, stream,
                           sinks, indices)
-        if events is not None:
-            events[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
         mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks)
+        if ev is not None:
+            ev[3].record(stream)
 
+    t_host = time.perf_counter()
     for i in range(args.warmup):
         step(i)
+    t_host = (time.perf_counter() - t_host) / max(args.warmup, 1)   # host seconds to enqueue a step
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` whole-path steps
+    # the spin kernel's rate, to hold the stream while a whole pass is enqueued
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
+
+    def hold(n_steps):
+        ms = 2.0 + 3.0 * n_steps * t_host * 1e3 + 5e-3 * n_steps   # enqueue time, with margin
+        torch.cuda._sleep(int(min(ms, 2000.0) * cycles_per_ms))
+
+    # timed region: exactly `steps` whole-path steps, back to back on the device
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    hold(args.steps)
     e0.record(stream)
     for i in range(args.steps):
         step(i)
@@ -201,20 +242,33 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
 
-    # the decode kernel alone, with HIP events on the stream it is launched on
+    # Per-launch durations from HIP events on the launch stream, in a pass of its own:
+    # `steps` settling steps, then `steps` steps with events around each launch.
     kernel_ms = None
     kernel_us_pct = None
+    launches = None
+    settle = max(args.steps, 20)
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    hold(settle + args.steps)
+    for i in range(settle):
+        step(i)
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    pct = lambda v, f: v[min(len(v) - 1, int(f * len(v)))] * 1e3
+    dec_ms = sorted(ev[1].elapsed_time(ev[2]) for ev in evs)
+    kernel_ms = sum(dec_ms) / len(dec_ms)
+    kernel_us_pct = {"p10": round(pct(dec_ms, 0.1), 2), "p50": round(pct(dec_ms, 0.5), 2),
+                     "p90": round(pct(dec_ms, 0.9), 2)}
+    launches = {"decode_us": round(kernel_ms * 1e3, 2)}
     if split:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            step(i, evs[i])
-        torch.cuda.synchronize()
-        per_launch = sorted(a.elapsed_time(b) for a, b in evs)
-        kernel_ms = sum(per_launch) / args.steps
-        pct = lambda f: per_launch[min(len(per_launch) - 1, int(f * len(per_launch)))] * 1e3
-        kernel_us_pct = {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
+        plan_ms = sum(ev[0].elapsed_time(ev[1]) for ev in evs) / len(evs)
+        comb_ms = sum(ev[2].elapsed_time(ev[3]) for ev in evs) / len(evs)
+        step_ev = sum(ev[0].elapsed_time(ev[3]) for ev in evs) / len(evs)
+        launches.update({"plan_us": round(plan_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
+                         "step_with_events_us": round(step_ev * 1e3, 2),
+                         "sum_le_step": bool(plan_ms + kernel_ms + comb_ms <= ms_per_step * 1.02)})
 
     t = ms_per_step * 1e-3
     tflops = flops / t / 1e12
@@ -227,8 +281,8 @@ def main():
         achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                    "kernel": DECODE_KERNEL, "kernel_ms": round(kernel_ms, 5), "kernel_us_per_launch": kernel_us_pct,
-                    "algorithmic_bytes_per_launch": total_bytes}
+                    "kernel": DECODE_KERNEL if split else "mla_decode_f32_kernel", "kernel_ms": round(kernel_ms, 5),
+                    "kernel_us_per_launch": kernel_us_pct, "algorithmic_bytes_per_launch": total_bytes}
 
     probe = None
     if not args.no_probe:
@@ -275,6 +329,7 @@ def main():
         "frac_roofline": round(max(frac_hbm, frac_mfma), 4),
         "algorithmic": {"flop": flops, "kv_bytes": kv_bytes, "total_bytes": total_bytes},
         "roofline": roofline,
+        "launches": launches,
         "hbm_probe": probe,
         "cpu_baseline": cpu,
     }

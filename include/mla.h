@@ -69,8 +69,10 @@
  * are reported before anything is enqueued.  Faults only the device can see
  * (a block_table entry outside [0, num_pages), or L > 64 * max_blocks_per_seq)
  * never cause an out-of-bounds access: the affected sequence's out and lse are
- * written as NaN and a flag is raised in the metadata, which
- * mla_plan_error() reads back (that call synchronises the stream).
+ * written as NaN and a flag is raised in the plan's metadata, which
+ * mla_plan_error() reads back (that call synchronises the stream).  A decode called
+ * without a plan (plan == NULL) has nowhere to raise the flag: its NaN rows are then
+ * the only report.  Float32 problems take a plan for this purpose alone.
  * No call throws across the ABI; the library is reentrant and thread-safe.
  */
 #ifndef MLA_H_
@@ -159,10 +161,15 @@ MLA_API size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_o
 
 /*
  * Size in bytes of the workspace mla_decode needs with a plan made for the same
- * problem/options/num_cus: room for the split partials (per split, every row's
- * normalised output as bf16 and its float32 log-sum-exp: 1028 bytes per row and
- * partial slot), and for a sparse problem the lists turned into pool rows (4 bytes per
- * entry, padded to 64 per (b, t), plus a count).  Host-only arithmetic.
+ * problem/options/num_cus: room for the split partials, and for a sparse problem the
+ * lists turned into pool rows (4 bytes per entry, padded to 64 per (b, t), plus a
+ * count).  Host-only arithmetic.
+ * A split partial row (one row of one split) takes 2056 bytes: the normalised float32
+ * output o as a compensated pair of bf16 halves, hi = bf16(o) and lo = bf16(o - hi)
+ * (2 x 1024 B), its float32 natural-log LSE and an int32 flag.  The decode always
+ * writes hi, and writes lo (and sets the flag) only for a row whose largest |o|
+ * exceeds 1; so a partial enters the merge within 2^-8 (hi alone, |o| <= 1) or
+ * 2^-16 |o| (hi + lo) of its float32 value, however much a row's partials cancel.
  */
 MLA_API size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
                            int32_t num_cus);
@@ -218,8 +225,8 @@ MLA_API int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* ca
  *              NULL: one workgroup per sequence, no splits, no workspace needed
  *   workspace  device buffer of >= mla_workspace_bytes (unused when plan is NULL)
  * bf16 problems run the MFMA kernel (split-KV decode, then the LSE combine when
- * the plan splits anything); float32 problems run a plain float32 kernel (plan
- * ignored).
+ * the plan splits anything); float32 problems run a plain float32 kernel that does not
+ * split, and use a plan (NULL allowed) only to raise the device-side fault flag.
  */
 MLA_API int32_t mla_decode(const mla_problem_t* problem,
                    const void* q, const void* kv_cache,
@@ -249,8 +256,8 @@ MLA_API int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t*
  * The two launches of mla_decode_ex, for callers (and benchmarks) that want them apart.
  * mla_decode_splits: the split-KV decode kernel alone -- writes out/lse of every
  *   sequence the plan did not split, and the partials of the split ones into
- *   `workspace` (per split: normalised output rounded to bf16, natural-log LSE in
- *   float32).
+ *   `workspace` (per split: the normalised output as a compensated bf16 pair, see
+ *   mla_workspace_bytes, and its natural-log LSE in float32).
  * mla_combine: merges those partials by log-sum-exp into out/lse (sequences with no
  *   cached tokens get out = 0, lse = -inf).  Same plan and workspace as the decode.
  * Both require a plan and a bf16 problem, and take the same `variant` (NULL = plain);

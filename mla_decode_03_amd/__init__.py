@@ -176,10 +176,12 @@ class Decoder:
         self.options = options
         self.num_cus = num_cus
         self.split = split and self.problem.dtype == DTYPE_BF16
+        # float32 problems are never split; their plan only carries the device-side fault flag
+        self.planned = split
         dev = q.device
-        if self.split:
+        if self.planned:
             mb = metadata_bytes(self.problem, options, num_cus)
-            wb = workspace_bytes(self.problem, options, num_cus)
+            wb = workspace_bytes(self.problem, options, num_cus) if self.split else 0
             if mb == 0:
                 raise MlaError(_abi.MLA_ERR_SHAPE, "invalid problem for planning")
             self.metadata = torch.empty(mb, dtype=torch.uint8, device=dev)
@@ -190,7 +192,7 @@ class Decoder:
         self.plan = None
 
     def plan_for(self, cache_seqlens, stream=None) -> Plan | None:
-        if not self.split:
+        if not self.planned:
             return None
         self.plan = get_metadata(self.problem, cache_seqlens, self.metadata, self.options,
                                  self.num_cus, stream)

@@ -18,9 +18,11 @@ constexpr int kDefaultMinBlocks = 4;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Split partials: bf16 normalised outputs [slots, rows, 512], then fp32 LSE [slots, rows].
+// Split partials: the normalised output's bf16 high halves [slots, rows, 512], its low
+// halves [slots, rows, 512], the fp32 LSE [slots, rows] and the low-half flags [slots, rows].
+constexpr size_t kPartialRowBytes = 2 * mla::kDv * sizeof(uint16_t) + sizeof(float) + sizeof(int32_t);
 size_t partial_bytes(int64_t slots, int64_t rows_per_wg) {
-  return (size_t)slots * rows_per_wg * (mla::kDv * sizeof(uint16_t) + sizeof(float));
+  return (size_t)slots * rows_per_wg * kPartialRowBytes;
 }
 
 int32_t check_problem(const mla_problem_t* p) {
@@ -240,8 +242,10 @@ int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* 
   a->bt_stride = p.block_table_stride;
   a->max_blocks = p.max_blocks_per_seq;
   a->meta = nullptr;
-  a->ws_o = nullptr;
+  a->ws_hi = nullptr;
+  a->ws_lo = nullptr;
   a->ws_lse = nullptr;
+  a->ws_flag = nullptr;
   a->rows_per_wg = a->rows;
   a->row_split = 1;
   a->sinks = nullptr;
@@ -288,8 +292,11 @@ int32_t attach_plan(const mla_problem_t& orig, const mla_plan_t* plan, const voi
   if (workspace && !aligned(workspace, 16)) return MLA_ERR_ALIGN;
   uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
   a->meta = static_cast<int32_t*>(plan->metadata);
-  a->ws_o = reinterpret_cast<uint16_t*>(ws);
-  a->ws_lse = reinterpret_cast<float*>(a->ws_o + (size_t)plan->max_partials * plan->rows_per_wg * mla::kDv);
+  const size_t prow = (size_t)plan->max_partials * plan->rows_per_wg;   // partial rows
+  a->ws_hi = reinterpret_cast<uint16_t*>(ws);
+  a->ws_lo = a->ws_hi + prow * mla::kDv;
+  a->ws_lse = reinterpret_cast<float*>(a->ws_lo + prow * mla::kDv);
+  a->ws_flag = reinterpret_cast<int32_t*>(a->ws_lse + prow);
   a->rows_per_wg = plan->rows_per_wg;
   a->row_split = plan->row_split;
   if (orig.topk > 0) {
@@ -323,8 +330,10 @@ int32_t launch_sparse_rows(const mla_problem_t& orig, const int32_t* indices, co
 int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
   mla::CombineArgs c;
   c.meta = a.meta;
-  c.ws_o = a.ws_o;
+  c.ws_hi = a.ws_hi;
+  c.ws_lo = a.ws_lo;
   c.ws_lse = a.ws_lse;
+  c.ws_flag = a.ws_flag;
   c.out = a.out;
   c.lse = a.lse;
   c.batch = a.batch;
@@ -389,6 +398,14 @@ int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t* variant
     f.num_pages = a.num_pages;
     f.bt_stride = a.bt_stride;
     f.max_blocks = a.max_blocks;
+    // float32 problems are not split; a plan, if given, only receives the fault flag
+    f.err = nullptr;
+    if (plan) {
+      if (!plan->metadata) return MLA_ERR_NULL;
+      if (plan->batch != a.batch || plan->rows != a.rows) return MLA_ERR_SHAPE;
+      if (!aligned(plan->metadata, 16)) return MLA_ERR_ALIGN;
+      f.err = static_cast<int32_t*>(plan->metadata) + mla::kHdrError;
+    }
     return mla_launch_decode_f32(&f, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
   }
   if (!plan) {

@@ -2,7 +2,10 @@
 //
 // A unit (rows of one sequence) cut across k > 1 workgroups left k partial results
 // (o_s = normalised output over its key range, lse_s = natural-log sum of exp over
-// it; o_s stored as bf16).  Over the union of the disjoint ranges:
+// it).  o_s is stored as its bf16 rounding hi_s, plus lo_s = bf16(o_s - hi_s) for the
+// rows whose flag says the decode wrote it (rows with a large |o_s|), so each partial
+// reaches the merge within 0.0039 + 2^-16 |o_s| of its fp32 value.  Over the union of
+// the disjoint ranges:
 //     lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s
 //     out = sum_s exp(lse_s - lse) * o_s
 // A partial with lse_s = -inf weighs 0; a NaN partial (a poisoned segment) makes the row NaN.  Units with no blocks at all get out = 0,
@@ -45,19 +48,33 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   // One pass over the splits, 4 at a time with every load of a group issued before any
   // is used: a running shift Ms (the largest partial LSE so far, 0 while there is none)
   // and the sums rescaled whenever it grows, so the partials are read once and no load
-  // waits on an earlier group's LSE.
+  // waits on an earlier group's LSE.  A flagged row's low half is loaded once its flag
+  // is known (the high halves are in flight meanwhile).
   float tot = 0.f, Ms = 0.f, M = -INFINITY;
-  auto part = [&](int sidx) { return a.ws_o + ((size_t)(s0 + sidx) * a.rows_per_wg + rl) * kDv + 8 * t; };
+  auto prow = [&](int sidx) { return ((size_t)(s0 + sidx) * a.rows_per_wg + rl); };
   for (int base = 0; base < ns; base += 4) {
     float ls[4];
-    u32x4 x[4][2];
+    int fl[4];
+    u32x4 x[4][2], y[4][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       ls[k] = -INFINITY;
+      fl[k] = 0;
       if (base + k < ns) {
-        ls[k] = a.ws_lse[(size_t)(s0 + base + k) * a.rows_per_wg + rl];
-        x[k][0] = *(const u32x4*)part(base + k);
-        x[k][1] = *(const u32x4*)(part(base + k) + kDv / 2);
+        const size_t pr = prow(base + k);
+        ls[k] = a.ws_lse[pr];
+        fl[k] = a.ws_flag[pr];
+        x[k][0] = *(const u32x4*)(a.ws_hi + pr * kDv + 8 * t);
+        x[k][1] = *(const u32x4*)(a.ws_hi + pr * kDv + kDv / 2 + 8 * t);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[k][0] = y[k][1] = u32x4{0u, 0u, 0u, 0u};
+      if (fl[k] != 0) {
+        const size_t pr = prow(base + k);
+        y[k][0] = *(const u32x4*)(a.ws_lo + pr * kDv + 8 * t);
+        y[k][1] = *(const u32x4*)(a.ws_lo + pr * kDv + kDv / 2 + 8 * t);
       }
     }
     float Mn = M;
@@ -81,12 +98,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
         const float wgt = expf(ls[k] - Ms);
         tot += wgt;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[2 * j] += wgt * __uint_as_float(x[k][0][j] << 16);
-          acc[2 * j + 1] += wgt * __uint_as_float(x[k][0][j] & 0xffff0000u);
-          acc[8 + 2 * j] += wgt * __uint_as_float(x[k][1][j] << 16);
-          acc[8 + 2 * j + 1] += wgt * __uint_as_float(x[k][1][j] & 0xffff0000u);
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v0 = __uint_as_float(x[k][h][j] << 16) + __uint_as_float(y[k][h][j] << 16);
+            const float v1 = __uint_as_float(x[k][h][j] & 0xffff0000u) + __uint_as_float(y[k][h][j] & 0xffff0000u);
+            acc[8 * h + 2 * j] += wgt * v0;
+            acc[8 * h + 2 * j + 1] += wgt * v1;
+          }
       }
     }
   }

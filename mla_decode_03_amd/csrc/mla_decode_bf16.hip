@@ -45,6 +45,12 @@ constexpr float kRefSlack = 16.0f;  // scores may exceed the reference max by 2^
 constexpr float kSumCap = 65536.0f; // 2^kRefSlack: a half-row page sum above it flags
 constexpr int kPrefK = 2;           // K-fragment prefetch distance (32-dim steps)
 constexpr int kPrefV = 4;           // V-fragment prefetch distance (16-wide value tiles)
+// A split partial row is stored as its bf16 rounding (hi), which is within 2^-8 |o| of the
+// fp32 value o; a row whose largest |o| exceeds kLoCut also stores lo = bf16(o - hi), and
+// hi + lo is within 2^-16 |o|.  So a partial the merge reads is never off by more than
+// 2^-8 * kLoCut = 0.0039 plus 2^-16 of its own size, however much the partials of a row
+// cancel in the merge.
+constexpr float kLoCut = 1.0f;
 
 // One wave-wide 16 B/lane global->LDS copy: lane i's 16 bytes from base + voff land at
 // LDS address lds + 16*i.  Issued as assembly so the compiler does not treat it as an
@@ -98,12 +104,13 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
   return r;
 }
 
-// Workgroup-wide OR through 4 words of caller-provided LDS that no wave touches
-// between the two barriers (the decode uses every byte of LDS, so the OR cannot
-// reserve its own).
+// Workgroup-wide OR through 4 words of caller-provided LDS (the decode uses every byte
+// of LDS, so the OR cannot reserve its own).  The first barrier lets every wave finish
+// its earlier reads of those words before any wave overwrites them.
 __device__ __forceinline__ bool wg_or(bool f, MLA_LDS int* scratch) {
   const int w = wave_id();
   const int wf = __builtin_amdgcn_ballot_w64(f) != 0;
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) scratch[w] = wf;
   __syncthreads();
   const bool r = (scratch[0] | scratch[1] | scratch[2] | scratch[3]) != 0;
@@ -616,6 +623,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   // sink enters a row once, where its final result is formed: here for an unsplit range,
   // in the combine for the partials of a split one.
   MLA_LDS float* stats = (MLA_LDS float*)pbuf;   // [row][scale_o, lse]
+  MLA_LDS float* amax = stats + 2 * 128;         // [wave][row]: largest |o| over the wave's columns
   lsum += __shfl_xor(lsum, 32, 64);              // the row's two halves
   const float nanv = __builtin_nanf("");
   // The epilogue's lane indices, formed here from an opaque copy of the thread index, so
@@ -645,8 +653,62 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   __syncthreads();
   // O (normalised, bf16) goes through LDS so that every store writes a whole 1 KB row:
   // row rr of the workgroup at rr*1024, 16-byte chunk c (values 8c .. 8c+7) at
-  // (c ^ (rr & 15))*16.  The page buffers are idle now.
+  // (c ^ (rr & 15))*16.  The page buffers are idle now.  For a split partial the same
+  // pass takes each row's largest |o| over the wave's columns (NaN is ignored here; the
+  // row's high half carries it).
   MLA_LDS uint8_t* ob = lds;
+  const bool part = slot >= 0;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int rr = 32 * rt + lr_e;
+    const float scale_o = stats[2 * rr];
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x16& t = o[dt][rt];
+        const float x0 = t[4 * i] * scale_o, x1 = t[4 * i + 1] * scale_o;
+        const float x2 = t[4 * i + 2] * scale_o, x3 = t[4 * i + 3] * scale_o;
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+        const int c = 16 * w + 4 * dt + i;
+        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) =
+            u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      }
+    if (part) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (g_e == 0) amax[w * 128 + rr] = mx;
+    }
+  }
+  __syncthreads();
+  // A split partial row whose largest |o| exceeds kLoCut also stores its low half.
+  auto needs_lo = [&](int rr) {
+    return row0 + rr < row_end && fmaxf(fmaxf(amax[rr], amax[128 + rr]), fmaxf(amax[256 + rr], amax[384 + rr])) > kLoCut;
+  };
+  const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
+  for (int k = 0; k < 32; ++k) {                  // the wave's rows 32w .. 32w+31
+    const int rr = 32 * w + k;
+    if (row0 + rr >= row_end) break;              // uniform
+    const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
+    uint16_t* dst = part ? a.ws_hi + (prow + rr) * kDv : a.out + ((size_t)b * R + row0 + rr) * kDv;
+    *(u32x4*)(dst + 8 * l_e) = v;
+  }
+  if (tid_e < 128 && row0 + tid_e < row_end) {
+    const int rr = tid_e;
+    const float lse_v = stats[2 * rr + 1];
+    if (!part) {
+      a.lse[(size_t)b * R + row0 + rr] = lse_v;
+    } else {
+      a.ws_lse[prow + rr] = lse_v;
+      a.ws_flag[prow + rr] = needs_lo(rr) ? 1 : 0;
+    }
+  }
+  if (!part) return;
+  // Low halves: lo = bf16(o - hi), o the fp32 normalised value and hi its bf16 rounding,
+  // so hi + lo carries o to 2^-16 relative.  Every wave checks every row (two per lane)
+  // on the same LDS words, so the branch is uniform over the workgroup.
+  if (__builtin_amdgcn_ballot_w64(needs_lo(l_e) || needs_lo(l_e + 64)) == 0) return;
+  __syncthreads();   // every wave has read its high halves out of LDS
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int rr = 32 * rt + lr_e;
@@ -656,26 +718,26 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x16& t = o[dt][rt];
-        const uint32_t lo2 = pack_bf16x2(t[4 * i] * scale_o, t[4 * i + 1] * scale_o);
-        const uint32_t hi2 = pack_bf16x2(t[4 * i + 2] * scale_o, t[4 * i + 3] * scale_o);
+        float x[4];
+        uint32_t lw[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = t[4 * i + j] * scale_o;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t hi2 = pack_bf16x2(x[2 * h], x[2 * h + 1]);
+          lw[h] = pack_bf16x2(x[2 * h] - __uint_as_float(hi2 << 16), x[2 * h + 1] - __uint_as_float(hi2 & 0xffff0000u));
+        }
         const int c = 16 * w + 4 * dt + i;
-        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) = u32x2{lo2, hi2};
+        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) = u32x2{lw[0], lw[1]};
       }
   }
   __syncthreads();
-  for (int k = 0; k < 32; ++k) {                  // the wave's rows 32w .. 32w+31
+  for (int k = 0; k < 32; ++k) {
     const int rr = 32 * w + k;
     if (row0 + rr >= row_end) break;              // uniform
+    if (!needs_lo(rr)) continue;                  // uniform
     const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
-    uint16_t* dst = (slot < 0) ? a.out + ((size_t)b * R + row0 + rr) * kDv
-                               : a.ws_o + ((size_t)slot * a.rows_per_wg + rr) * kDv;
-    *(u32x4*)(dst + 8 * l_e) = v;
-  }
-  if (tid_e < 128 && row0 + tid_e < row_end) {
-    const int rr = tid_e;
-    const float lse_v = stats[2 * rr + 1];
-    if (slot < 0) a.lse[(size_t)b * R + row0 + rr] = lse_v;
-    else a.ws_lse[(size_t)slot * a.rows_per_wg + rr] = lse_v;
+    *(u32x4*)(a.ws_lo + (prow + rr) * kDv + 8 * l_e) = v;
   }
 }
 

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
       for (int i = 0; i < 8; ++i) o[i] = fmaf(wk, vrow[l + 64 * i], o[i]);
     }
   }
+  if (poison && a.err && l == 0) *a.err = 1;   // the plan's fault flag, when there is a plan
   const bool empty = lsum == 0.f;  // no visible key; NaN propagates
   float inv = poison ? __builtin_nanf("") : (empty ? 0.f : 1.f / lsum);
   float lse_v = poison ? __builtin_nanf("") : (empty ? -INFINITY : m + logf(lsum));

@@ -74,20 +74,6 @@ def compare(o, l, ref_o, ref_l, what=""):
     return summary
 
 
-def sample_rows(case, n_seq=6, heads=(0, 1, 31, 32, 63, 64, 100, 127), seed=0):
-    """Row ids to check at full size: a few sequences (first, last, longest, shortest and
-    random ones), every query position, a spread of heads."""
-    rng = np.random.default_rng(seed)
-    B, T, H = case.batch, case.q_len, case.num_heads
-    lens = case.cache_seqlens
-    pick = {0, B - 1, int(np.argmax(lens)), int(np.argmin(lens))}
-    while len(pick) < min(n_seq, B):
-        pick.add(int(rng.integers(0, B)))
-    hs = sorted({h for h in heads if h < H} | {H - 1})
-    rows = [(b * T + t) * H + h for b in sorted(pick) for t in range(T) for h in hs]
-    return np.array(rows, dtype=np.int64)
-
-
 def oracle_rows(case, rows=None, sinks=None, indices=None):
     """Oracle rows; `sinks` float32 [H] is widened exactly to float64."""
     sk = None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64)
