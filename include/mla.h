@@ -275,6 +275,33 @@ MLA_API int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* v
                             void* stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  mla_get_metadata + mla_decode_ex in one
+ * call, with the default plan (one workgroup per CU of the stream's device) and the split
+ * partials kept in device memory the library owns: a static array of
+ * MLA_NOALLOC_SCRATCH_BYTES (137 MiB: 1 MiB of plan metadata, 136 MiB of workspace) that
+ * every device the library runs on holds until the process ends.  The caller passes the
+ * inputs and outputs only; the call allocates nothing and never synchronises.
+ *   - A problem whose default plan needs more metadata or workspace than that (for
+ *     128-row problems, more than 544 partial slots, i.e. far more sequences than CUs)
+ *     returns MLA_ERR_WORKSPACE before anything is enqueued; a sparse problem
+ *     (topk > 0) returns MLA_ERR_UNSUPPORTED (its row lists need a caller workspace).
+ *   - Every call on a device shares that device's scratch, which keeps the last call's
+ *     contents: two calls that overlap on one device (different streams, or different
+ *     host threads) race and may corrupt each other's results.  Serialise them.
+ *   - Device-side input faults make the affected rows NaN, as in mla_decode; the flag
+ *     they raise stays in the scratch and is not reported (use mla_decode with a plan to
+ *     read it).
+ * Results are bit-identical to mla_get_metadata (default options, the device's CU count)
+ * followed by mla_decode_ex with that plan.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)137 << 20)
+MLA_API int32_t mla_decode_noalloc(const mla_problem_t* problem, const mla_variant_t* variant,
+                                   const void* q, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* cache_seqlens,
+                                   float scale, void* out, float* lse, void* stream);
+
+/*
  * Read back the device-side error flag of a plan after mla_decode ran with it:
  * synchronises `stream`, returns MLA_OK or MLA_ERR_BAD_INPUT, and clears the flag.
  */

@@ -30,7 +30,7 @@ from ._abi import (D_QK, D_V, DTYPE_BF16, DTYPE_F32, MAX_ROWS, PAGE, MlaError, P
 __all__ = ["D_QK", "D_V", "PAGE", "MAX_ROWS", "DTYPE_BF16", "DTYPE_F32", "MlaError", "Problem",
            "PlanOptions", "Plan", "lib", "lib_path", "metadata_bytes", "workspace_bytes",
            "get_metadata", "decode", "decode_splits", "combine", "make_problem", "Decoder",
-           "device_num_cus", "hbm_read_probe"]
+           "device_num_cus", "hbm_read_probe", "decode_noalloc"]
 
 
 def _stream_handle(stream):
@@ -150,6 +150,17 @@ def combine(problem: Problem, out, lse, plan: Plan, workspace, stream=None, sink
                            ctypes.byref(plan.c_plan),
                            _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
     _abi.check(rc, "mla_combine")
+
+
+def decode_noalloc(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: float, out, lse,
+                   stream=None, sinks=None) -> None:
+    """Enqueue the decode through mla_decode_noalloc: default plan and split partials in the
+    library's own device scratch (no buffers from the caller but inputs and outputs).
+    Calls that overlap on one device race on that scratch."""
+    rc = lib().mla_decode_noalloc(ctypes.byref(problem), _variant(sinks), _ptr(q), _ptr(kv_cache),
+                                  _ptr(block_table), _ptr(cache_seqlens), ctypes.c_float(scale), _ptr(out),
+                                  _ptr(lse), _stream_handle(stream))
+    _abi.check(rc, "mla_decode_noalloc")
 
 
 def hbm_read_probe(src, mode: int, sink, num_workgroups: int = 0, nbytes: int | None = None, stream=None) -> None:

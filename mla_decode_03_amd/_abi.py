@@ -25,7 +25,7 @@ MLA_ERR_BAD_INPUT = 9
 # Exported functions, as declared in include/mla.h.
 EXPORTS = ("mla_status_string", "mla_device_num_cus", "mla_metadata_bytes", "mla_workspace_bytes",
            "mla_get_metadata", "mla_decode", "mla_decode_ex", "mla_decode_splits", "mla_combine",
-           "mla_plan_error", "mla_hbm_read_probe")
+           "mla_plan_error", "mla_hbm_read_probe", "mla_decode_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmla.so")
@@ -101,6 +101,8 @@ def lib():
         L.mla_combine.argtypes = [ctypes.POINTER(Problem), V, vp, vp, ctypes.POINTER(CPlan), vp, sz, vp]
         L.mla_plan_error.restype = i32
         L.mla_plan_error.argtypes = [ctypes.POINTER(CPlan), vp]
+        L.mla_decode_noalloc.restype = i32
+        L.mla_decode_noalloc.argtypes = [ctypes.POINTER(Problem), V, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
         L.mla_hbm_read_probe.restype = i32
         L.mla_hbm_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
         _lib = L

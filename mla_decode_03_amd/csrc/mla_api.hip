@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_args.h"
@@ -460,6 +461,80 @@ int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant, 
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
   return launch_combine(a, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing --------------------------------------------
+// mla_decode_noalloc keeps its plan and split partials in `scratch`, library-owned device
+// memory: the first kScratchMetaBytes hold the plan's metadata, the rest the workspace.
+namespace {
+constexpr size_t kScratchMetaBytes = size_t(1) << 20;
+constexpr size_t kScratchWorkspaceBytes = size_t(136) << 20;
+constexpr size_t kScratchBytes = kScratchMetaBytes + kScratchWorkspaceBytes;
+static_assert(kScratchBytes == MLA_NOALLOC_SCRATCH_BYTES, "mla.h states the scratch size");
+}  // namespace
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices];   // per device: the array's device address there
+
+// Device address of `scratch` on device `dev`, looked up once per device with that device
+// current (each device holds its own copy of the array at its own address).
+int32_t scratch_on(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MLA_ERR_DEVICE;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MLA_ERR_DEVICE;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MLA_ERR_DEVICE;
+    if (e != hipSuccess || !ptr) return MLA_ERR_DEVICE;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t mla_decode_noalloc(const mla_problem_t* problem, const mla_variant_t* variant, const void* q,
+                           const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                           float scale, void* out, float* lse, void* stream) {
+  int32_t rc = check_problem(problem);
+  if (rc != MLA_OK) return rc;
+  if (problem->topk > 0) return MLA_ERR_UNSUPPORTED;   // sparse row lists need a caller workspace
+  if (problem->batch == 0) return MLA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MLA_ERR_DEVICE;
+  // the default plan on that device must fit the scratch (checked before anything is enqueued)
+  PlanShape s;
+  rc = plan_shape(problem, nullptr, cus, &s);
+  if (rc != MLA_OK) return rc;
+  const size_t meta_need = mla::meta_words(problem->batch, s.row_split, s.grid_wg) * sizeof(int32_t);
+  const size_t ws_need = problem->dtype == MLA_DTYPE_BF16 ? partial_bytes(s.max_partials, s.rows_per_wg) : 0;
+  if (meta_need > kScratchMetaBytes || ws_need > kScratchWorkspaceBytes) return MLA_ERR_WORKSPACE;
+  uint8_t* base = nullptr;
+  rc = scratch_on(dev, &base);
+  if (rc != MLA_OK) return rc;
+  mla_plan_t plan;
+  std::memset(&plan, 0, sizeof plan);
+  plan.metadata = base;
+  plan.metadata_bytes = kScratchMetaBytes;
+  rc = mla_get_metadata(problem, cache_seqlens, nullptr, cus, &plan, stream);
+  if (rc != MLA_OK) return rc;
+  return mla_decode_ex(problem, variant, q, kv_cache, block_table, cache_seqlens, scale, out, lse, &plan,
+                       base + kScratchMetaBytes, kScratchWorkspaceBytes, stream);
 }
 
 int32_t mla_plan_error(const mla_plan_t* plan, void* stream) {

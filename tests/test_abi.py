@@ -202,3 +202,15 @@ def test_hbm_probe_argument_checks():
     assert L.mla_hbm_read_probe(src, mib + 16384, 0, 4, sink, None) == _abi.MLA_ERR_SHAPE   # not divisible by 4 x 16 KiB
     assert L.mla_hbm_read_probe(src, 3 * 16384, 1, 2, sink, None) == _abi.MLA_ERR_SHAPE    # 24 KiB chunks
     assert L.mla_hbm_read_probe(src, 1 << 33, 0, 2, sink, None) == _abi.MLA_ERR_SHAPE      # 4 GiB chunks
+
+
+def test_noalloc_host_checks():
+    """mla_decode_noalloc's checks that need no device: null and invalid problems, batch 0
+    (a no-op), and the sparse form it does not serve."""
+    L = m.lib()
+    args = (None, None, None, None, ctypes.c_float(1.0), None, None, None)
+    assert L.mla_decode_noalloc(None, None, *args) == _abi.MLA_ERR_NULL
+    assert L.mla_decode_noalloc(ctypes.byref(_problem(num_heads=129)), None, *args) == _abi.MLA_ERR_SHAPE
+    assert L.mla_decode_noalloc(ctypes.byref(_problem(dtype=5)), None, *args) == _abi.MLA_ERR_DTYPE
+    assert L.mla_decode_noalloc(ctypes.byref(_problem(batch=0)), None, *args) == _abi.MLA_OK
+    assert L.mla_decode_noalloc(ctypes.byref(_problem(topk=64)), None, *args) == _abi.MLA_ERR_UNSUPPORTED
