@@ -741,6 +741,561 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   }
 }
 
+// ===== 128 rows: half pages through a four-slot ring =====================================
+// The page stream moves in half pages (32 tokens, 36,864 B) through a ring of four LDS
+// slots.  Each wave scores its own 32 rows (S^T = K . Q^T, one MFMA chain over the 36
+// 16-dim steps) and takes their softmax; its bf16 P goes to a double-buffered P area
+// after the ring.  P.V is split by value columns: wave w accumulates O^T over value
+// tiles 4w .. 4w+3 for all four row tiles (all 256 AGPRs), so a half page's V is read
+// from LDS once per workgroup, and every wave reads the other waves' P.  The waves meet
+// once per half page.  Iteration i runs P.V of half page i and the score MFMAs of half
+// page i+1 as one interleaved schedule, the softmax of half page i+1 under its last P.V
+// MFMAs; the copies of half page i+3 go out meanwhile, into the slot that half page i-1
+// freed.  (Every instruction between two MFMAs must issue within the MFMA's 32 cycles:
+// the schedule is built around that budget, with scalar work kept out of the slots.)
+// A half page in LDS is 9 column blocks of 64 dims x 32 tokens (4 KB each, rope last):
+// token t, 16-byte chunk p of block c at c*4096 + t*128 + (p ^ cswz(t))*16.
+constexpr int kHalf = 32;                          // tokens per half page
+constexpr int kSlotBytes = kHalf * kRowBytes;      // 36864
+constexpr int kSlotBlock = kHalf * 128;            // 4096: one column block of a half page
+constexpr int kRingScratch = 4 * kSlotBytes;       // 147456: the P area after the ring
+static_assert(kRingScratch + 2 * 8192 <= kLdsBytes, "ring and P area fit the LDS");
+constexpr int kRingPK = 2;                         // K-fragment prefetch distance (score steps)
+
+struct HalfPage {
+  const uint8_t* base;   // page start in the pool
+  int tok0;              // 0 or 32: which half of the page
+  int valid;             // tokens of the page in the sequence (later tokens read token 0)
+};
+// Half page h of a sequence (h counts 32-token halves from its start) held by pool page
+// `page`; a page index outside the pool reads page 0 and poisons the segment.
+__device__ __forceinline__ HalfPage half_page(const DecodeArgs& a, int page, int h, int Lc, bool& bad_page) {
+  const bool bad = page < 0 || page >= a.num_pages;
+  bad_page |= bad;
+  return HalfPage{a.kv + (size_t)(bad ? 0 : page) * kBlockBytes, (h & 1) * kHalf,
+                  bad ? 1 : min(kPage, Lc - (h >> 1) * kPage)};
+}
+// One wave-wide copy: column block i, tokens 8k .. 8k+7 of the half page, into `slot`.  The
+// slot address is made opaque per copy, so that the destinations of a run of copies are
+// each one scalar add here, not dozens of precomputed scalars held (and spilled) across it.
+__device__ __forceinline__ void half_copy(const HalfPage& h, MLA_LDS uint8_t* slot, int i, int k, int l) {
+  const int t = 8 * k + (l >> 3);
+  const int tp = h.tok0 + t;
+  const int te = tp < h.valid ? tp : 0;
+  uint32_t dst = (uint32_t)(uintptr_t)slot;
+  asm volatile("" : "+s"(dst));
+  dma16(h.base, (uint32_t)(te * kRowBytes + i * 128 + (((l & 7) ^ cswz(t)) << 4)),
+        (MLA_LDS uint8_t*)(uintptr_t)(dst + (uint32_t)(i * kSlotBlock + k * 1024)));
+}
+// The lane's byte offset in a half page for the copies of tokens 8k .. 8k+7 (column block 0;
+// block i adds 128 i): formed once per half page, so that each copy is one vector add and
+// one scalar add.
+__device__ __forceinline__ uint32_t half_copy_lane(const HalfPage& h, int k, int l) {
+  const int t = 8 * k + (l >> 3);
+  const int tp = h.tok0 + t;
+  const int te = tp < h.valid ? tp : 0;
+  return (uint32_t)(te * kRowBytes + (((l & 7) ^ cswz(t)) << 4));
+}
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+// P.V MFMA with no wait states ahead: for operands that no vector instruction has just
+// written (LDS reads, or registers written many instructions earlier).
+__device__ __forceinline__ void mfma_pv_ds(f32x16& o, const bf16x8& v, const bf16x8& p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+}
+// Score MFMA of one chain (accumulator in VGPRs); `first` starts the chain from zero.
+__device__ __forceinline__ void mfma_s(f32x16& acc, const bf16x8& k, const bf16x8& q, bool first) {
+  if (first)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+}
+// MFMA results retire before vector instructions read their accumulators.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 4" : : : "memory"); }
+
+__device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS uint8_t* lds, int b, int row0,
+                                                    int blk_lo, int blk_hi, int slot) {
+  const int w = wave_id(), l = threadIdx.x & 63;
+  const int g = l >> 5, lr = l & 31;
+  const int R = a.rows;
+  const int row_end = min(row0 + a.rows_per_wg, R);
+  const int myrow = row0 + 32 * w + lr;
+  const float c = a.scale_log2;
+
+  const int L = ld_const(a.seqlens, b);
+  // more keys than the block table's row can hold: ceil(L / kPage) > max_blocks, in 32 bits
+  const bool bad_len = (L < 0) || (L > 0 && (L - 1) / kPage >= a.max_blocks);
+  const int Lc = bad_len ? 0 : L;
+  int nvis = Lc;
+  if (a.causal && a.q_len > 1) nvis = Lc - a.q_len + 1 + min(myrow, R - 1) / a.heads;
+  nvis = max(nvis, 0);
+  int nmin = Lc;   // fewest visible keys over the wave's rows: masking starts there
+  if (a.causal && a.q_len > 1) nmin = max(Lc - a.q_len + 1 + min(row0 + 32 * w, R - 1) / a.heads, 0);
+  const int hp0 = 2 * blk_lo;                                                   // first half page
+  const int H = max(0, (min(blk_hi * kPage, Lc) + kHalf - 1) / kHalf - hp0);   // half pages with keys
+  const int* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  bool bad_page = false;
+  // P of two half pages after the ring: [half page & 1][row tile][K step][lane] x 16 B.
+  // After the page loop the same bytes hold the workgroup-OR words and the row statistics.
+  MLA_LDS uint8_t* pbuf = lds + kRingScratch;
+  MLA_LDS int* or_words = (MLA_LDS int*)pbuf;
+
+  __syncthreads();   // LDS free (a previous segment may still be reading it)
+  // ---- Q: each lane loads its row's fragments straight into registers (dims 16kk + 8g .. +8
+  // of row myrow: the B operand of S^T = K . Q^T), ahead of the first half pages' copies, so
+  // that both are in flight together.  A row past the workgroup's reads row row0; it is
+  // scored but never stored.
+  bf16x8 qf[36];
+  {
+    int tq = threadIdx.x;   // opaque: the address is formed here, not kept across the kernel
+    asm volatile("" : "+v"(tq));
+    const int qr = row0 + 32 * w + (tq & 31);
+    const uint8_t* qrow = a.q + ((size_t)b * R + (qr < row_end ? qr : row0)) * kRowBytes + 16 * ((tq >> 5) & 1);
+#pragma unroll
+    for (int kk = 0; kk < 36; ++kk) qf[kk] = *(const bf16x8*)(qrow + 32 * kk);
+  }
+  // The first two half pages into slots 0 and 1, each wave its 9 pieces of each (tokens
+  // 8w .. 8w+7), behind Q's loads: at most 54 loads in flight per wave, under the 63 that the
+  // wait counter holds.  The lane index comes from an opaque copy of the thread index, so
+  // that the copies' lane terms are formed here and not kept (spilled) across the kernel; a
+  // reload between these copies would wait for all of them.
+  auto first_pages = [&]() {
+    int tl = threadIdx.x;
+    asm volatile("" : "+v"(tl));
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      if (n < H) {
+        const HalfPage h = half_page(a, ld_const(bt_row, (hp0 + n) >> 1), hp0 + n, Lc, bad_page);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) half_copy(h, lds + n * kSlotBytes, i, w, tl & 63);
+      }
+    }
+  };
+  first_pages();
+  // lane terms of the K reads (token lr, dims 16kk + 8g) and the transposing V reads
+  int ky[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) ky[m] = lr * 128 + (((2 * m + g) ^ cswz(lr)) << 4);
+  const int jj = l & 15, qh = (l >> 4) & 1;
+  const int tv = 4 * g + (jj >> 2);
+  const int v_base = tv * 128 + 8 * (jj & 1);
+  int vy[2][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) vy[e][r] = v_base + 1024 * r + (((4 * e + 2 * qh + ((jj & 3) >> 1)) ^ cswz(tv + 8 * r)) << 4);
+
+  f32x16 o[16];   // O^T: value tile 4w + vt (values 128w + 32vt ..), row tile (w + r) % 4 at o[4 vt + r]
+  float m_ref = -INFINITY, mtrue = -INFINITY, lsum = 0.f;
+  bool over = false;
+  float mref_init = -INFINITY;
+  for (int pass = 0; pass < 2; ++pass) {
+    m_ref = mref_init;
+    mtrue = -INFINITY;
+    lsum = 0.f;
+    over = false;
+    // zeros from an opaque scalar formed in this pass (a plain zero vector is one value the
+    // compiler would keep, and spill, from the kernel's start to every pass)
+    int zi = 0;
+    asm volatile("" : "+s"(zi));
+    const float zf = __int_as_float(zi);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      o[t] = f32x16{zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf};
+      asm volatile("" : "+a"(o[t]));
+    }
+    if (pass == 1) first_pages();   // the second pass streams them again
+
+    // Wait for half page n, then meet the other waves: it has landed in every wave's copies,
+    // every wave's P of half page n-1 is in the P buffer, and every wave is past P.V of half
+    // page n-2 (its slot and P buffer are free).  Every wave issues 9 copies per half page,
+    // in half-page order, and at the wait for half page n only half page n+1 can be in
+    // flight behind it.
+    auto wait_half = [&](int n) {
+      if (n + 1 < H) asm volatile("s_waitcnt vmcnt(9)" : : : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      __syncthreads();
+    };
+
+    f32x16 sc;                    // the score chain, then the softmax's terms in place
+    u32x4 pn0, pn1;               // the wave's own P (bf16 B operands of the two K steps)
+    float rs = 0.f, rmax = -INFINITY, msub = 0.f;
+    auto sm_mask = [&](f32x16& s, int hpa) {
+      if ((hpa + 1) * kHalf > nmin) {
+        asm volatile("");
+        // element e holds token 8(e/4) + 4g + e%4 of the half page
+        const int lim = nvis - hpa * kHalf - 4 * g;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3) < lim) ? s[e] : -INFINITY;
+      }
+    };
+    // Softmax set-up of the (masked) scores in sc: the reference max where the row has none
+    // yet, from these scores and `extra` (the lane's max over the rest of the page).
+    auto sm_ref = [&](float extra) {
+      if (__builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0) {
+        float mr = extra;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mr = fmaxf(mr, sc[e]);
+        const float mx = half_max(mr) * c;
+        if (m_ref == -INFINITY) m_ref = mx;   // nothing accumulated yet: exact
+      }
+      msub = (m_ref == -INFINITY) ? 0.f : m_ref;
+      rs = 0.f;
+      rmax = -INFINITY;
+    };
+    auto sm_elem = [&](int e) {
+      rmax = fmaxf(rmax, sc[e]);
+      sc[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -msub));
+      rs += sc[e];
+    };
+    auto sm_pack = [&](int m) {
+      const uint32_t x = pack_bf16x2(sc[4 * m], sc[4 * m + 1]), y = pack_bf16x2(sc[4 * m + 2], sc[4 * m + 3]);
+      if (m < 2) { pn0[2 * m] = x; pn0[2 * m + 1] = y; }
+      else { pn1[2 * (m - 2)] = x; pn1[2 * (m - 2) + 1] = y; }
+    };
+    // After the 16 terms: this lane's half of the row sum.  No term exceeds 2^kRefSlack
+    // unless this half-row sum does (an overflow to inf included), and only then does the
+    // row take the half page's max, for the second pass's bound.
+    auto sm_finish = [&]() {
+      lsum += rs;
+      if (__builtin_amdgcn_ballot_w64(rs > kSumCap) != 0) {
+        over |= rs > kSumCap;
+        mtrue = fmaxf(mtrue, rmax * c);
+      }
+    };
+    auto softmax_alone = [&](float extra) {
+      sm_ref(extra);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sm_elem(e);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sm_pack(m);
+      sm_finish();
+    };
+    // The wave's P of half page n into the P buffer: row tile w, both K steps.
+    auto put_p = [&](int n) {
+      MLA_LDS uint8_t* pb = pbuf + (n & 1) * 8192 + (2 * w * 64 + l) * 16;
+      *(MLA_LDS u32x4*)pb = pn0;
+      *(MLA_LDS u32x4*)(pb + 64 * 16) = pn1;
+    };
+    auto get_p = [&](int n, int rt, int ks) {
+      return lds_read_b128(pbuf + (n & 1) * 8192 + ((2 * rt + ks) * 64 + l) * 16);
+    };
+    // Score loop over the half page in `ks` alone: one MFMA per step (one dependent chain
+    // issues at the full MFMA rate); when cp, this wave's 9 copies of `nxt` into `nslot` go
+    // out at steps 2, 6, ..., 34, each behind its step's MFMA.  Ends with the scores in sc.
+    auto score = [&](const MLA_LDS uint8_t* ks, bool cp, const HalfPage& nxt, MLA_LDS uint8_t* nslot) {
+      auto load_k = [&](int kk) { return lds_read_b128(ks + (kk >> 2) * kSlotBlock + ky[kk & 3]); };
+      bf16x8 kr[kRingPK + 1];
+#pragma unroll
+      for (int kk = 0; kk < kRingPK; ++kk) kr[kk] = load_k(kk);
+#pragma unroll
+      for (int kk = 0; kk < 36; ++kk) {
+        if (kk + kRingPK < 36) kr[(kk + kRingPK) % (kRingPK + 1)] = load_k(kk + kRingPK);
+        mfma_s(sc, kr[kk % (kRingPK + 1)], qf[kk], kk == 0);
+        if (cp && (kk & 3) == 2) half_copy(nxt, nslot, kk >> 2, w, l);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma_drain();
+    };
+    // V^T fragment of value tile 4w + vt, K step ks, of the half page in slot `vs`.
+    auto load_v = [&](const MLA_LDS uint8_t* vs, int vt, int ks) {
+      const int t = 4 * w + vt;
+      const MLA_LDS uint8_t* vp = vs + ks * 16 * 128 + (t >> 1) * kSlotBlock;
+      return cat8(lds_read_tr(vp + vy[t & 1][0]), lds_read_tr(vp + vy[t & 1][1]));
+    };
+    // P.V of half page n as 32 steps q: K step q/16, value tile (q/4)%4, row tile
+    // (w + q%4)%4, so that each step group starts on the wave's own row tile, whose P is
+    // still in registers (pn0, pn1).  V fragments: one group ahead, in vq[group & 1]; the
+    // last group reads the next half page's first one (slot `nvs`).  Other row tiles' P
+    // come from the P buffer: K step 0's at the start, K step 1's each right after its
+    // last K-step-0 use.
+    bf16x8 vq[2];
+    bf16x8 pq[3];                 // P of row tiles w+1, w+2, w+3 for the current K step
+    auto pv_begin = [&](int n) {
+#pragma unroll
+      for (int r = 1; r < 4; ++r) pq[r - 1] = get_p(n, (w + r) & 3, 0);
+    };
+    auto pv_step = [&](int n, const MLA_LDS uint8_t* vs, const MLA_LDS uint8_t* nvs, bool pre, int q) {
+      const int ks = q >> 4, vt = (q >> 2) & 3, r = q & 3;
+      if (r == 0) {
+        const int gq = (q >> 2) + 1;   // the next group
+        if (gq < 8) vq[gq & 1] = load_v(vs, gq & 3, gq >> 2);
+        else if (pre) vq[0] = load_v(nvs, 0, 0);
+      }
+      const bf16x8 pb = (r == 0) ? __builtin_bit_cast(bf16x8, ks == 0 ? pn0 : pn1) : pq[r - 1];
+      mfma_pv_ds(o[4 * vt + r], vq[(q >> 2) & 1], pb);   // o[4 vt + r]: row tile (w + r) % 4
+      if (ks == 0 && vt == 3 && r > 0) pq[r - 1] = get_p(n, (w + r) & 3, 1);
+    };
+    auto pv_alone = [&](int n, const MLA_LDS uint8_t* vs, bool pre, const MLA_LDS uint8_t* nvs) {
+      pv_begin(n);
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        pv_step(n, vs, nvs, pre, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // One fused iteration i (1 <= i <= H-2), after the barrier at its top: P.V of half page
+    // i (slot i&3), the scores of half page i+1 (slot (i+1)&3) and their softmax, as one
+    // schedule of 68 MFMA slots:
+    //   0-1    P.V steps 0-1 (the first on registers alone: V read ahead, the wave's own P);
+    //   2-49   16 x (score, score, P.V): score steps 0-31, P.V steps 2-17;
+    //   50-53  score steps 32-35;
+    //   54-67  P.V steps 18-31 with the softmax between them; its K-step-1 P replaces pn1
+    //          only after P.V step 28, the last to read it.
+    // Then the wave's new P goes to the P buffer (other waves read it after the next barrier).
+    // The 9 copies of half page i+3 into slot (i+3)&3 go out every 7 slots from slot 5.
+    auto fused = [&](int i, auto cp_tag, const HalfPage& nxt) {
+      constexpr bool cp = decltype(cp_tag)::value;
+      const MLA_LDS uint8_t* ks = lds + ((i + 1) & 3) * kSlotBytes;
+      const MLA_LDS uint8_t* vs = lds + (i & 3) * kSlotBytes;
+      MLA_LDS uint8_t* nslot = lds + ((i + 3) & 3) * kSlotBytes + w * 1024;
+      const uint32_t coff = cp ? half_copy_lane(nxt, w, l) : 0u;
+      auto load_k = [&](int kk) { return lds_read_b128(ks + (kk >> 2) * kSlotBlock + ky[kk & 3]); };
+      bf16x8 kr[kRingPK + 1];
+      pv_begin(i);
+#pragma unroll
+      for (int kk = 0; kk < kRingPK; ++kk) kr[kk] = load_k(kk);
+      auto s_step = [&](int kk) {
+        if (kk + kRingPK < 36) kr[(kk + kRingPK) % (kRingPK + 1)] = load_k(kk + kRingPK);
+        mfma_s(sc, kr[kk % (kRingPK + 1)], qf[kk], kk == 0);
+      };
+      // what slot j carries besides its MFMA: a copy, or a piece of the softmax (each
+      // piece's results pass through an empty asm statement, which keeps the piece in its
+      // slot: pure arithmetic would otherwise sink to its first use)
+      auto extra = [&](int j) {
+        if (cp && j % 7 == 5) dma16(nxt.base, coff + (j / 7) * 128, nslot + (j / 7) * kSlotBlock);
+        if (j == 55) {
+          mfma_drain();                      // the last score MFMA's result, read below
+          sm_mask(sc, hp0 + i + 1);
+          sm_ref(-INFINITY);
+        }
+        if (j >= 56 && j < 64) {
+          sm_elem(2 * (j - 56));
+          sm_elem(2 * (j - 56) + 1);
+          asm volatile("" : "+v"(sc[2 * (j - 56)]), "+v"(sc[2 * (j - 56) + 1]), "+v"(rs), "+v"(rmax));
+        }
+        if (j == 60 || j == 62) {            // pn0 is free after P.V step 12 (slot 40)
+          sm_pack((j - 60) >> 1);
+          asm volatile("" : "+v"(pn0));
+        }
+        if (j == 65 || j == 66) {            // pn1 after P.V step 28 (slot 64)
+          sm_pack(2 + (j - 65));
+          asm volatile("" : "+v"(pn1));
+        }
+        if (j == 67) {
+          sm_finish();
+          put_p(i + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {          // slots 0-1
+        pv_step(i, vs, ks, true, q);
+        extra(q);
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {         // slots 2-49
+        s_step(2 * m);
+        extra(2 + 3 * m);
+        s_step(2 * m + 1);
+        extra(3 + 3 * m);
+        pv_step(i, vs, ks, true, 2 + m);
+        extra(4 + 3 * m);
+      }
+#pragma unroll
+      for (int kk = 32; kk < 36; ++kk) {     // slots 50-53
+        s_step(kk);
+        extra(18 + kk);
+      }
+#pragma unroll
+      for (int q = 18; q < 32; ++q) {        // slots 54-67
+        pv_step(i, vs, ks, true, q);
+        extra(36 + q);
+      }
+    };
+
+    if (H > 0) {
+      int pg_ahead = (H > 4) ? ld_const(bt_row, (hp0 + 4) >> 1) : 0;   // page of half page 4
+      // half pages 2 and 3 go out in the first two score loops
+      HalfPage h2{}, h3{};
+      if (H > 2) h2 = half_page(a, ld_const(bt_row, (hp0 + 2) >> 1), hp0 + 2, Lc, bad_page);
+      if (H > 3) h3 = half_page(a, ld_const(bt_row, (hp0 + 3) >> 1), hp0 + 3, Lc, bad_page);
+      // Half pages 0 and 1 are scored before the first softmax, so that a row's reference
+      // max comes from the segment's whole first page, as keys are laid out in pages.
+      wait_half(0);
+      score(lds, H > 2, h2, lds + 2 * kSlotBytes);
+      sm_mask(sc, hp0);
+      f32x16 s1 = sc;
+      float ex = -INFINITY;
+      if (H > 1) {
+        wait_half(1);
+        score(lds + kSlotBytes, H > 3, h3, lds + 3 * kSlotBytes);
+        sm_mask(sc, hp0 + 1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ex = fmaxf(ex, sc[e]);
+        const f32x16 t = sc;
+        sc = s1;
+        s1 = t;
+      }
+      softmax_alone(ex);                     // half page 0
+      put_p(0);
+      vq[0] = load_v(lds, 0, 0);
+      __syncthreads();                       // every wave's P of half page 0
+      pv_alone(0, lds, H > 1, lds + kSlotBytes);
+      if (H > 1) {
+        sc = s1;
+        softmax_alone(-INFINITY);            // half page 1 (its P goes to the other buffer)
+        put_p(1);
+      }
+      // Iterations that copy half page i+3, then the last two that do not: two copies of the
+      // fused schedule, so that no copy carries a branch.
+      int i = 1;
+      for (; i + 3 < H; ++i) {
+        const HalfPage nxt = half_page(a, pg_ahead, hp0 + i + 3, Lc, bad_page);
+        // The next page entry: a scalar load, issued before the barrier and waited for right
+        // after it.  Scalar loads share the LDS wait counter and may return out of order, so
+        // one still in flight would turn the iteration's LDS waits into full waits.
+        pg_ahead = ld_const(bt_row, (hp0 + min(i + 4, H - 1)) >> 1);
+        wait_half(i + 1);
+        asm volatile("" : : "s"(pg_ahead));
+        fused(i, BoolC<true>{}, nxt);
+      }
+      for (; i + 1 < H; ++i) {
+        wait_half(i + 1);
+        fused(i, BoolC<false>{}, HalfPage{});
+      }
+      if (H > 1) {                           // the last half page
+        __syncthreads();                     // every wave's P of it
+        pv_alone(H - 1, lds + ((H - 1) & 3) * kSlotBytes, false, lds);
+      }
+    }
+    mfma_drain();
+    if (!wg_or(over, or_words)) break;
+    // Second pass from an upper bound of every score of the row: half pages that did not
+    // flag stayed within m_ref + kRefSlack, the flagged ones gave their maxima.
+    {
+      const float mt = fmaxf(mtrue, m_ref + kRefSlack);
+      mref_init = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    }
+  }
+
+  // ---- epilogue: every wave needs the row statistics of all 128 rows ---------------------
+  const bool poison = bad_len || wg_or(bad_page, or_words);   // (its barriers: every slot is idle)
+  if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
+  MLA_LDS float* stats = (MLA_LDS float*)pbuf + 16;   // [row][scale_o, lse], after the OR words
+  MLA_LDS float* amax = stats + 2 * 128;              // [wave][row]: largest |o| over the wave's columns
+  lsum += __shfl_xor(lsum, 32, 64);                   // the row's two halves
+  int tid_e = threadIdx.x;                            // lane terms formed after the loop (not kept across it)
+  asm volatile("" : "+v"(tid_e));
+  const int l_e = tid_e & 63, g_e = l_e >> 5, lr_e = l_e & 31;
+  if (g_e == 0) {
+    const int rr = 32 * w + lr_e;
+    float so, lse_v;
+    if (poison) {
+      so = __builtin_nanf("");
+      lse_v = __builtin_nanf("");
+    } else if (slot < 0 && a.sinks) {
+      const SinkFold f = fold_sink<true>(m_ref, lsum, a.sinks[(row0 + rr) % a.heads] * kLog2e);
+      so = f.scale_o;
+      lse_v = f.lse * kLn2;
+    } else {
+      const bool empty = lsum == 0.f;   // no visible key; NaN propagates
+      so = empty ? 0.f : 1.f / lsum;
+      lse_v = empty ? -INFINITY : (m_ref + __log2f(lsum)) * kLn2;
+    }
+    stats[2 * rr] = so;
+    stats[2 * rr + 1] = lse_v;
+  }
+  __syncthreads();
+  // O (normalised, bf16) goes through the idle ring so that every store writes a whole 1 KB
+  // row: row rr at rr*1024, 16-byte chunk cc (values 8cc .. 8cc+7) at (cc ^ (rr & 15))*16.
+  // For a split partial the same pass takes each row's largest |o| over the wave's columns.
+  const bool part = slot >= 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 32 * ((w + r) & 3) + lr_e;
+    const float so = stats[2 * rr];
+    float mx = 0.f;
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x16& t = o[4 * vt + r];
+        const float x0 = t[4 * i] * so, x1 = t[4 * i + 1] * so;
+        const float x2 = t[4 * i + 2] * so, x3 = t[4 * i + 3] * so;
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+        const int cc = 16 * w + 4 * vt + i;
+        *(MLA_LDS u32x2*)(lds + rr * 1024 + ((cc ^ (rr & 15)) << 4) + 8 * g_e) =
+            u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      }
+    if (part) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (g_e == 0) amax[w * 128 + rr] = mx;
+    }
+  }
+  __syncthreads();
+  // A split partial row whose largest |o| exceeds kLoCut also stores its low half.
+  auto needs_lo = [&](int rr) {
+    return row0 + rr < row_end && fmaxf(fmaxf(amax[rr], amax[128 + rr]), fmaxf(amax[256 + rr], amax[384 + rr])) > kLoCut;
+  };
+  const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
+  for (int k = 0; k < 32; ++k) {                      // the wave's rows 32w .. 32w+31
+    const int rr = 32 * w + k;
+    if (row0 + rr >= row_end) break;                  // uniform
+    const u32x4 v = *(const MLA_LDS u32x4*)(lds + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
+    uint16_t* dst = part ? a.ws_hi + (prow + rr) * kDv : a.out + ((size_t)b * R + row0 + rr) * kDv;
+    *(u32x4*)(dst + 8 * l_e) = v;
+  }
+  if (tid_e < 128 && row0 + tid_e < row_end) {
+    const int rr = tid_e;
+    const float lse_v = stats[2 * rr + 1];
+    if (!part) {
+      a.lse[(size_t)b * R + row0 + rr] = lse_v;
+    } else {
+      a.ws_lse[prow + rr] = lse_v;
+      a.ws_flag[prow + rr] = needs_lo(rr) ? 1 : 0;
+    }
+  }
+  if (!part) return;
+  // Low halves: lo = bf16(o - hi), o the fp32 normalised value and hi its bf16 rounding,
+  // so hi + lo carries o to 2^-16 relative.  Every wave checks every row (two per lane)
+  // on the same LDS words, so the branch is uniform over the workgroup.
+  if (__builtin_amdgcn_ballot_w64(needs_lo(l_e) || needs_lo(l_e + 64)) == 0) return;
+  __syncthreads();   // every wave has read its high halves out of LDS
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 32 * ((w + r) & 3) + lr_e;
+    const float so = stats[2 * rr];
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x16& t = o[4 * vt + r];
+        float x[4];
+        uint32_t lw[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = t[4 * i + j] * so;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t hi2 = pack_bf16x2(x[2 * h], x[2 * h + 1]);
+          lw[h] = pack_bf16x2(x[2 * h] - __uint_as_float(hi2 << 16), x[2 * h + 1] - __uint_as_float(hi2 & 0xffff0000u));
+        }
+        const int cc = 16 * w + 4 * vt + i;
+        *(MLA_LDS u32x2*)(lds + rr * 1024 + ((cc ^ (rr & 15)) << 4) + 8 * g_e) = u32x2{lw[0], lw[1]};
+      }
+  }
+  __syncthreads();
+  for (int k = 0; k < 32; ++k) {
+    const int rr = 32 * w + k;
+    if (row0 + rr >= row_end) break;                  // uniform
+    if (!needs_lo(rr)) continue;                      // uniform
+    const u32x4 v = *(const MLA_LDS u32x4*)(lds + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
+    *(u32x4*)(a.ws_lo + (prow + rr) * kDv + 8 * l_e) = v;
+  }
+}
+
 // ===== kernel ==========================================================================
 // NRT = 32-row tiles per workgroup (1, 2 or 4).
 template <int NRT, bool SPARSE>
@@ -788,7 +1343,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
       slot = -1;
       pos = end;
     }
-    decode_segment_wide<NRT, SPARSE>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    if constexpr (NRT == 4 && !SPARSE) decode_segment_cols(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    else decode_segment_wide<NRT, SPARSE>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
   }
 }
 

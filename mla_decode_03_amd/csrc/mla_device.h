@@ -90,6 +90,13 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ inline float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
+// max of v over lanes l and l ^ 32, in VALU (gfx950's lane-half swap): no LDS access, so
+// it adds nothing to the LDS wait counter.  After the swap of v with itself, the first
+// result holds the low half's values in both halves and the second the high half's.
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Two floats -> a packed bf16 pair (lo in bits 0-15), round to nearest even, NaN kept
 // NaN: one v_cvt_pk_bf16_f32 on gfx950.
