@@ -843,37 +843,38 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
   MLA_LDS int* or_words = (MLA_LDS int*)pbuf;
 
   __syncthreads();   // LDS free (a previous segment may still be reading it)
+  // Half page n (0 or 1) into slot n, each wave its 9 pieces (tokens 8w .. 8w+7).  The
+  // lane index comes from an opaque copy of the thread index, so that the copies' lane
+  // terms are formed here and not kept (spilled) across the kernel; a reload between these
+  // copies would wait for all of them.
+  auto first_copy = [&](int n) {
+    if (n < H) {
+      int tl = threadIdx.x;
+      asm volatile("" : "+v"(tl));
+      const HalfPage h = half_page(a, ld_const(bt_row, (hp0 + n) >> 1), hp0 + n, Lc, bad_page);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) half_copy(h, lds + n * kSlotBytes, i, w, tl & 63);
+    }
+  };
+  // Half page 0 goes out first, then Q, then half page 1: the first score loop starts once
+  // half page 0 is in (every wave's copies), and each of its steps waits only for its own
+  // Q fragment.  At most 54 loads are in flight per wave, under the 63 the counter holds.
+  first_copy(0);
   // ---- Q: each lane loads its row's fragments straight into registers (dims 16kk + 8g .. +8
-  // of row myrow: the B operand of S^T = K . Q^T), ahead of the first half pages' copies, so
-  // that both are in flight together.  A row past the workgroup's reads row row0; it is
-  // scored but never stored.
+  // of row myrow: the B operand of S^T = K . Q^T).  A row past the workgroup's reads row
+  // row0; it is scored but never stored.
   bf16x8 qf[36];
   {
     int tq = threadIdx.x;   // opaque: the address is formed here, not kept across the kernel
     asm volatile("" : "+v"(tq));
-    const int qr = row0 + 32 * w + (tq & 31);
-    const uint8_t* qrow = a.q + ((size_t)b * R + (qr < row_end ? qr : row0)) * kRowBytes + 16 * ((tq >> 5) & 1);
+    // a scalar base for the workgroup's rows and a 32-bit lane offset (under 148 KB)
+    const uint8_t* qb = a.q + ((size_t)b * R + row0) * kRowBytes;
+    const int rq = 32 * w + (tq & 31);
+    const uint32_t qo = (uint32_t)((row0 + rq < row_end ? rq : 0) * kRowBytes + 16 * ((tq >> 5) & 1));
 #pragma unroll
-    for (int kk = 0; kk < 36; ++kk) qf[kk] = *(const bf16x8*)(qrow + 32 * kk);
+    for (int kk = 0; kk < 36; ++kk) qf[kk] = *(const bf16x8*)(qb + qo + 32 * kk);
   }
-  // The first two half pages into slots 0 and 1, each wave its 9 pieces of each (tokens
-  // 8w .. 8w+7), behind Q's loads: at most 54 loads in flight per wave, under the 63 that the
-  // wait counter holds.  The lane index comes from an opaque copy of the thread index, so
-  // that the copies' lane terms are formed here and not kept (spilled) across the kernel; a
-  // reload between these copies would wait for all of them.
-  auto first_pages = [&]() {
-    int tl = threadIdx.x;
-    asm volatile("" : "+v"(tl));
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      if (n < H) {
-        const HalfPage h = half_page(a, ld_const(bt_row, (hp0 + n) >> 1), hp0 + n, Lc, bad_page);
-#pragma unroll
-        for (int i = 0; i < 9; ++i) half_copy(h, lds + n * kSlotBytes, i, w, tl & 63);
-      }
-    }
-  };
-  first_pages();
+  first_copy(1);
   // lane terms of the K reads (token lr, dims 16kk + 8g) and the transposing V reads
   int ky[4];
 #pragma unroll
@@ -906,7 +907,10 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       o[t] = f32x16{zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf, zf};
       asm volatile("" : "+a"(o[t]));
     }
-    if (pass == 1) first_pages();   // the second pass streams them again
+    if (pass == 1) {                // the second pass streams them again
+      first_copy(0);
+      first_copy(1);
+    }
 
     // Wait for half page n, then meet the other waves: it has landed in every wave's copies,
     // every wave's P of half page n-1 is in the P buffer, and every wave is past P.V of half
@@ -918,6 +922,14 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
       __syncthreads();
     };
+    // The first pass's wait for half page 0: Q's 36 loads, and half page 1's copies, may
+    // still be in flight behind it.
+    auto wait_first = [&]() {
+      if (pass == 1) wait_half(0);
+      else if (1 < H) asm volatile("s_waitcnt vmcnt(45)" : : : "memory");
+      else asm volatile("s_waitcnt vmcnt(36)" : : : "memory");
+      if (pass == 0) __syncthreads();
+    };
 
     f32x16 sc;                    // the score chain, then the softmax's terms in place
     u32x4 pn0, pn1;               // the wave's own P (bf16 B operands of the two K steps)
@@ -925,8 +937,11 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     auto sm_mask = [&](f32x16& s, int hpa) {
       if ((hpa + 1) * kHalf > nmin) {
         asm volatile("");
-        // element e holds token 8(e/4) + 4g + e%4 of the half page
-        const int lim = nvis - hpa * kHalf - 4 * g;
+        // element e holds token 8(e/4) + 4g + e%4 of the half page; lim is formed here (an
+        // opaque value), so that the compares stay inside this rarely taken branch
+        int lz = threadIdx.x;
+        asm volatile("" : "+v"(lz));
+        const int lim = nvis - hpa * kHalf - 4 * ((lz >> 5) & 1);
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3) < lim) ? s[e] : -INFINITY;
       }
@@ -979,6 +994,10 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       *(MLA_LDS u32x4*)pb = pn0;
       *(MLA_LDS u32x4*)(pb + 64 * 16) = pn1;
     };
+    auto put_p_half = [&](int n, int ks) {
+      MLA_LDS uint8_t* pb = pbuf + (n & 1) * 8192 + ((2 * w + ks) * 64 + l) * 16;
+      *(MLA_LDS u32x4*)pb = ks == 0 ? pn0 : pn1;
+    };
     auto get_p = [&](int n, int rt, int ks) {
       return lds_read_b128(pbuf + (n & 1) * 8192 + ((2 * rt + ks) * 64 + l) * 16);
     };
@@ -988,13 +1007,17 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     auto score = [&](const MLA_LDS uint8_t* ks, bool cp, const HalfPage& nxt, MLA_LDS uint8_t* nslot) {
       auto load_k = [&](int kk) { return lds_read_b128(ks + (kk >> 2) * kSlotBlock + ky[kk & 3]); };
       bf16x8 kr[kRingPK + 1];
+      int lc = threadIdx.x;                  // lane index formed here, not kept across the kernel
+      asm volatile("" : "+v"(lc));
+      const uint32_t coff = cp ? half_copy_lane(nxt, w, lc & 63) : 0u;
+      MLA_LDS uint8_t* nw = nslot + w * 1024;
 #pragma unroll
       for (int kk = 0; kk < kRingPK; ++kk) kr[kk] = load_k(kk);
 #pragma unroll
       for (int kk = 0; kk < 36; ++kk) {
         if (kk + kRingPK < 36) kr[(kk + kRingPK) % (kRingPK + 1)] = load_k(kk + kRingPK);
         mfma_s(sc, kr[kk % (kRingPK + 1)], qf[kk], kk == 0);
-        if (cp && (kk & 3) == 2) half_copy(nxt, nslot, kk >> 2, w, l);
+        if (cp && (kk & 3) == 2) dma16(nxt.base, coff + (kk >> 2) * 128, nw + (kk >> 2) * kSlotBlock);
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma_drain();
@@ -1046,12 +1069,16 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     //          only after P.V step 28, the last to read it.
     // Then the wave's new P goes to the P buffer (other waves read it after the next barrier).
     // The 9 copies of half page i+3 into slot (i+3)&3 go out every 7 slots from slot 5.
+    HalfPage nn{};                // the next iteration's copy source, formed in slot 14
+    int pg_ahead = 0;             // page entry of the half page after it
     auto fused = [&](int i, auto cp_tag, const HalfPage& nxt) {
       constexpr bool cp = decltype(cp_tag)::value;
       const MLA_LDS uint8_t* ks = lds + ((i + 1) & 3) * kSlotBytes;
       const MLA_LDS uint8_t* vs = lds + (i & 3) * kSlotBytes;
       MLA_LDS uint8_t* nslot = lds + ((i + 3) & 3) * kSlotBytes + w * 1024;
-      const uint32_t coff = cp ? half_copy_lane(nxt, w, l) : 0u;
+      int lc = threadIdx.x;                  // lane index formed here, not kept across the kernel
+      asm volatile("" : "+v"(lc));
+      const uint32_t coff = cp ? half_copy_lane(nxt, w, lc & 63) : 0u;
       auto load_k = [&](int kk) { return lds_read_b128(ks + (kk >> 2) * kSlotBlock + ky[kk & 3]); };
       bf16x8 kr[kRingPK + 1];
       pv_begin(i);
@@ -1066,27 +1093,38 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       // slot: pure arithmetic would otherwise sink to its first use)
       auto extra = [&](int j) {
         if (cp && j % 7 == 5) dma16(nxt.base, coff + (j / 7) * 128, nslot + (j / 7) * kSlotBlock);
-        if (j == 55) {
-          mfma_drain();                      // the last score MFMA's result, read below
-          sm_mask(sc, hp0 + i + 1);
-          sm_ref(-INFINITY);
+        if (cp && j == 14 && i + 4 < H) {    // half page i+4's source (its page entry came in at the top)
+          nn = half_page(a, pg_ahead, hp0 + i + 4, Lc, bad_page);
+          asm volatile("" : "+s"(nn.base), "+s"(nn.tok0), "+s"(nn.valid));
         }
-        if (j >= 56 && j < 64) {
-          sm_elem(2 * (j - 56));
-          sm_elem(2 * (j - 56) + 1);
-          asm volatile("" : "+v"(sc[2 * (j - 56)]), "+v"(sc[2 * (j - 56) + 1]), "+v"(rs), "+v"(rmax));
+        // the softmax terms: slot 55 (the last score MFMA's result has retired) takes the
+        // set-up and term 0, slots 56-58 two terms each, slots 59-66 one or two more
+        constexpr int kT0[12] = {0, 1, 3, 5, 7, 8, 9, 10, 11, 12, 13, 15};   // first term of slot 55 + n
+        if (j >= 55 && j <= 66) {
+          if (j == 55) {
+            mfma_drain();
+            sm_mask(sc, hp0 + i + 1);
+            sm_ref(-INFINITY);
+          }
+          const int e0 = kT0[j - 55], e1 = (j == 66) ? 16 : kT0[j - 54];
+#pragma unroll
+          for (int e = e0; e < e1; ++e) {
+            sm_elem(e);
+            asm volatile("" : "+v"(sc[e]), "+v"(rs));
+          }
         }
-        if (j == 60 || j == 62) {            // pn0 is free after P.V step 12 (slot 40)
-          sm_pack((j - 60) >> 1);
+        if (j == 58 || j == 59) {            // pn0 is free after P.V step 12 (slot 34)
+          sm_pack(j - 58);
           asm volatile("" : "+v"(pn0));
         }
+        if (j == 60) put_p_half(i + 1, 0);
         if (j == 65 || j == 66) {            // pn1 after P.V step 28 (slot 64)
           sm_pack(2 + (j - 65));
           asm volatile("" : "+v"(pn1));
         }
-        if (j == 67) {
+        if (j == 66) {
           sm_finish();
-          put_p(i + 1);
+          put_p_half(i + 1, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -1117,14 +1155,14 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     };
 
     if (H > 0) {
-      int pg_ahead = (H > 4) ? ld_const(bt_row, (hp0 + 4) >> 1) : 0;   // page of half page 4
+      pg_ahead = (H > 4) ? ld_const(bt_row, (hp0 + 4) >> 1) : 0;   // page of half page 4
       // half pages 2 and 3 go out in the first two score loops
       HalfPage h2{}, h3{};
       if (H > 2) h2 = half_page(a, ld_const(bt_row, (hp0 + 2) >> 1), hp0 + 2, Lc, bad_page);
       if (H > 3) h3 = half_page(a, ld_const(bt_row, (hp0 + 3) >> 1), hp0 + 3, Lc, bad_page);
       // Half pages 0 and 1 are scored before the first softmax, so that a row's reference
       // max comes from the segment's whole first page, as keys are laid out in pages.
-      wait_half(0);
+      wait_first();
       score(lds, H > 2, h2, lds + 2 * kSlotBytes);
       sm_mask(sc, hp0);
       f32x16 s1 = sc;
@@ -1151,9 +1189,10 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       }
       // Iterations that copy half page i+3, then the last two that do not: two copies of the
       // fused schedule, so that no copy carries a branch.
+      if (H > 4) nn = half_page(a, pg_ahead, hp0 + 4, Lc, bad_page);
       int i = 1;
       for (; i + 3 < H; ++i) {
-        const HalfPage nxt = half_page(a, pg_ahead, hp0 + i + 3, Lc, bad_page);
+        const HalfPage nxt = nn;             // half page i+3
         // The next page entry: a scalar load, issued before the barrier and waited for right
         // after it.  Scalar loads share the LDS wait counter and may return out of order, so
         // one still in flight would turn the iteration's LDS waits into full waits.
