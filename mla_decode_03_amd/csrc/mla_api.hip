@@ -42,7 +42,7 @@ int32_t check_problem(const mla_problem_t* p) {
   if (p->num_pages < 1 || p->max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
   if (p->block_table_stride < p->max_blocks_per_seq) return MLA_ERR_SHAPE;
   // global block positions, page offsets and partial indices stay in int32 range
-  if ((int64_t)p->batch * p->max_blocks_per_seq * 4 > INT32_MAX) return MLA_ERR_SHAPE;
+  if ((int64_t)p->batch * p->max_blocks_per_seq > INT32_MAX / 4) return MLA_ERR_SHAPE;
   if ((int64_t)p->batch * p->block_table_stride > INT32_MAX) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
@@ -118,7 +118,7 @@ int32_t plan_shape(const mla_problem_t* problem, const mla_plan_options_t* o, in
   const int64_t units = (int64_t)p->batch * rsplit;
   if (fixed > 0) {
     // one workgroup per chunk of `fixed` blocks, at most ceil(max_blocks / fixed) per unit
-    const int64_t g = units * ((p->max_blocks_per_seq + fixed - 1) / fixed);
+    const int64_t g = units * (((int64_t)p->max_blocks_per_seq + fixed - 1) / fixed);
     if (g > 65536) return MLA_ERR_SHAPE;
     grid = (int)(g > 0 ? g : 1);
   }
