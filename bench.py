@@ -14,9 +14,9 @@ step before it.
 Timed passes hold the stream with a short spin kernel while the host enqueues the
 whole pass, so the device runs the steps back to back: the figures are device time,
 with no host enqueue gaps inside them (a serving loop gets the same by enqueueing
-ahead or replaying a captured graph).  A second pass, after its own settling steps,
-records events around each launch of every step for the per-kernel durations (plan,
-decode, combine).
+ahead or replaying a captured graph).  The planner and the combine are then timed in
+passes of their own (back to back, after settling steps), and the decode kernel's
+duration is the step's remainder.
 
 Prints one JSON line: throughput in TFLOP/s (algorithmic FLOPs: 2*(576+512) per
 visible key per query row), KV GB/s, roofline fractions, the decode kernel's own
@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 METRIC = "MLA decode TFLOP/s + KV GB/s (% roofline), 128 heads, B=64, seqlen 4096"
 DECODE_KERNEL = "mla_decode_bf16_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_h128_l4096_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_%s_traffic.json")   # per workload name
 
 
 def workload_sizes(case, indices=None):
@@ -63,11 +63,11 @@ def workload_sizes(case, indices=None):
     return flops, kv_bytes, kv_bytes + other
 
 
-def traffic_from_profile():
-    """HBM bytes per decode launch from the committed counter profile, if it was taken
-    on the current kernel source; else None."""
+def traffic_from_profile(workload):
+    """HBM bytes per decode launch from the workload's committed counter profile, if it was
+    taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE % workload) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -242,33 +242,39 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
 
-    # Per-launch durations from HIP events on the launch stream, in a pass of its own:
-    # `steps` settling steps, then `steps` steps with events around each launch.
-    kernel_ms = None
-    kernel_us_pct = None
-    launches = None
+    # Per-kernel durations.  Events between the launches of a step would change them (each
+    # timing event is a stream packet that waits for and releases the work before it, and
+    # the kernel after it starts cold), so the planner and the combine are timed in passes
+    # of their own, `steps` launches back to back between two events, each pass after
+    # `settle` whole untimed steps; the decode's duration is the step's remainder:
+    # ms_per_step - plan - combine (launch gaps inside a held stream are under 1 us).
+    # A kernel trace of the same command agrees with it (the timed steps' dispatches).
     settle = max(args.steps, 20)
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    hold(settle + args.steps)
-    for i in range(settle):
-        step(i)
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    pct = lambda v, f: v[min(len(v) - 1, int(f * len(v)))] * 1e3
-    dec_ms = sorted(ev[1].elapsed_time(ev[2]) for ev in evs)
-    kernel_ms = sum(dec_ms) / len(dec_ms)
-    kernel_us_pct = {"p10": round(pct(dec_ms, 0.1), 2), "p50": round(pct(dec_ms, 0.5), 2),
-                     "p90": round(pct(dec_ms, 0.9), 2)}
-    launches = {"decode_us": round(kernel_ms * 1e3, 2)}
+
+    def timed_pass(fn):
+        torch.cuda.synchronize()
+        hold(settle + args.steps)
+        for i in range(settle):
+            step(i)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        p1.record(stream)
+        torch.cuda.synchronize()
+        return p0.elapsed_time(p1) / args.steps
+
     if split:
-        plan_ms = sum(ev[0].elapsed_time(ev[1]) for ev in evs) / len(evs)
-        comb_ms = sum(ev[2].elapsed_time(ev[3]) for ev in evs) / len(evs)
-        step_ev = sum(ev[0].elapsed_time(ev[3]) for ev in evs) / len(evs)
-        launches.update({"plan_us": round(plan_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
-                         "step_with_events_us": round(step_ev * 1e3, 2),
-                         "sum_le_step": bool(plan_ms + kernel_ms + comb_ms <= ms_per_step * 1.02)})
+        plan_ms = timed_pass(lambda i: dec.plan_for(lens, stream))
+        plan = dec.plan_for(lens, stream)
+        comb_ms = timed_pass(lambda i: mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks))
+        kernel_ms = ms_per_step - plan_ms - comb_ms
+        launches = {"method": "decode = step - plan - combine; plan and combine timed in passes of their own",
+                    "decode_us": round(kernel_ms * 1e3, 2), "plan_us": round(plan_ms * 1e3, 2),
+                    "combine_us": round(comb_ms * 1e3, 2), "step_us": round(ms_per_step * 1e3, 2)}
+    else:
+        kernel_ms = ms_per_step
+        launches = {"method": "decode = step (one launch per step)", "decode_us": round(kernel_ms * 1e3, 2)}
 
     t = ms_per_step * 1e-3
     tflops = flops / t / 1e12
@@ -280,9 +286,9 @@ def main():
     if kernel_ms is not None:
         achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(CONFIGS[args.config]["name"]),
                     "kernel": DECODE_KERNEL if split else "mla_decode_f32_kernel", "kernel_ms": round(kernel_ms, 5),
-                    "kernel_us_per_launch": kernel_us_pct, "algorithmic_bytes_per_launch": total_bytes}
+                    "algorithmic_bytes_per_launch": total_bytes}
 
     probe = None
     if not args.no_probe:

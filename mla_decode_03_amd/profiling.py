@@ -9,6 +9,10 @@
         (bench.py reports the figure only while that hash matches).
     python -m mla_decode_03_amd.profiling stats KERNEL_STATS_CSV
         Markdown table of a --kernel-trace --stats run (calls, average/min/max us).
+    python -m mla_decode_03_amd.profiling trace KERNEL_TRACE_CSV --steps K --warmup W
+        Per-kernel durations of a traced `bench.py --steps K --warmup W` run: over every
+        dispatch, and over the dispatches of the K timed steps (what bench.py's step time
+        and its decode figure, step minus planner minus combine, cover).
     python -m mla_decode_03_amd.profiling counters CSV [CSV ...]
         Median per dispatch of every counter in SQ/TCC passes, per kernel.
 """
@@ -99,6 +103,40 @@ def stats(path):
                                                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
 
 
+def trace(path, steps, warmup, decode=DECODE_KERNEL):
+    """Markdown table of per-kernel durations from a kernel-trace CSV of a `bench.py
+    --steps K --warmup W` run: over every dispatch, and over the dispatches of the K timed
+    steps (the W+1st .. W+Kth decode launches and, in launch order, the dispatch just
+    before and just after each: that step's planner and combine).
+    Returns {kernel: {"all": us, "timed": us}}."""
+    allds = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            allds.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    allds.sort()
+    dec_pos = [i for i, d in enumerate(allds) if decode in d[2]]
+    timed = set()
+    if len(dec_pos) >= warmup + steps:
+        for p in dec_pos[warmup:warmup + steps]:
+            timed.update(q for q in (p - 1, p, p + 1) if 0 <= q < len(allds))
+    per = collections.defaultdict(lambda: ([], []))
+    for i, (b, e, name) in enumerate(allds):
+        per[name][0].append((e - b) / 1e3)
+        if i in timed:
+            per[name][1].append((e - b) / 1e3)
+    print("| kernel | calls | avg us | timed steps: calls | timed steps: avg us |")
+    print("|---|---|---|---|---|")
+    res = {}
+    for name, (us, tus) in sorted(per.items(), key=lambda kv: -len(kv[1][0])):
+        short = name.split("(")[0].replace("void ", "").replace("mla::", "")
+        res[short] = {"all": sum(us) / len(us)}
+        if tus:
+            res[short]["timed"] = sum(tus) / len(tus)
+        print("| %s | %d | %.2f | %d | %s |" % (short, len(us), sum(us) / len(us), len(tus),
+                                                "%.2f" % (sum(tus) / len(tus)) if tus else "-"))
+    return res
+
+
 def counters(paths):
     for path in paths:
         tab = _per_dispatch(path)
@@ -122,6 +160,10 @@ def main(argv=None):
     t.add_argument("--out")
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--steps", type=int, required=True)
+    tr.add_argument("--warmup", type=int, required=True)
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")
     a = ap.parse_args(argv)
@@ -129,6 +171,8 @@ def main(argv=None):
         traffic(a.fetch_csv, a.write_csv, a.copy_bytes, a.out)
     elif a.cmd == "stats":
         stats(a.csv)
+    elif a.cmd == "trace":
+        trace(a.csv, a.steps, a.warmup)
     else:
         counters(a.csv)
 

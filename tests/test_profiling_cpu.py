@@ -44,3 +44,28 @@ def test_traffic_scales_by_copy(tmp_path):
 def test_kernel_source_hash_is_stable():
     assert profiling.kernel_source_hash() == profiling.kernel_source_hash()
     assert len(profiling.kernel_source_hash()) == 16
+
+
+def test_trace_picks_the_timed_steps(tmp_path, capsys):
+    """The timed steps are the W+1st .. W+Kth decode launches with the launch just before
+    (the planner) and just after (the combine) each, in start order whatever the file order."""
+    path = tmp_path / "t_kernel_trace.csv"
+    W, K = 2, 3
+    rows, t = [], 0
+    for step in range(W + K + 4):                # warm-up, timed, then settling steps
+        timed = W <= step < W + K
+        for name, d in (("void mla::mla_plan_kernel<true>(int)", 10 if timed else 1),
+                        ("void mla::mla_decode_bf16_kernel<4, false>(mla::DecodeArgs)", 100 if timed else 7),
+                        ("void mla::mla_combine_kernel(mla::CombineArgs)", 20 if timed else 3)):
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + 1000 * d})
+            t += 1000 * d + 500
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in reversed(rows):
+            w.writerow(r)
+    res = profiling.trace(str(path), K, W)
+    assert res["mla_decode_bf16_kernel<4, false>"]["timed"] == 100.0
+    assert res["mla_plan_kernel<true>"]["timed"] == 10.0
+    assert res["mla_combine_kernel"]["timed"] == 20.0
+    assert "| mla_combine_kernel | 9 |" in capsys.readouterr().out
