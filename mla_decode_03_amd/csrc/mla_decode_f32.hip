@@ -1,120 +1,176 @@
-// Plain float32 MLA decode (one wave per query row).
+// Float32 MLA decode on the fp32 matrix cores (v_mfma_f32_32x32x2_f32).
 //
-// Serves float32 problems, where speed is not the point: every step is the
-// definition done directly on the vector ALUs.  Per 64-token page, lane j scores
-// token p0 + j (a 576-long dot product against the q row held in LDS, in four
-// interleaved partial sums), the wave
-// takes the running max / sum by shuffles (online softmax, natural exp), and then
-// every lane accumulates 8 of the 512 value dims over the page's tokens.
+// Serves float32 problems, where speed is not the point but the arithmetic is the
+// decode's own: both products of the TileLang notes' FlashMLA example (S = Q K^T, then
+// O = P V; "A complete example: two-stage optimisation of FlashMLA") run on 32x32
+// matrix tiles with fp32 inputs and fp32 accumulation.  One workgroup (4 waves) takes one
+// sequence's rows in tiles of 32, and walks its keys 32 at a time:
+//   1. the 32 keys' 576-float rows go into LDS (masked keys as zeros);
+//   2. S^T (32 keys x 32 rows) = K . Q^T: wave w takes dims 144w .. 144w+143 (72
+//      two-dim MFMA steps, its Q fragments held in registers) and the four partial
+//      tiles are summed through LDS;
+//   3. one thread per row updates the row's running max and sum (online softmax,
+//      natural exp) and writes the chunk's weights P into LDS;
+//   4. O^T (512 values x 32 rows) += V^T . P^T: wave w takes value tiles 4w .. 4w+3
+//      (16 two-key steps each), after scaling its accumulators by the rows' factor.
+// The MFMA tile layout (32x32 result, 16 registers per lane): lane l holds column l%32,
+// rows 8(i/4) + 4(l/32) + i%4 of register i; an A or B operand element sits in lane
+// (row or column) + 32 * (k index).
 #include "mla_args.h"
 #include "mla_device.h"
 
 namespace mla {
 
+constexpr int kF32Tile = 32;                   // rows per tile, keys per chunk
+constexpr int kF32DimsPerWave = kDqk / 4;      // 144
+// LDS row pitch of a key row (floats): 16-byte aligned rows, and the 32 rows of a score
+// step's A operand spread over the banks (a 576-float pitch would put them in one)
+constexpr int kF32Pitch = kDqk + 4;
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-__global__ __launch_bounds__(256) void mla_decode_f32_kernel(F32Args a) {
-  __shared__ __attribute__((aligned(16))) float qs[4][kDqk];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int chunks = (a.rows + 3) / 4;
-  const int b = blockIdx.x / chunks;
-  const int r = (blockIdx.x % chunks) * 4 + w;
-  if (r >= a.rows) return;  // whole wave leaves; no workgroup barrier below
-  const float* qrow = a.q + ((size_t)b * a.rows + r) * kDqk;
-  for (int d = l; d < kDqk; d += 64) qs[w][d] = qrow[d];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0);
+__global__ __launch_bounds__(256, 1) void mla_decode_f32_kernel(F32Args a) {
+  __shared__ __attribute__((aligned(16))) float kc[kF32Tile][kF32Pitch];  // the chunk's key rows
+  __shared__ float sp[4][16][64];                                         // partial S tiles, per wave
+  __shared__ float pt[kF32Tile][kF32Tile + 1];                            // P [key][row]
+  __shared__ float alpha_s[kF32Tile];                                     // rows' rescale factors
+  __shared__ int poison_s;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int tiles = (a.rows + kF32Tile - 1) / kF32Tile;
+  const int b = blockIdx.x / tiles;
+  const int row0 = (blockIdx.x % tiles) * kF32Tile;
+  const int col = l & 31, kh = l >> 5;          // operand element: row/column, k index
 
   const int L = a.seqlens[b];
   bool poison = (L < 0) || ((int64_t)L > (int64_t)kPage * a.max_blocks);
-  int n = poison ? 0 : L;
-  if (a.causal && a.q_len > 1) n = n - a.q_len + 1 + r / a.heads;
-  n = max(n, 0);
+  const int Lc = poison ? 0 : L;
+  // the most keys any row of the tile sees (causal rows see fewer)
+  auto visible = [&](int r) {
+    int n = Lc;
+    if (a.causal && a.q_len > 1) n = n - a.q_len + 1 + r / a.heads;
+    return max(n, 0);
+  };
+  const int nmax = visible(min(row0 + kF32Tile, a.rows) - 1);
 
-  float m = -INFINITY, lsum = 0.f, o[8];
+  // this wave's Q fragments: B operand of step j (dims 144w + 2j + kh), row row0 + col
+  float qf[kF32DimsPerWave / 2];
+  {
+    const int r = row0 + col;
+    const float* qrow = a.q + ((size_t)b * a.rows + (r < a.rows ? r : row0)) * kDqk + kF32DimsPerWave * w + kh;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  for (int p0 = 0; p0 < n; p0 += kPage) {
+    for (int j = 0; j < kF32DimsPerWave / 2; ++j) qf[j] = r < a.rows ? qrow[2 * j] : 0.f;
+  }
+  // softmax state of row row0 + t (threads 0..31)
+  float m_run = -INFINITY, l_run = 0.f;
+  const int nvis_t = visible(row0 + (t < kF32Tile ? t : 0));
+  f32x16 o[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[v][i] = 0.f;
+  if (t == 0) poison_s = 0;
+
+  for (int p0 = 0; p0 < nmax; p0 += kF32Tile) {
+    __syncthreads();   // the previous chunk's reads of kc and pt are done
+    // 1. key rows p0 .. p0+31 (one page holds them: pages are 64 keys, chunks 32-aligned)
     const int page = a.block_table[(size_t)b * a.bt_stride + p0 / kPage];
-    if (page < 0 || page >= a.num_pages) { poison = true; break; }
-    const float* pbase = a.kv + (size_t)page * kPage * kDqk;
-    const bool valid = p0 + l < n;
-    float s = -INFINITY;
-    if (valid) {
-      // 16-byte loads and four independent partial sums (one per vector component), so
-      // the 576-term dot product is not one dependent chain of scalar loads and FMAs
-      const f32x4* krow = (const f32x4*)(pbase + (size_t)l * kDqk);
-      const f32x4* qv = (const f32x4*)qs[w];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool bad = page < 0 || page >= a.num_pages;
+    if (bad && t == 0) poison_s = 1;
+    const float* base = a.kv + (size_t)(bad ? 0 : page) * kPage * kDqk + (size_t)(p0 % kPage) * kDqk;
+    const int nkeys = min(kF32Tile, nmax - p0);
+    for (int e = t; e < kF32Tile * kDqk / 4; e += 256) {
+      const int k = e / (kDqk / 4), d4 = e % (kDqk / 4);
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (k < nkeys && !bad) v = *(const f32x4*)(base + (size_t)k * kDqk + 4 * d4);
+      *(f32x4*)&kc[k][4 * d4] = v;
+    }
+    __syncthreads();
+    // 2. partial S^T over this wave's dims
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kF32DimsPerWave / 2; ++j)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[col][kF32DimsPerWave * w + 2 * j + kh], qf[j], s, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sp[w][i][l] = s[i];
+    __syncthreads();
+    // 3. softmax update, one thread per row: key k of the chunk is register i = 4(k/8) + k%4
+    // of lane 32(k/4 % 2) + row
+    if (t < kF32Tile) {
+      const int r = t;
+      float sv[kF32Tile];
+      float mx = m_run;
+#pragma unroll
+      for (int k = 0; k < kF32Tile; ++k) {
+        const int i = 4 * (k >> 3) + (k & 3), ln = 32 * ((k >> 2) & 1) + r;
+        float x = (sp[0][i][ln] + sp[1][i][ln]) + (sp[2][i][ln] + sp[3][i][ln]);
+        x = (p0 + k < nvis_t) ? x * a.scale : -INFINITY;
+        sv[k] = x;
+        mx = fmaxf(mx, x);
+      }
+      // nothing visible yet: keep the shift at 0 so exp(-inf - 0) = 0
+      const float ms = mx == -INFINITY ? 0.f : mx;
+      const float al = m_run == -INFINITY ? 0.f : expf(m_run - ms);
+      float ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < kF32Tile; ++k) {
+        const float p = expf(sv[k] - ms);
+        pt[k][r] = p;
+        ls += p;
+      }
+      l_run = l_run * al + ls;
+      m_run = mx;
+      alpha_s[r] = al;
+    }
+    __syncthreads();
+    // 4. O^T += V^T . P^T over the chunk's 32 keys, value tiles 4w .. 4w+3
+    const float al = alpha_s[col];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[v][i] *= al;
 #pragma unroll 4
-      for (int d = 0; d < kDqk / 4; ++d) {
-        const f32x4 kq = krow[d], qq = qv[d];
-        acc[0] = fmaf(qq[0], kq[0], acc[0]);
-        acc[1] = fmaf(qq[1], kq[1], acc[1]);
-        acc[2] = fmaf(qq[2], kq[2], acc[2]);
-        acc[3] = fmaf(qq[3], kq[3], acc[3]);
-      }
-      s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale;
-    }
-    const float mn = fmaxf(m, wave_max(s));
-    const float alpha = expf(m - mn);
-    const float pw = valid ? expf(s - mn) : 0.f;
-    lsum = lsum * alpha + wave_sum(pw);
-    m = mn;
+    for (int ks = 0; ks < kF32Tile / 2; ++ks) {
+      const float pb = pt[2 * ks + kh][col];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-    const int cnt = min(kPage, n - p0);
-    // token k's weight from lane k (a scalar read: k is uniform); eight tokens at a time,
-    // so that their value rows are in flight together
-    int k = 0;
-    for (; k + 8 <= cnt; k += 8) {
-      float wk[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) wk[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), k + u));
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* vrow = pbase + (size_t)(k + u) * kDqk;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = fmaf(wk[u], vrow[l + 64 * i], o[i]);
-      }
-    }
-    for (; k < cnt; ++k) {
-      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), k));
-      const float* vrow = pbase + (size_t)k * kDqk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = fmaf(wk, vrow[l + 64 * i], o[i]);
+      for (int v = 0; v < 4; ++v)
+        o[v] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[2 * ks + kh][128 * w + 32 * v + col], pb, o[v], 0, 0, 0);
     }
   }
-  if (poison && a.err && l == 0) *a.err = 1;   // the plan's fault flag, when there is a plan
-  const bool empty = lsum == 0.f;  // no visible key; NaN propagates
-  float inv = poison ? __builtin_nanf("") : (empty ? 0.f : 1.f / lsum);
-  float lse_v = poison ? __builtin_nanf("") : (empty ? -INFINITY : m + logf(lsum));
-  if (a.sinks && !poison) {   // attention sink: one more softmax term, zero value row
-    const SinkFold f = fold_sink<false>(m, lsum, a.sinks[r % a.heads]);
-    inv = f.scale_o;
-    lse_v = f.lse;
+  __syncthreads();
+  poison = poison || poison_s;
+  if (poison && a.err && t == 0) *a.err = 1;   // the plan's fault flag, when there is a plan
+  // row factors and LSE, then the output: O^T register i of lane l is value
+  // 128w + 32v + 8(i/4) + 4(l/32) + i%4 of row row0 + l%32
+  if (t < kF32Tile) {
+    const bool empty = l_run == 0.f;  // no visible key; NaN propagates
+    float inv = poison ? __builtin_nanf("") : (empty ? 0.f : 1.f / l_run);
+    float lse_v = poison ? __builtin_nanf("") : (empty ? -INFINITY : m_run + logf(l_run));
+    if (a.sinks && !poison && row0 + t < a.rows) {   // attention sink: one more term, zero value row
+      const SinkFold f = fold_sink<false>(m_run, l_run, a.sinks[(row0 + t) % a.heads]);
+      inv = f.scale_o;
+      lse_v = f.lse;
+    }
+    alpha_s[t] = inv;
+    if (row0 + t < a.rows) a.lse[(size_t)b * a.rows + row0 + t] = lse_v;
   }
-  float* orow = a.out + ((size_t)b * a.rows + r) * kDv;
+  __syncthreads();
+  const int r = row0 + col;
+  if (r < a.rows) {
+    const float inv = alpha_s[col];
+    float* orow = a.out + ((size_t)b * a.rows + r) * kDv + 128 * w + 4 * kh;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) orow[l + 64 * i] = o[i] * inv;
-  if (l == 0)
-    a.lse[(size_t)b * a.rows + r] = lse_v;
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)(orow + 32 * v + 8 * q) =
+            f32x4{o[v][4 * q] * inv, o[v][4 * q + 1] * inv, o[v][4 * q + 2] * inv, o[v][4 * q + 3] * inv};
+  }
 }
 
 }  // namespace mla
 
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_f32(const mla::F32Args* args, hipStream_t stream) {
-  const int grid = args->batch * ((args->rows + 3) / 4);
+  const int grid = args->batch * ((args->rows + mla::kF32Tile - 1) / mla::kF32Tile);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(mla::mla_decode_f32_kernel, dim3(grid), dim3(256), 0, stream, *args);
   return hipGetLastError();

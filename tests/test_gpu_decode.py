@@ -32,6 +32,23 @@ def test_config0_fp32_full():
     assert s["max_abs"] < 1e-4  # fp32 path: far inside the bf16 tolerance
 
 
+@pytest.mark.parametrize("B,T,H,lens,causal", [
+    (4, 1, 128, [1, 31, 32, 33], False),          # four row tiles; chunk tails
+    (3, 1, 48, [64, 65, 1000], False),            # a part-filled row tile
+    (2, 2, 64, [0, 97], True),                    # causal q_len 2, an empty sequence
+    (1, 1, 16, [4096], False),
+])
+def test_fp32_matrix_core_shapes(B, T, H, lens, causal):
+    """The fp32 path on the fp32 matrix cores: 32-row tiles (part-filled ones too), 32-key
+    chunks with ragged tails, causal rows, empty sequences."""
+    case = _case(B, T, H, lens, seed=40 + B + H, causal=causal, dtype="f32")
+    say("fp32 mfma", B, T, H, lens, causal)
+    ref_o, ref_l = oracle_rows(case)
+    o, l, _ = run(case)
+    s = compare(o, l, ref_o, ref_l, "fp32 %dx%dx%d" % (B, T, H))
+    assert s["max_abs"] < 1e-4 and s["max_lse"] < 1e-5
+
+
 SMALL = [
     # (B, T, H, lens, causal): token counts crossing page edges; every row/wave layout
     (2, 1, 128, [1, 70], False),
