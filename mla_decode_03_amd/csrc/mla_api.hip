@@ -4,6 +4,7 @@
 // checks out of Python into compiled host code).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -92,12 +93,17 @@ struct PlanShape {
 };
 
 // Cost-model overhead of one segment (a unit's rows decoded by one workgroup) besides
-// its KV blocks, in quarter blocks: the traffic of its Q rows (1152 B each) and its
-// output or partial rows (1024 B + a 4 B LSE each) over a block's 73,728 B, rounded
-// to the nearest quarter.  128 rows give 15 (3.75 blocks).
+// its KV blocks, in quarter blocks: the step-time model's per-segment time over its time
+// per block at this row count, the larger of a block's HBM time and its MFMA time (the
+// TileLang notes' tile recommender in its roofline form, "Key design 2: tile
+// recommendation").  The three times, in hundredths of a microsecond, were measured by
+// fitting the model to plan sweeps on MI355X (mla_decode_03_amd.tune fit): 7.61 us per
+// segment, 2.31 us per block from HBM, 2.86 us per block of MFMA work at 128 rows.
+// 128 rows give 11 quarters, 64 or fewer 13.
+constexpr int64_t kSegHundredthsUs = 761, kBlkMemHundredthsUs = 231, kBlkMfma128HundredthsUs = 286;
 int segment_cost_quarters(int rows_per_wg) {
-  const int64_t bytes = (int64_t)rows_per_wg * (1152 + 1024 + 4);
-  return (int)((4 * bytes + mla::kPage * mla::kDqk * 2 / 2) / (mla::kPage * mla::kDqk * 2));
+  const int64_t blk = std::max<int64_t>(kBlkMemHundredthsUs * 128, kBlkMfma128HundredthsUs * (int64_t)rows_per_wg);
+  return (int)((4 * kSegHundredthsUs * 128 + blk / 2) / blk);
 }
 
 int32_t plan_shape(const mla_problem_t* problem, const mla_plan_options_t* o, int32_t num_cus, PlanShape* s) {

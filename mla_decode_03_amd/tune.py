@@ -1,30 +1,33 @@
-"""Offline sweep of the split planner's options: measured step time against the cost model.
+"""Offline sweep of the split planner's options: measured step time against the step-time model.
 
-    python -m mla_decode_03_amd.tune --config 1 [--steps 40] [--out table.md]
+    python -m mla_decode_03_amd.tune --config 1 [--steps 40] [--out table.md] [--dump sweep.json]
+    python -m mla_decode_03_amd.tune fit sweep1.json sweep2.json ... [--out profiles/plan_cost_model.json]
 
 For one seeded workload, every candidate plan (split rule x workgroup count x row split x
 smallest share, plus the batch-invariant fixed-chunk plans) is made by the device planner
 and timed as the whole decode path (plan, split decode, combine) with HIP events, two KV
 pools alternated as in the benchmark, in round-robin passes (a new seeded order each pass)
-after a settling run; the median over passes is reported.  Beside each time stands the planner's own cost model
-applied to the plan it made: the TileLang notes' tile recommender ranks candidates by
-traffic over bandwidth ("Key design 2: tile recommendation"), and here a workgroup costs 4
-quarter blocks per 64-token block it streams plus the per-segment overhead (the header's
-segment cost, or for fixed-chunk plans the default one) for each unit it touches.  Workgroups are dealt to the CUs in launch order,
-each taking the first CU to come free (one resident workgroup per CU), and the busiest CU's
-total is the predicted time.  The report gives the rank agreement of prediction and
+after a settling run; the median over passes is reported.  Beside each time stands the
+step-time model's prediction for the plan (see PARAM_NAMES below: the TileLang notes' tile
+recommender, "Key design 2: tile recommendation", in its roofline form: per block the larger
+of memory and MFMA time, plus intrinsic per-segment and per-step terms; workgroups dealt to
+XCDs and CUs in launch order).  The report gives the rank agreement of prediction and
 measurement, and where the default plan (cost model picks the rule, one workgroup per CU)
-lands.  Every candidate's output is compared with the default plan's.
+lands.  Every candidate's output is compared with the default plan's.  `fit` measures the
+model's parameters from sweep dumps, with the rank agreement of each workload also checked
+with that workload left out of the fit.
 """
 from __future__ import annotations
 
 import argparse
 import heapq
 import json
+import os
 import sys
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HDR_WORDS = 16
 HDR_ROW_SPLIT, HDR_ROWS_PER_WG, HDR_NUM_WG, HDR_GRID_WG, HDR_RULE, HDR_SEG_COST = 3, 4, 5, 6, 12, 15
 RULE_NAMES = {1: "pages", 2: "cost", 3: "fixed"}
@@ -40,39 +43,117 @@ def plan_arrays(words: np.ndarray, batch: int):
     return words[:HDR_WORDS], cu, words[wg0:wg0 + grid + 1].astype(np.int64)
 
 
-def workgroup_costs(words: np.ndarray, batch: int) -> np.ndarray:
-    """Cost of each launched workgroup in quarter blocks: 4 per block of its range plus the
-    segment cost per unit the range touches (0 for a workgroup without work)."""
+# The step-time model, in the form of the TileLang notes' tile recommender ("Key design
+# 2: tile recommendation"): a kernel's time is the largest of its traffic over bandwidth
+# and its compute over throughput, plus an intrinsic term for launch, prologue and
+# epilogue.  For the split decode:
+#   block     each 64-token KV block a workgroup streams takes max(t_mem, t_mfma * R / 128):
+#             the HBM time of its 73,728 B at one CU's share of the stream, or the MFMA time
+#             of its two products for R rows (R = rows per workgroup);
+#   segment   each unit a workgroup touches adds t_seg (its Q rows and first pages in, its
+#             output or partial rows out);
+#   launch    workgroups go to the XCDs in launch order (index i to XCD i mod 8, the
+#             decode's own numbering maps it to a logical workgroup) and there to the CU
+#             that comes free first; the decode ends with the busiest CU;
+#   step      + t_fix (the planner, the launches, the combine's fixed part)
+#             + t_part * R / 128 per partial segment the combine merges.
+# The parameters are measured: fitted (least squares on log time) to the sweep's timings,
+# the figures in profiles/plan_cost_model.json.
+PARAM_NAMES = ("t_mem", "t_mfma", "t_seg", "t_fix", "t_part")
+MODEL_FILE = os.path.join(ROOT, "profiles", "plan_cost_model.json")
+
+
+def plan_segments(words: np.ndarray, batch: int):
+    """Per launched workgroup, its segments as (blocks, split) pairs (split: the unit is cut
+    across workgroups, so this segment writes a partial); rows per workgroup."""
     hdr, cu, wg_begin = plan_arrays(words, batch)
-    rs, num_wg, c = int(hdr[HDR_ROW_SPLIT]), int(hdr[HDR_NUM_WG]), int(hdr[HDR_SEG_COST])
-    if c == 0:   # fixed-chunk plans record none: the default, a segment's rows at 2180 B each
-        c = (4 * int(hdr[HDR_ROWS_PER_WG]) * 2180 + 36864) // 73728   # over a 73,728 B block
+    rs, num_wg = int(hdr[HDR_ROW_SPLIT]), int(hdr[HDR_NUM_WG])
     nb = np.diff(cu)
-    # start of every non-empty unit on the concatenated block axis (sequence-major)
-    starts = np.array([rs * cu[b] + g * nb[b] for b in range(batch) if nb[b] > 0 for g in range(rs)],
-                      dtype=np.int64)
-    cost = np.zeros(len(wg_begin) - 1, dtype=np.int64)
-    for w in range(min(num_wg, len(cost))):
+    starts, lens = [], []
+    for b in range(batch):
+        if nb[b] > 0:
+            for g in range(rs):
+                starts.append(rs * cu[b] + g * nb[b])
+                lens.append(nb[b])
+    starts = np.array(starts, dtype=np.int64)
+    out = []
+    for w in range(len(wg_begin) - 1):
         lo, hi = wg_begin[w], wg_begin[w + 1]
-        if hi <= lo:
-            continue
-        first = np.searchsorted(starts, lo, side="right") - 1
-        last = np.searchsorted(starts, hi - 1, side="right") - 1
-        cost[w] = 4 * (hi - lo) + c * (last - first + 1)
-    return cost
+        segs = []
+        if w < num_wg and hi > lo:
+            i = int(np.searchsorted(starts, lo, side="right")) - 1
+            while i < len(starts) and starts[i] < hi:
+                s0, s1 = max(lo, starts[i]), min(hi, starts[i] + lens[i])
+                segs.append((int(s1 - s0), bool(s0 > starts[i] or s1 < starts[i] + lens[i])))
+                i += 1
+        out.append(segs)
+    return out, int(hdr[HDR_ROWS_PER_WG])
 
 
-def makespan(costs: np.ndarray, num_cus: int) -> int:
-    """Busiest CU when the grid's workgroups are started in launch order, each on the first CU
-    to come free.  Launch index i runs logical workgroup (i mod 8) * (G / 8) + i div 8 when the
-    grid G is a multiple of 8 (the decode's XCD-aware numbering), else i."""
+def dispatch(costs, num_cus: int) -> float:
+    """Busiest CU when launch index i goes to XCD i mod 8 and there to the CU that comes free
+    first; launch index i runs logical workgroup (i mod 8) * (G / 8) + i div 8 when the grid
+    G is a multiple of 8 (the decode's XCD-aware numbering), else i."""
     G = len(costs)
-    order = ([(i & 7) * (G >> 3) + (i >> 3) for i in range(G)] if G % 8 == 0 else list(range(G)))
-    free = [0] * max(1, num_cus)
-    for w in order:
-        t = heapq.heappop(free)
-        heapq.heappush(free, t + int(costs[w]))
-    return max(free)
+    order = [(i & 7) * (G >> 3) + (i >> 3) for i in range(G)] if G % 8 == 0 else list(range(G))
+    xcds = [[0.0] * max(1, num_cus // 8) for _ in range(8)]
+    for i, w in enumerate(order):
+        h = xcds[i & 7]
+        t = heapq.heappop(h)
+        heapq.heappush(h, t + float(costs[w]))
+    return max(max(h) for h in xcds)
+
+
+def model_us(params: dict, words: np.ndarray, batch: int, num_cus: int) -> float:
+    """Predicted microseconds per step (planner + decode + combine) of a plan."""
+    segs, R = plan_segments(words, batch)
+    blk = max(params["t_mem"], params["t_mfma"] * R / 128.0)
+    costs = [sum(params["t_seg"] + n * blk for n, _ in s) for s in segs]
+    parts = sum(1 for s in segs for _, split in s if split)
+    return params["t_fix"] + dispatch(costs, num_cus) + params["t_part"] * parts * R / 128.0
+
+
+def load_params(path: str = MODEL_FILE) -> dict:
+    with open(path) as f:
+        return json.load(f)["params"]
+
+
+def fit(dumps, out=None):
+    """Fit the model's parameters to sweep dumps (`--dump` files): least squares on the log
+    of the step time over every candidate of every workload, and the rank agreement per
+    workload, with all workloads in the fit and with the workload left out of it."""
+    from scipy.optimize import least_squares
+    data = []
+    for path in dumps:
+        with open(path) as f:
+            d = json.load(f)
+        for c in d["candidates"]:
+            segs_R = np.array(c["words"], dtype=np.int64)
+            data.append((d["workload"], segs_R, d["batch"], d["num_cus"], c["us"]))
+    names = sorted({w for w, *_ in data}, key=lambda w: [x[0] for x in data].index(w))
+
+    def solve(rows):
+        def resid(p):
+            prm = dict(zip(PARAM_NAMES, p))
+            return [np.log(model_us(prm, wd, b, n)) - np.log(us) for _, wd, b, n, us in rows]
+        r = least_squares(resid, [2.5, 2.5, 6.0, 15.0, 0.1], bounds=([0.1] * 2 + [0.0] * 3, [50.0] * 2 + [100.0] * 3))
+        return dict(zip(PARAM_NAMES, (round(float(x), 4) for x in r.x))), float(np.sqrt(np.mean(np.square(r.fun))))
+
+    params, rms = solve(data)
+    report = {"params": params, "rms_log_error": round(rms, 4), "workloads": {}}
+    for w in names:
+        rows = [x for x in data if x[0] == w]
+        rho = spearman([model_us(params, wd, b, n) for _, wd, b, n, _ in rows], [us for *_, us in rows])
+        held, _ = solve([x for x in data if x[0] != w])
+        rho_held = spearman([model_us(held, wd, b, n) for _, wd, b, n, _ in rows], [us for *_, us in rows])
+        report["workloads"][w] = {"candidates": len(rows), "spearman": round(rho, 4),
+                                  "spearman_left_out_of_fit": round(rho_held, 4), "params_without_it": held}
+    text = json.dumps(report, indent=1)
+    if out:
+        with open(out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+    return report
 
 
 def spearman(x, y) -> float:
@@ -112,6 +193,14 @@ def candidates(rows: int):
 
 
 def main(argv=None):
+    argv = sys.argv[1:] if argv is None else argv
+    if argv and argv[0] == "fit":
+        fp = argparse.ArgumentParser(prog="tune fit", description="fit the step-time model to sweep dumps")
+        fp.add_argument("dumps", nargs="+")
+        fp.add_argument("--out", default=None)
+        fa = fp.parse_args(argv[1:])
+        fit(fa.dumps, fa.out)
+        return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--config", type=int, default=1, help="seeded workload index (bf16 ones: 1..4)")
     ap.add_argument("--steps", type=int, default=100, help="timed steps per candidate and round")
@@ -119,6 +208,7 @@ def main(argv=None):
     ap.add_argument("--rounds", type=int, default=5, help="round-robin passes; the median is reported")
     ap.add_argument("--settle", type=int, default=1000, help="untimed steps before the first round")
     ap.add_argument("--out", default=None, help="also write the table (markdown) here")
+    ap.add_argument("--dump", default=None, help="also write every candidate's plan words and times (JSON)")
     args = ap.parse_args(argv)
 
     import torch
@@ -175,6 +265,7 @@ def main(argv=None):
             times[k].append(time_steps(run, args.steps))
         print("round %d of %d done" % (r + 1, args.rounds), flush=True)
 
+    params = load_params() if os.path.exists(MODEL_FILE) else None
     ref_out = runs[0][2].float()
     results = []
     for k, (label, dec, out, lse) in enumerate(runs):
@@ -186,28 +277,31 @@ def main(argv=None):
             raise RuntimeError("%s: output differs from the default plan's beyond tolerance" % label)
         rec = {"label": label, "rule": RULE_NAMES.get(int(words[HDR_RULE]), "?"),
                "row_split": int(words[HDR_ROW_SPLIT]), "num_wg": int(words[HDR_NUM_WG]),
-               "grid_wg": int(words[HDR_GRID_WG]), "model": makespan(workgroup_costs(words, B), num_cus),
+               "grid_wg": int(words[HDR_GRID_WG]),
+               "model": round(model_us(params, words, B, num_cus), 2) if params else float("nan"),
                "us": round(float(np.median(times[k])), 2), "spread_us": round(max(times[k]) - min(times[k]), 2),
                "max_abs_vs_default": float(d.max())}
         results.append(rec)
         print(json.dumps(rec), flush=True)
+        rec["times_us"] = [round(x, 3) for x in times[k]]
+        rec["words"] = words.tolist()
 
     best = min(results, key=lambda r: r["us"])
     default = results[0]
     rank = 1 + sum(r["us"] < default["us"] for r in results)
     rho = spearman([r["model"] for r in results], [r["us"] for r in results])
-    by_model = min(results, key=lambda r: (r["model"], r["us"]))
+    by_model = min(results, key=lambda r: r["model"])   # the first of equal predictions, in sweep order
     lines = ["Workload: %s (%d candidate plans; µs per step = planner + decode + combine, median of %d "
              "shuffled round-robin rounds of %d timed steps)" % (CONFIGS[args.config]["name"], len(results), args.rounds,
                                                           args.steps), "",
              "Default plan: %.2f µs, rank %d of %d; fastest: %s at %.2f µs (default / fastest = %.3f)."
              % (default["us"], rank, len(results), best["label"], best["us"], default["us"] / best["us"]),
-             "Model's pick (lowest busiest-CU cost): %s at %.2f µs.  Spearman rank correlation of "
-             "model cost and measured time: %.3f." % (by_model["label"], by_model["us"], rho), "",
-             "| plan | rule used | row split | workgroups with work / launched | model (quarter blocks, busiest CU) "
+             "Model's pick (lowest predicted step time): %s at %.2f µs measured.  Spearman rank correlation "
+             "of predicted and measured time: %.3f." % (by_model["label"], by_model["us"], rho), "",
+             "| plan | rule used | row split | workgroups with work / launched | model (µs per step) "
              "| µs per step | spread over rounds | max abs diff vs default |", "|---|---|---|---|---|---|---|---|"]
     for r in sorted(results, key=lambda r: r["us"]):
-        lines.append("| %s | %s | %d | %d / %d | %d | %.2f | %.2f | %.3g |" % (
+        lines.append("| %s | %s | %d | %d / %d | %.1f | %.2f | %.2f | %.3g |" % (
             r["label"], r["rule"], r["row_split"], r["num_wg"], r["grid_wg"], r["model"], r["us"],
             r["spread_us"], r["max_abs_vs_default"]))
     text = "\n".join(lines)
@@ -215,6 +309,10 @@ def main(argv=None):
     if args.out:
         with open(args.out, "w") as f:
             f.write(text + "\n")
+    if args.dump:
+        with open(args.dump, "w") as f:
+            json.dump({"workload": CONFIGS[args.config]["name"], "config": args.config, "num_cus": num_cus,
+                       "batch": B, "rows": rows, "seqlens": case.cache_seqlens.tolist(), "candidates": results}, f)
 
 
 if __name__ == "__main__":

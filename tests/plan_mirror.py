@@ -11,8 +11,8 @@ units are laid end to end (sequence-major, then row slice) and the block range
 A workgroup costs 4 per block plus c per unit it touches; rule "auto" keeps the rule
 whose busiest workgroup costs less, pages on a tie.  It skips the comparison (and keeps
 pages, header costs 0) when every non-empty unit holds the same nb blocks and the equal
-shares line up with them (share a multiple of nb or nb of share).  c defaults to the traffic of a
-segment's rows: rows * 2180 B over 73,728 B per block, in quarters, rounded.  A unit cut
+shares line up with them (share a multiple of nb or nb of share).  c defaults to the step-time
+model's time per segment over its time per block at the row count, in quarters, rounded.  A unit cut
 across k > 1 workgroups owns k consecutive partial slots, numbered unit by unit.
 
 Written from the rules, not from the kernel: the workgroup holding a position is found
@@ -30,8 +30,11 @@ RULES = {"auto": 0, "pages": 1, "cost": 2, "fixed": 3}
 
 
 def segment_cost(rows_per_wg):
-    """Default per-segment overhead in quarter blocks (nearest)."""
-    return (4 * rows_per_wg * 2180 + 36864) // 73728
+    """Default per-segment overhead in quarter blocks (nearest): the step-time model's 7.61 us
+    per segment over its time per block, max(2.31 us from HBM, 2.86 us * rows / 128 of MFMA
+    work), in hundredths of a microsecond and integers."""
+    blk = max(231 * 128, 286 * rows_per_wg)
+    return (4 * 761 * 128 + blk // 2) // blk
 
 
 def make_plan(seqlens, *, row_split=1, grid_wg=256, min_blocks=4, max_blocks=1 << 30, fixed_blocks=0,

@@ -112,10 +112,11 @@ def test_aligned_even_batches_need_no_comparison(seed):
     assert plan_cost(auto, c) <= plan_cost(cost, c)
 
 
-def test_segment_cost_is_the_traffic_of_a_segments_rows():
-    # 128 rows move 128 * (1152 + 1024 + 4) B besides their KV: 3.78 blocks -> 15 quarters
-    assert segment_cost(128) == 15 and segment_cost(64) == 8 and segment_cost(32) == 4
-    assert segment_cost(16) == 2
+def test_segment_cost_is_the_models_segment_time_in_blocks():
+    # 7.61 us per segment; a block takes 2.86 us of MFMA work at 128 rows (MFMA-bound:
+    # 10.6 blocks -> 11 quarters) and 2.31 us from HBM at 64 rows or fewer (13.2 -> 13)
+    assert segment_cost(128) == 11 and segment_cost(64) == 13 and segment_cost(32) == 13
+    assert segment_cost(16) == 13 and segment_cost(104) == 13 and segment_cost(96) == 13
 
 
 def test_even_batches_keep_the_pages_cut_and_ragged_ones_take_the_cost_cut():
@@ -139,12 +140,12 @@ def test_headline_shape_splits_each_sequence_in_four():
 def test_small_problem_is_not_over_split_and_empty_batch():
     # 2 + 4 blocks with at least 4 per workgroup: two workgroups.  The pages rule cuts
     # at block 3 and splits the second sequence in two (busiest workgroup: 3 blocks and
-    # 2 segments, 12 + 2*15 = 42 quarters); the cost rule gives each sequence its own
-    # workgroup (busiest: 4 blocks and 1 segment, 31), so the cost model keeps that.
+    # 2 segments, 12 + 2*11 = 34 quarters); the cost rule gives each sequence its own
+    # workgroup (busiest: 4 blocks and 1 segment, 27), so the cost model keeps that.
     plan = make_plan([100, 200], grid_wg=256, min_blocks=4, rule="pages")
     assert plan["num_wg"] == 2 and plan["num_splits"] == [1, 2] and plan["num_partials"] == 2
     plan = make_plan([100, 200], grid_wg=256, min_blocks=4)
-    assert (plan["cost_pages"], plan["cost_balanced"]) == (42, 31)
+    assert (plan["cost_pages"], plan["cost_balanced"]) == (34, 27)
     assert plan["rule"] == 2 and plan["num_splits"] == [1, 1] and plan["num_partials"] == 0
     plan = make_plan([100, 200], grid_wg=256, min_blocks=8)
     assert plan["num_wg"] == 1 and plan["num_splits"] == [1, 1] and plan["num_partials"] == 0
