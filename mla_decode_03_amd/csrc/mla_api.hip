@@ -21,7 +21,8 @@ constexpr int kDefaultMinBlocks = 4;
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Split partials: the normalised output's bf16 high halves [slots, rows, 512], its low
-// halves [slots, rows, 512], the fp32 LSE [slots, rows] and the low-half flags [slots, rows].
+// halves [slots, rows, 512], the fp32 LSE [slots, rows] and the low-half flag words [slots, rows] (a bit per
+// quarter of the row).
 constexpr size_t kPartialRowBytes = 2 * mla::kDv * sizeof(uint16_t) + sizeof(float) + sizeof(int32_t);
 size_t partial_bytes(int64_t slots, int64_t rows_per_wg) {
   return (size_t)slots * rows_per_wg * kPartialRowBytes;

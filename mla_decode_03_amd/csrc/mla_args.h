@@ -16,9 +16,9 @@ struct DecodeArgs {
   float* lse;                  // [B, R]
   int32_t* meta;               // plan, or nullptr (one workgroup per sequence)
   uint16_t* ws_hi;             // split partials: normalised output rounded to bf16 [slots, rows_per_wg, 512]
-  uint16_t* ws_lo;             // bf16(output - hi) [slots, rows_per_wg, 512], written for flagged rows only
+  uint16_t* ws_lo;             // bf16(output - hi) [slots, rows_per_wg, 512], written for flagged quarters only
   float* ws_lse;               // partial log-sum-exp [slots, rows_per_wg]
-  int32_t* ws_flag;            // 1 where the row's low half was written [slots, rows_per_wg]
+  int32_t* ws_flag;            // bit q: values 128q .. 128q+127 of the row have a low half [slots, rows_per_wg]
   const float* sinks;          // attention-sink logits [heads], or nullptr
   const int32_t* sparse_rows;  // sparse: pool rows per unit [units, row_stride], or nullptr
   int sparse_stride;           // row_stride of sparse_rows (a multiple of 64)
@@ -30,7 +30,7 @@ struct DecodeArgs {
 struct CombineArgs {
   const int32_t* meta;
   const uint16_t* ws_hi;       // partial outputs, high halves (bf16)
-  const uint16_t* ws_lo;       // low halves, read where ws_flag is set
+  const uint16_t* ws_lo;       // low halves, read where ws_flag's quarter bit is set
   const float* ws_lse;
   const int32_t* ws_flag;
   uint16_t* out;    // bf16 [B, R, 512]

@@ -3,8 +3,9 @@
 // A unit (rows of one sequence) cut across k > 1 workgroups left k partial results
 // (o_s = normalised output over its key range, lse_s = natural-log sum of exp over
 // it).  o_s is stored as its bf16 rounding hi_s, plus lo_s = bf16(o_s - hi_s) for the
-// rows whose flag says the decode wrote it (rows with a large |o_s|), so each partial
-// reaches the merge within 0.0039 + 2^-16 |o_s| of its fp32 value.  Over the union of
+// quarters of a row (128 values each) whose flag bit says the decode wrote it (quarters
+// with a large |o_s|), so each partial reaches the merge within 0.0039 + 2^-16 |o_s| of
+// its fp32 value.  Over the union of
 // the disjoint ranges:
 //     lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s
 //     out = sum_s exp(lse_s - lse) * o_s
@@ -48,8 +49,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   // One pass over the splits, 4 at a time with every load of a group issued before any
   // is used: a running shift Ms (the largest partial LSE so far, 0 while there is none)
   // and the sums rescaled whenever it grows, so the partials are read once and no load
-  // waits on an earlier group's LSE.  A flagged row's low half is loaded once its flag
-  // is known (the high halves are in flight meanwhile).
+  // waits on an earlier group's LSE.  A flagged quarter's low half is loaded once its
+  // flag is known (the high halves are in flight meanwhile).
   float tot = 0.f, Ms = 0.f, M = -INFINITY;
   auto prow = [&](int sidx) { return ((size_t)(s0 + sidx) * a.rows_per_wg + rl); };
   for (int base = 0; base < ns; base += 4) {
@@ -68,14 +69,13 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
         x[k][1] = *(const u32x4*)(a.ws_hi + pr * kDv + kDv / 2 + 8 * t);
       }
     }
+    // this thread's values 8t .. 8t+7 lie in quarter t/16 of the row, 256+8t .. in 2 + t/16
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       y[k][0] = y[k][1] = u32x4{0u, 0u, 0u, 0u};
-      if (fl[k] != 0) {
-        const size_t pr = prow(base + k);
-        y[k][0] = *(const u32x4*)(a.ws_lo + pr * kDv + 8 * t);
-        y[k][1] = *(const u32x4*)(a.ws_lo + pr * kDv + kDv / 2 + 8 * t);
-      }
+      const size_t pr = prow(base + k);
+      if (fl[k] & (1 << (t >> 4))) y[k][0] = *(const u32x4*)(a.ws_lo + pr * kDv + 8 * t);
+      if (fl[k] & (4 << (t >> 4))) y[k][1] = *(const u32x4*)(a.ws_lo + pr * kDv + kDv / 2 + 8 * t);
     }
     float Mn = M;
 #pragma unroll

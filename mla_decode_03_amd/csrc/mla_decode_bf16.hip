@@ -46,11 +46,39 @@ constexpr float kSumCap = 65536.0f; // 2^kRefSlack: a half-row page sum above it
 constexpr int kPrefK = 2;           // K-fragment prefetch distance (32-dim steps)
 constexpr int kPrefV = 4;           // V-fragment prefetch distance (16-wide value tiles)
 // A split partial row is stored as its bf16 rounding (hi), which is within 2^-8 |o| of the
-// fp32 value o; a row whose largest |o| exceeds kLoCut also stores lo = bf16(o - hi), and
-// hi + lo is within 2^-16 |o|.  So a partial the merge reads is never off by more than
+// fp32 value o; each quarter of the row (128 values) whose largest |o| exceeds kLoCut also
+// stores lo = bf16(o - hi), and hi + lo is within 2^-16 |o|.  So a partial the merge reads is never off by more than
 // 2^-8 * kLoCut = 0.0039 plus 2^-16 of its own size, however much the partials of a row
 // cancel in the merge.
 constexpr float kLoCut = 1.0f;
+// The low half of one row's quarter (the wave's 128 value columns), straight from the
+// accumulators: lane (l/32) of the row's pair holds values 32 t + 8 i + 4 (l/32) .. +3 of
+// tile t, so `dst` points at the quarter's first value plus 4 (l/32), and each 4-value
+// piece is one 8-byte store.  tile(t) gives the accumulator of value tile t (0..3).
+template <class Tile>
+__device__ __forceinline__ void store_lo_quarter(uint16_t* dst, float so, Tile tile) {
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16& t = tile(t4);
+      uint32_t lw[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float x0 = t[4 * i + 2 * h] * so, x1 = t[4 * i + 2 * h + 1] * so;
+        const uint32_t hi2 = pack_bf16x2(x0, x1);
+        lw[h] = pack_bf16x2(x0 - __uint_as_float(hi2 << 16), x1 - __uint_as_float(hi2 & 0xffff0000u));
+      }
+      *(u32x2*)(dst + 32 * t4 + 8 * i) = u32x2{lw[0], lw[1]};
+    }
+}
+// A partial row's low-half flags: bit q set where quarter q (values 128q .. 128q+127) of
+// the row stored its low half, i.e. where that quarter's largest |o| (amax[q][row], the
+// value the storing wave compared) exceeds kLoCut.
+__device__ __forceinline__ int lo_quarters(const MLA_LDS float* amax, int rr) {
+  return (amax[rr] > kLoCut ? 1 : 0) | (amax[128 + rr] > kLoCut ? 2 : 0) | (amax[256 + rr] > kLoCut ? 4 : 0) |
+         (amax[384 + rr] > kLoCut ? 8 : 0);
+}
 
 // One wave-wide 16 B/lane global->LDS copy: lane i's 16 bytes from base + voff land at
 // LDS address lds + 16*i.  Issued as assembly so the compiler does not treat it as an
@@ -658,6 +686,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   // row's high half carries it).
   MLA_LDS uint8_t* ob = lds;
   const bool part = slot >= 0;
+  const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int rr = 32 * rt + lr_e;
@@ -676,16 +705,13 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
             u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
       }
     if (part) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));      // over the wave's 128 columns of the row
       if (g_e == 0) amax[w * 128 + rr] = mx;
+      if (mx > kLoCut && row0 + rr < row_end)      // this quarter of the row keeps its low half
+        store_lo_quarter(a.ws_lo + (prow + rr) * kDv + 128 * w + 4 * g_e, scale_o, [&](int dt) -> const f32x16& { return o[dt][rt]; });
     }
   }
   __syncthreads();
-  // A split partial row whose largest |o| exceeds kLoCut also stores its low half.
-  auto needs_lo = [&](int rr) {
-    return row0 + rr < row_end && fmaxf(fmaxf(amax[rr], amax[128 + rr]), fmaxf(amax[256 + rr], amax[384 + rr])) > kLoCut;
-  };
-  const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
   for (int k = 0; k < 32; ++k) {                  // the wave's rows 32w .. 32w+31
     const int rr = 32 * w + k;
     if (row0 + rr >= row_end) break;              // uniform
@@ -700,44 +726,8 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       a.lse[(size_t)b * R + row0 + rr] = lse_v;
     } else {
       a.ws_lse[prow + rr] = lse_v;
-      a.ws_flag[prow + rr] = needs_lo(rr) ? 1 : 0;
+      a.ws_flag[prow + rr] = lo_quarters(amax, rr);
     }
-  }
-  if (!part) return;
-  // Low halves: lo = bf16(o - hi), o the fp32 normalised value and hi its bf16 rounding,
-  // so hi + lo carries o to 2^-16 relative.  Every wave checks every row (two per lane)
-  // on the same LDS words, so the branch is uniform over the workgroup.
-  if (__builtin_amdgcn_ballot_w64(needs_lo(l_e) || needs_lo(l_e + 64)) == 0) return;
-  __syncthreads();   // every wave has read its high halves out of LDS
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int rr = 32 * rt + lr_e;
-    const float scale_o = stats[2 * rr];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x16& t = o[dt][rt];
-        float x[4];
-        uint32_t lw[2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = t[4 * i + j] * scale_o;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t hi2 = pack_bf16x2(x[2 * h], x[2 * h + 1]);
-          lw[h] = pack_bf16x2(x[2 * h] - __uint_as_float(hi2 << 16), x[2 * h + 1] - __uint_as_float(hi2 & 0xffff0000u));
-        }
-        const int c = 16 * w + 4 * dt + i;
-        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) = u32x2{lw[0], lw[1]};
-      }
-  }
-  __syncthreads();
-  for (int k = 0; k < 32; ++k) {
-    const int rr = 32 * w + k;
-    if (row0 + rr >= row_end) break;              // uniform
-    if (!needs_lo(rr)) continue;                  // uniform
-    const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
-    *(u32x4*)(a.ws_lo + (prow + rr) * kDv + 8 * l_e) = v;
   }
 }
 
@@ -1252,6 +1242,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
   // row: row rr at rr*1024, 16-byte chunk cc (values 8cc .. 8cc+7) at (cc ^ (rr & 15))*16.
   // For a split partial the same pass takes each row's largest |o| over the wave's columns.
   const bool part = slot >= 0;
+  const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rr = 32 * ((w + r) & 3) + lr_e;
@@ -1270,16 +1261,13 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
             u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
       }
     if (part) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));      // over the wave's 128 columns of the row
       if (g_e == 0) amax[w * 128 + rr] = mx;
+      if (mx > kLoCut && row0 + rr < row_end)      // this quarter of the row keeps its low half
+        store_lo_quarter(a.ws_lo + (prow + rr) * kDv + 128 * w + 4 * g_e, so, [&](int vt) -> const f32x16& { return o[4 * vt + r]; });
     }
   }
   __syncthreads();
-  // A split partial row whose largest |o| exceeds kLoCut also stores its low half.
-  auto needs_lo = [&](int rr) {
-    return row0 + rr < row_end && fmaxf(fmaxf(amax[rr], amax[128 + rr]), fmaxf(amax[256 + rr], amax[384 + rr])) > kLoCut;
-  };
-  const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
   for (int k = 0; k < 32; ++k) {                      // the wave's rows 32w .. 32w+31
     const int rr = 32 * w + k;
     if (row0 + rr >= row_end) break;                  // uniform
@@ -1294,44 +1282,8 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       a.lse[(size_t)b * R + row0 + rr] = lse_v;
     } else {
       a.ws_lse[prow + rr] = lse_v;
-      a.ws_flag[prow + rr] = needs_lo(rr) ? 1 : 0;
+      a.ws_flag[prow + rr] = lo_quarters(amax, rr);
     }
-  }
-  if (!part) return;
-  // Low halves: lo = bf16(o - hi), o the fp32 normalised value and hi its bf16 rounding,
-  // so hi + lo carries o to 2^-16 relative.  Every wave checks every row (two per lane)
-  // on the same LDS words, so the branch is uniform over the workgroup.
-  if (__builtin_amdgcn_ballot_w64(needs_lo(l_e) || needs_lo(l_e + 64)) == 0) return;
-  __syncthreads();   // every wave has read its high halves out of LDS
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int rr = 32 * ((w + r) & 3) + lr_e;
-    const float so = stats[2 * rr];
-#pragma unroll
-    for (int vt = 0; vt < 4; ++vt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x16& t = o[4 * vt + r];
-        float x[4];
-        uint32_t lw[2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = t[4 * i + j] * so;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t hi2 = pack_bf16x2(x[2 * h], x[2 * h + 1]);
-          lw[h] = pack_bf16x2(x[2 * h] - __uint_as_float(hi2 << 16), x[2 * h + 1] - __uint_as_float(hi2 & 0xffff0000u));
-        }
-        const int cc = 16 * w + 4 * vt + i;
-        *(MLA_LDS u32x2*)(lds + rr * 1024 + ((cc ^ (rr & 15)) << 4) + 8 * g_e) = u32x2{lw[0], lw[1]};
-      }
-  }
-  __syncthreads();
-  for (int k = 0; k < 32; ++k) {
-    const int rr = 32 * w + k;
-    if (row0 + rr >= row_end) break;                  // uniform
-    if (!needs_lo(rr)) continue;                      // uniform
-    const u32x4 v = *(const MLA_LDS u32x4*)(lds + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
-    *(u32x4*)(a.ws_lo + (prow + rr) * kDv + 8 * l_e) = v;
   }
 }
 

@@ -160,7 +160,8 @@ def test_merge_of_large_cancelling_partials():
     partials are peaked (their P is exact to a few ulps) and hold values up to ~16x the
     unit scale, and rows whose merge cancels them come out small.  A float64 model of the
     kernel's rounding puts bf16-only partials at 1.4x the absolute bound on this case, and
-    the compensated pair (bf16 high half plus the low half stored for rows with |o| > 1)
+    the compensated pair (bf16 high half plus the low half stored for row quarters with
+    |o| > 1)
     at 0.36x.  The low halves must have been written, and every row must meet the oracle.
     (Past about 16x, with block scales that keep growing, the bf16 rounding of P alone
     exceeds the absolute bound, whatever the partials' precision.)"""
@@ -175,8 +176,8 @@ def test_merge_of_large_cancelling_partials():
     rows = dec.plan.max_partials * 128                 # partial rows of the workspace
     flags = dec.workspace[rows * 2048 + rows * 4: rows * 2048 + rows * 8].view(torch.int32).cpu().numpy()
     # only the slots the plan uses were written; the rest of the region is uninitialised
-    say("  partial rows with a low half:", int((flags == 1).sum()))
-    assert (flags == 1).sum() > 1000
+    say("  partial rows with a low half:", int((flags != 0).sum()))
+    assert (flags != 0).sum() > 1000
     compare(o, l, ref_o, ref_l, "large cancelling partials")
 
 
