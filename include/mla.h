@@ -164,14 +164,13 @@ MLA_API size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_o
  * problem/options/num_cus: room for the split partials, and for a sparse problem the
  * lists turned into pool rows (4 bytes per entry, padded to 64 per (b, t), plus a
  * count).  Host-only arithmetic.
- * A split partial row (one row of one split) takes 2056 bytes: the normalised float32
- * output o as a compensated pair of bf16 halves, hi = bf16(o) and lo = bf16(o - hi)
- * (2 x 1024 B), its float32 natural-log LSE and an int32 flag word.  The decode
- * always writes hi, and writes lo only for a quarter of the row (128 values) whose
- * largest |o| exceeds 1, setting that quarter's bit (bit q for values 128q ..
- * 128q+127) in the flag word; so a partial enters the merge within 2^-8 (hi alone,
- * |o| <= 1) or 2^-16 |o| (hi + lo) of its float32 value, however much a row's
- * partials cancel.
+ * A split partial row (one row of one split) takes 2052 bytes, and each partial slot
+ * 64 more: the row's normalised float32 output o as a compensated pair of bf16 halves,
+ * hi = bf16(o) and lo = bf16(o - hi) (2 x 1024 B), its float32 natural-log LSE, and per
+ * slot 4 flag bits per row.  The decode always writes hi, and writes lo only for a
+ * quarter of a row (128 values) whose largest |o| exceeds 1, setting that quarter's
+ * bit; so a partial enters the merge within 2^-8 (hi alone, |o| <= 1) or 2^-16 |o|
+ * (hi + lo) of its float32 value, however much a row's partials cancel.
  */
 MLA_API size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
                            int32_t num_cus);

@@ -20,12 +20,13 @@ constexpr int kDefaultMinBlocks = 4;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Split partials: the normalised output's bf16 high halves [slots, rows, 512], its low
-// halves [slots, rows, 512], the fp32 LSE [slots, rows] and the low-half flag words [slots, rows] (a bit per
-// quarter of the row).
-constexpr size_t kPartialRowBytes = 2 * mla::kDv * sizeof(uint16_t) + sizeof(float) + sizeof(int32_t);
+// Split partials, over prow = slots * rows partial rows: the normalised output's bf16
+// high halves [prow, 512]; the fp32 LSEs [prow], padded to 16 bytes; the low-half flags
+// [slots, kLoMaskWords]; the low halves [prow, 512].  The combine reads the first three.
+size_t lse_bytes(size_t prow) { return (prow * sizeof(float) + 15) / 16 * 16; }
 size_t partial_bytes(int64_t slots, int64_t rows_per_wg) {
-  return (size_t)slots * rows_per_wg * kPartialRowBytes;
+  const size_t prow = (size_t)slots * rows_per_wg;
+  return 2 * prow * mla::kDv * sizeof(uint16_t) + lse_bytes(prow) + (size_t)slots * mla::kLoMaskWords * sizeof(uint32_t);
 }
 
 int32_t check_problem(const mla_problem_t* p) {
@@ -253,7 +254,7 @@ int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* 
   a->ws_hi = nullptr;
   a->ws_lo = nullptr;
   a->ws_lse = nullptr;
-  a->ws_flag = nullptr;
+  a->ws_lo_mask = nullptr;
   a->rows_per_wg = a->rows;
   a->row_split = 1;
   a->sinks = nullptr;
@@ -301,10 +302,12 @@ int32_t attach_plan(const mla_problem_t& orig, const mla_plan_t* plan, const voi
   uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
   a->meta = static_cast<int32_t*>(plan->metadata);
   const size_t prow = (size_t)plan->max_partials * plan->rows_per_wg;   // partial rows
+  uint8_t* p_lse = ws + prow * mla::kDv * sizeof(uint16_t);
+  uint8_t* p_mask = p_lse + lse_bytes(prow);
   a->ws_hi = reinterpret_cast<uint16_t*>(ws);
-  a->ws_lo = a->ws_hi + prow * mla::kDv;
-  a->ws_lse = reinterpret_cast<float*>(a->ws_lo + prow * mla::kDv);
-  a->ws_flag = reinterpret_cast<int32_t*>(a->ws_lse + prow);
+  a->ws_lse = reinterpret_cast<float*>(p_lse);
+  a->ws_lo_mask = reinterpret_cast<uint32_t*>(p_mask);
+  a->ws_lo = reinterpret_cast<uint16_t*>(p_mask + (size_t)plan->max_partials * mla::kLoMaskWords * sizeof(uint32_t));
   a->rows_per_wg = plan->rows_per_wg;
   a->row_split = plan->row_split;
   if (orig.topk > 0) {
@@ -341,7 +344,7 @@ int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
   c.ws_hi = a.ws_hi;
   c.ws_lo = a.ws_lo;
   c.ws_lse = a.ws_lse;
-  c.ws_flag = a.ws_flag;
+  c.ws_lo_mask = a.ws_lo_mask;
   c.out = a.out;
   c.lse = a.lse;
   c.batch = a.batch;

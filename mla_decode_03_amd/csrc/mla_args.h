@@ -7,6 +7,10 @@
 
 namespace mla {
 
+// Low-half flags of a partial slot: 4 bits per row (bit q: values 128q .. 128q+127 of the
+// row have a low half), rows 8m .. 8m+7 in word m, so 16 words cover a slot's 128 rows.
+constexpr int kLoMaskWords = 16;
+
 struct DecodeArgs {
   const uint8_t* q;            // bf16 [B, R, 576]
   const uint8_t* kv;           // bf16 [num_pages, 64, 576]
@@ -18,7 +22,7 @@ struct DecodeArgs {
   uint16_t* ws_hi;             // split partials: normalised output rounded to bf16 [slots, rows_per_wg, 512]
   uint16_t* ws_lo;             // bf16(output - hi) [slots, rows_per_wg, 512], written for flagged quarters only
   float* ws_lse;               // partial log-sum-exp [slots, rows_per_wg]
-  int32_t* ws_flag;            // bit q: values 128q .. 128q+127 of the row have a low half [slots, rows_per_wg]
+  uint32_t* ws_lo_mask;        // low-half flags [slots, kLoMaskWords]
   const float* sinks;          // attention-sink logits [heads], or nullptr
   const int32_t* sparse_rows;  // sparse: pool rows per unit [units, row_stride], or nullptr
   int sparse_stride;           // row_stride of sparse_rows (a multiple of 64)
@@ -30,9 +34,9 @@ struct DecodeArgs {
 struct CombineArgs {
   const int32_t* meta;
   const uint16_t* ws_hi;       // partial outputs, high halves (bf16)
-  const uint16_t* ws_lo;       // low halves, read where ws_flag's quarter bit is set
+  const uint16_t* ws_lo;       // low halves, read where ws_lo_mask has the quarter's bit
   const float* ws_lse;
-  const int32_t* ws_flag;
+  const uint32_t* ws_lo_mask;
   uint16_t* out;    // bf16 [B, R, 512]
   float* lse;       // [B, R]
   const float* sinks;  // attention-sink logits [heads], or nullptr

@@ -49,33 +49,39 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   // One pass over the splits, 4 at a time with every load of a group issued before any
   // is used: a running shift Ms (the largest partial LSE so far, 0 while there is none)
   // and the sums rescaled whenever it grows, so the partials are read once and no load
-  // waits on an earlier group's LSE.  A flagged quarter's low half is loaded once its
-  // flag is known (the high halves are in flight meanwhile).
+  // waits on an earlier group's LSE.  The low-half flags of the workgroup's 8 rows (word
+  // rl0/8 of each slot's mask) are scalar loads issued first, so the few low halves a
+  // group needs are requested while its high halves are still in flight.
   float tot = 0.f, Ms = 0.f, M = -INFINITY;
+  const int rl0 = (blockIdx.x % chunks) * kCombineRows;
   auto prow = [&](int sidx) { return ((size_t)(s0 + sidx) * a.rows_per_wg + rl); };
   for (int base = 0; base < ns; base += 4) {
+    uint32_t mw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      mw[k] = base + k < ns ? a.ws_lo_mask[(size_t)(s0 + base + k) * kLoMaskWords + (rl0 >> 3)] : 0u;
     float ls[4];
-    int fl[4];
     u32x4 x[4][2], y[4][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       ls[k] = -INFINITY;
-      fl[k] = 0;
       if (base + k < ns) {
         const size_t pr = prow(base + k);
         ls[k] = a.ws_lse[pr];
-        fl[k] = a.ws_flag[pr];
         x[k][0] = *(const u32x4*)(a.ws_hi + pr * kDv + 8 * t);
         x[k][1] = *(const u32x4*)(a.ws_hi + pr * kDv + kDv / 2 + 8 * t);
       }
     }
-    // this thread's values 8t .. 8t+7 lie in quarter t/16 of the row, 256+8t .. in 2 + t/16
+    // this thread's values 8t .. 8t+7 lie in quarter t/16 of its row, 256+8t .. in 2 + t/16
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       y[k][0] = y[k][1] = u32x4{0u, 0u, 0u, 0u};
-      const size_t pr = prow(base + k);
-      if (fl[k] & (1 << (t >> 4))) y[k][0] = *(const u32x4*)(a.ws_lo + pr * kDv + 8 * t);
-      if (fl[k] & (4 << (t >> 4))) y[k][1] = *(const u32x4*)(a.ws_lo + pr * kDv + kDv / 2 + 8 * t);
+      if (mw[k] != 0) {                                  // uniform over the workgroup
+        const uint32_t fl = mw[k] >> (4 * (rl & 7));     // this row's 4 bits
+        const size_t pr = prow(base + k);
+        if (fl & (1u << (t >> 4))) y[k][0] = *(const u32x4*)(a.ws_lo + pr * kDv + 8 * t);
+        if (fl & (4u << (t >> 4))) y[k][1] = *(const u32x4*)(a.ws_lo + pr * kDv + kDv / 2 + 8 * t);
+      }
     }
     float Mn = M;
 #pragma unroll

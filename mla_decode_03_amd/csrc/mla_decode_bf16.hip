@@ -72,12 +72,21 @@ __device__ __forceinline__ void store_lo_quarter(uint16_t* dst, float so, Tile t
       *(u32x2*)(dst + 32 * t4 + 8 * i) = u32x2{lw[0], lw[1]};
     }
 }
-// A partial row's low-half flags: bit q set where quarter q (values 128q .. 128q+127) of
-// the row stored its low half, i.e. where that quarter's largest |o| (amax[q][row], the
-// value the storing wave compared) exceeds kLoCut.
-__device__ __forceinline__ int lo_quarters(const MLA_LDS float* amax, int rr) {
-  return (amax[rr] > kLoCut ? 1 : 0) | (amax[128 + rr] > kLoCut ? 2 : 0) | (amax[256 + rr] > kLoCut ? 4 : 0) |
-         (amax[384 + rr] > kLoCut ? 8 : 0);
+// Word m of a partial slot's low-half flags: rows 8m .. 8m+7 (of `rows`), 4 bits each, bit
+// q set where quarter q (values 128q .. 128q+127) of the row stored its low half, i.e.
+// where that quarter's largest |o| (amax[q][row], the value the storing wave compared)
+// exceeds kLoCut.
+__device__ __forceinline__ uint32_t lo_mask_word(const MLA_LDS float* amax, int m, int rows) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rr = 8 * m + j;
+    if (rr < rows)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (amax[128 * q + rr] > kLoCut) word |= 1u << (4 * j + q);
+  }
+  return word;
 }
 
 // One wave-wide 16 B/lane global->LDS copy: lane i's 16 bytes from base + voff land at
@@ -726,9 +735,9 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
       a.lse[(size_t)b * R + row0 + rr] = lse_v;
     } else {
       a.ws_lse[prow + rr] = lse_v;
-      a.ws_flag[prow + rr] = lo_quarters(amax, rr);
     }
   }
+  if (part && tid_e < kLoMaskWords) a.ws_lo_mask[(size_t)slot * kLoMaskWords + tid_e] = lo_mask_word(amax, tid_e, row_end - row0);
 }
 
 // ===== 128 rows: half pages through a four-slot ring =====================================
@@ -1282,9 +1291,9 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       a.lse[(size_t)b * R + row0 + rr] = lse_v;
     } else {
       a.ws_lse[prow + rr] = lse_v;
-      a.ws_flag[prow + rr] = lo_quarters(amax, rr);
     }
   }
+  if (part && tid_e < kLoMaskWords) a.ws_lo_mask[(size_t)slot * kLoMaskWords + tid_e] = lo_mask_word(amax, tid_e, row_end - row0);
 }
 
 // ===== kernel ==========================================================================

@@ -90,16 +90,18 @@ def test_plan_sizes_and_workspace_checks():
     # header + cu_blocks[B+1] + 3 per unit + wg_begin[grid+1] int32 words
     assert mb == 4 * (16 + 5 + 3 * 4 + 257)
     # partial slots: grid + min(grid, units), each rows_per_wg rows of a compensated bf16
-    # pair (hi and lo halves), a float32 LSE and an int32 low-half flag
-    assert wb == (256 + 4) * 128 * (512 * 4 + 8)
+    # pair (hi and lo halves) and a float32 LSE, plus 16 words of low-half flags a slot
+    def part(slots, rows):
+        return slots * rows * 512 * 4 + (slots * rows * 4 + 15) // 16 * 16 + slots * 64
+    assert wb == part(256 + 4, 128)
     opts = m.PlanOptions(num_workgroups=8, min_blocks_per_wg=1, row_split=2)
-    assert m.workspace_bytes(p, opts, 256) == (8 + 8) * 64 * (512 * 4 + 8)
+    assert m.workspace_bytes(p, opts, 256) == part(8 + 8, 64)
     assert m.workspace_bytes(p, m.PlanOptions(row_split=3), 256) == 0  # unsupported split
     # batch-invariant plan: one workgroup and one partial slot per possible chunk
     fo = m.PlanOptions(fixed_split_blocks=5, row_split=2, num_workgroups=3)
     grid = 4 * 2 * 4                                       # units * ceil(16 / 5)
     assert m.metadata_bytes(p, fo, 256) == 4 * (16 + 5 + 3 * 8 + grid + 1)
-    assert m.workspace_bytes(p, fo, 256) == grid * 64 * (512 * 4 + 8)
+    assert m.workspace_bytes(p, fo, 256) == part(grid, 64)
     assert m.workspace_bytes(p, fo, 80) == m.workspace_bytes(p, fo, 256)   # no CU dependence
     # partition rule: 0 (cost model), 1 (pages) or 2 (cost); anything else is refused
     for rule in (0, 1, 2):
@@ -161,7 +163,7 @@ def test_sparse_problem_checks():
     mb = m.metadata_bytes(sp, None, 256)
     assert mb == 4 * (16 + 9 + 3 * 8 + 257)
     # workspace: partials (256-byte aligned), then the row lists and the counts
-    part = (256 + 8) * 128 * 2056
+    part = (256 + 8) * 128 * 2052 + (256 + 8) * 64
     rows = 8 * 128 * 4
     assert m.workspace_bytes(sp, None, 256) == ((part + 255) // 256 * 256) + rows + 256
     assert m.metadata_bytes(_problem(q_len=2, num_heads=128), None, 256) == 0   # dense: too many rows
