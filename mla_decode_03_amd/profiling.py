@@ -9,8 +9,9 @@
         (bench.py reports the figure only while that hash matches).
     python -m mla_decode_03_amd.profiling stats KERNEL_STATS_CSV
         Markdown table of a --kernel-trace --stats run (calls, average/min/max us).
-    python -m mla_decode_03_amd.profiling trace KERNEL_TRACE_CSV --steps K --warmup W
-        Per-kernel durations of a traced `bench.py --steps K --warmup W` run: over every
+    python -m mla_decode_03_amd.profiling trace KERNEL_TRACE_CSV --steps K --skip N
+        Per-kernel durations of a traced `bench.py --steps K` run whose line gives
+        first_timed_step N (the whole steps enqueued before the timed ones): over every
         dispatch, and over the dispatches of the K timed steps (what bench.py's step time
         and its decode figure, step minus planner minus combine, cover).
     python -m mla_decode_03_amd.profiling counters CSV [CSV ...]
@@ -103,11 +104,12 @@ def stats(path):
                                                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
 
 
-def trace(path, steps, warmup, decode=DECODE_KERNEL):
+def trace(path, steps, skip, decode=DECODE_KERNEL):
     """Markdown table of per-kernel durations from a kernel-trace CSV of a `bench.py
-    --steps K --warmup W` run: over every dispatch, and over the dispatches of the K timed
-    steps (the W+1st .. W+Kth decode launches and, in launch order, the dispatch just
-    before and just after each: that step's planner and combine).
+    --steps K` run: over every dispatch, and over the dispatches of the K timed steps (the
+    decode launches skip+1 .. skip+K and, in launch order, the dispatch just before and
+    just after each: that step's planner and combine).  `skip` is the number of whole
+    steps the run enqueued before its timed ones (`first_timed_step` in bench.py's line).
     Returns {kernel: {"all": us, "timed": us}}."""
     allds = []
     with open(path, newline="") as f:
@@ -116,8 +118,8 @@ def trace(path, steps, warmup, decode=DECODE_KERNEL):
     allds.sort()
     dec_pos = [i for i, d in enumerate(allds) if decode in d[2]]
     timed = set()
-    if len(dec_pos) >= warmup + steps:
-        for p in dec_pos[warmup:warmup + steps]:
+    if len(dec_pos) >= skip + steps:
+        for p in dec_pos[skip:skip + steps]:
             timed.update(q for q in (p - 1, p, p + 1) if 0 <= q < len(allds))
     per = collections.defaultdict(lambda: ([], []))
     for i, (b, e, name) in enumerate(allds):
@@ -163,7 +165,7 @@ def main(argv=None):
     tr = sub.add_parser("trace")
     tr.add_argument("csv")
     tr.add_argument("--steps", type=int, required=True)
-    tr.add_argument("--warmup", type=int, required=True)
+    tr.add_argument("--skip", type=int, required=True, help="whole steps before the timed ones")
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")
     a = ap.parse_args(argv)
@@ -172,7 +174,7 @@ def main(argv=None):
     elif a.cmd == "stats":
         stats(a.csv)
     elif a.cmd == "trace":
-        trace(a.csv, a.steps, a.warmup)
+        trace(a.csv, a.steps, a.skip)
     else:
         counters(a.csv)
 

@@ -47,8 +47,9 @@ def test_kernel_source_hash_is_stable():
 
 
 def test_trace_picks_the_timed_steps(tmp_path, capsys):
-    """The timed steps are the W+1st .. W+Kth decode launches with the launch just before
-    (the planner) and just after (the combine) each, in start order whatever the file order."""
+    """The timed steps are the decode launches W+1 .. W+K (W whole steps enqueued before
+    them) with the launch just before (the planner) and just after (the combine) each, in
+    start order whatever the file order."""
     path = tmp_path / "t_kernel_trace.csv"
     W, K = 2, 3
     rows, t = [], 0
