@@ -793,11 +793,15 @@ __device__ __forceinline__ uint32_t half_copy_lane(const HalfPage& h, int k, int
   const int t = 8 * k + (l >> 3);
   const int tp = h.tok0 + t;
   const int te = tp < h.valid ? tp : 0;
-  return (uint32_t)(te * kRowBytes + (((l & 7) ^ cswz(t)) << 4));
+  return __umul24((uint32_t)te, (uint32_t)kRowBytes) + (uint32_t)(((l & 7) ^ cswz(t)) << 4);
 }
 template <bool B>
 struct BoolC {
   static constexpr bool value = B;
+};
+template <int N>
+struct IntC {
+  static constexpr int value = N;
 };
 // P.V MFMA with no wait states ahead: for operands that no vector instruction has just
 // written (LDS reads, or registers written many instructions earlier).
@@ -993,12 +997,13 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       *(MLA_LDS u32x4*)pb = pn0;
       *(MLA_LDS u32x4*)(pb + 64 * 16) = pn1;
     };
-    auto put_p_half = [&](int n, int ks) {
-      MLA_LDS uint8_t* pb = pbuf + (n & 1) * 8192 + ((2 * w + ks) * 64 + l) * 16;
+    // (poff: byte offset of the half page's P buffer, (n & 1) * 8192)
+    auto put_p_half = [&](uint32_t poff, int ks) {
+      MLA_LDS uint8_t* pb = pbuf + poff + ((2 * w + ks) * 64 + l) * 16;
       *(MLA_LDS u32x4*)pb = ks == 0 ? pn0 : pn1;
     };
-    auto get_p = [&](int n, int rt, int ks) {
-      return lds_read_b128(pbuf + (n & 1) * 8192 + ((2 * rt + ks) * 64 + l) * 16);
+    auto get_p = [&](uint32_t poff, int rt, int ks) {
+      return lds_read_b128(pbuf + poff + ((2 * rt + ks) * 64 + l) * 16);
     };
     // Score loop over the half page in `ks` alone: one MFMA per step (one dependent chain
     // issues at the full MFMA rate); when cp, this wave's 9 copies of `nxt` into `nslot` go
@@ -1035,11 +1040,11 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     // last K-step-0 use.
     bf16x8 vq[2];
     bf16x8 pq[3];                 // P of row tiles w+1, w+2, w+3 for the current K step
-    auto pv_begin = [&](int n) {
+    auto pv_begin = [&](uint32_t poff) {
 #pragma unroll
-      for (int r = 1; r < 4; ++r) pq[r - 1] = get_p(n, (w + r) & 3, 0);
+      for (int r = 1; r < 4; ++r) pq[r - 1] = get_p(poff, (w + r) & 3, 0);
     };
-    auto pv_step = [&](int n, const MLA_LDS uint8_t* vs, const MLA_LDS uint8_t* nvs, bool pre, int q) {
+    auto pv_step = [&](uint32_t poff, const MLA_LDS uint8_t* vs, const MLA_LDS uint8_t* nvs, bool pre, int q) {
       const int ks = q >> 4, vt = (q >> 2) & 3, r = q & 3;
       if (r == 0) {
         const int gq = (q >> 2) + 1;   // the next group
@@ -1048,13 +1053,13 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       }
       const bf16x8 pb = (r == 0) ? __builtin_bit_cast(bf16x8, ks == 0 ? pn0 : pn1) : pq[r - 1];
       mfma_pv_ds(o[4 * vt + r], vq[(q >> 2) & 1], pb);   // o[4 vt + r]: row tile (w + r) % 4
-      if (ks == 0 && vt == 3 && r > 0) pq[r - 1] = get_p(n, (w + r) & 3, 1);
+      if (ks == 0 && vt == 3 && r > 0) pq[r - 1] = get_p(poff, (w + r) & 3, 1);
     };
     auto pv_alone = [&](int n, const MLA_LDS uint8_t* vs, bool pre, const MLA_LDS uint8_t* nvs) {
-      pv_begin(n);
+      pv_begin((n & 1) * 8192);
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
-        pv_step(n, vs, nvs, pre, q);
+        pv_step((n & 1) * 8192, vs, nvs, pre, q);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -1070,17 +1075,23 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     // The 9 copies of half page i+3 into slot (i+3)&3 go out every 7 slots from slot 5.
     HalfPage nn{};                // the next iteration's copy source, formed in slot 14
     int pg_ahead = 0;             // page entry of the half page after it
-    auto fused = [&](int i, auto cp_tag, const HalfPage& nxt) {
+    auto fused = [&](int i, auto cp_tag, auto pos_tag, const HalfPage& nxt) {
       constexpr bool cp = decltype(cp_tag)::value;
-      const MLA_LDS uint8_t* ks = lds + ((i + 1) & 3) * kSlotBytes;
-      const MLA_LDS uint8_t* vs = lds + (i & 3) * kSlotBytes;
-      MLA_LDS uint8_t* nslot = lds + ((i + 3) & 3) * kSlotBytes + w * 1024;
+      // ring position i & 3 (a template value, or -1: taken from i)
+      constexpr int RS = decltype(pos_tag)::value;
+      const int R = RS >= 0 ? RS : (i & 3);
+      const uint32_t kso = ((R + 1) & 3) * kSlotBytes, vso = R * kSlotBytes, nso = ((R + 3) & 3) * kSlotBytes;
+      const MLA_LDS uint8_t* ks = lds + kso;
+      const MLA_LDS uint8_t* vs = lds + vso;
+      MLA_LDS uint8_t* nslot = lds + nso + w * 1024;
       int lc = threadIdx.x;                  // lane index formed here, not kept across the kernel
       asm volatile("" : "+v"(lc));
       const uint32_t coff = cp ? half_copy_lane(nxt, w, lc & 63) : 0u;
       auto load_k = [&](int kk) { return lds_read_b128(ks + (kk >> 2) * kSlotBlock + ky[kk & 3]); };
       bf16x8 kr[kRingPK + 1];
-      pv_begin(i);
+      // P buffers by half-page parity
+      const uint32_t pcur = (R & 1) * 8192, pnxt = ((R + 1) & 1) * 8192;
+      pv_begin(pcur);
 #pragma unroll
       for (int kk = 0; kk < kRingPK; ++kk) kr[kk] = load_k(kk);
       auto s_step = [&](int kk) {
@@ -1092,9 +1103,13 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       // slot: pure arithmetic would otherwise sink to its first use)
       auto extra = [&](int j) {
         if (cp && j % 7 == 5) dma16(nxt.base, coff + (j / 7) * 128, nslot + (j / 7) * kSlotBlock);
-        if (cp && j == 14 && i + 4 < H) {    // half page i+4's source (its page entry came in at the top)
-          nn = half_page(a, pg_ahead, hp0 + i + 4, Lc, bad_page);
-          asm volatile("" : "+s"(nn.base), "+s"(nn.tok0), "+s"(nn.valid));
+        if (cp && j == 14 && i + 4 < H) {    // half page i+4's source
+          if ((R & 1) == 0) {                // a new page: its entry came in at the top
+            nn = half_page(a, pg_ahead, hp0 + i + 4, Lc, bad_page);
+            asm volatile("" : "+s"(nn.base), "+s"(nn.tok0), "+s"(nn.valid));
+          } else {                           // the second half of half page i+3's page
+            nn.tok0 = kHalf;
+          }
         }
         // the softmax terms: slot 55 (the last score MFMA's result has retired) takes the
         // set-up and term 0, slots 56-58 two terms each, slots 59-66 one or two more
@@ -1116,20 +1131,20 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
           sm_pack(j - 58);
           asm volatile("" : "+v"(pn0));
         }
-        if (j == 60) put_p_half(i + 1, 0);
+        if (j == 60) put_p_half(pnxt, 0);
         if (j == 65 || j == 66) {            // pn1 after P.V step 28 (slot 64)
           sm_pack(2 + (j - 65));
           asm volatile("" : "+v"(pn1));
         }
         if (j == 66) {
           sm_finish();
-          put_p_half(i + 1, 1);
+          put_p_half(pnxt, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       };
 #pragma unroll
       for (int q = 0; q < 2; ++q) {          // slots 0-1
-        pv_step(i, vs, ks, true, q);
+        pv_step(pcur, vs, ks, true, q);
         extra(q);
       }
 #pragma unroll
@@ -1138,7 +1153,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
         extra(2 + 3 * m);
         s_step(2 * m + 1);
         extra(3 + 3 * m);
-        pv_step(i, vs, ks, true, 2 + m);
+        pv_step(pcur, vs, ks, true, 2 + m);
         extra(4 + 3 * m);
       }
 #pragma unroll
@@ -1148,7 +1163,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       }
 #pragma unroll
       for (int q = 18; q < 32; ++q) {        // slots 54-67
-        pv_step(i, vs, ks, true, q);
+        pv_step(pcur, vs, ks, true, q);
         extra(36 + q);
       }
     };
@@ -1192,17 +1207,18 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       int i = 1;
       for (; i + 3 < H; ++i) {
         const HalfPage nxt = nn;             // half page i+3
-        // The next page entry: a scalar load, issued before the barrier and waited for right
-        // after it.  Scalar loads share the LDS wait counter and may return out of order, so
-        // one still in flight would turn the iteration's LDS waits into full waits.
-        pg_ahead = ld_const(bt_row, (hp0 + min(i + 4, H - 1)) >> 1);
+        // Even i: the page entry of half page i+4 (the next page), a scalar load issued
+        // before the barrier and waited for right after it.  Scalar loads share the LDS
+        // wait counter and may return out of order, so one still in flight would turn the
+        // iteration's LDS waits into full waits.
+        if ((i & 1) == 0) pg_ahead = ld_const(bt_row, (hp0 + min(i + 4, H - 1)) >> 1);
         wait_half(i + 1);
         asm volatile("" : : "s"(pg_ahead));
-        fused(i, BoolC<true>{}, nxt);
+        fused(i, BoolC<true>{}, IntC<-1>{}, nxt);
       }
       for (; i + 1 < H; ++i) {
         wait_half(i + 1);
-        fused(i, BoolC<false>{}, HalfPage{});
+        fused(i, BoolC<false>{}, IntC<-1>{}, HalfPage{});
       }
       if (H > 1) {                           // the last half page
         __syncthreads();                     // every wave's P of it
