@@ -1325,22 +1325,30 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   int wg = blockIdx.x;
   if (planned && (gridDim.x & 7) == 0) wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   int pos = 0, end = 1;                       // unsplit: one segment, the whole sequence
+  int first_seq = -1;
   if (planned) {
     if (wg >= ld_const(v.hdr, kHdrNumWg)) return;
     pos = ld_const(v.wg_begin, wg);
     end = ld_const(v.wg_begin, wg + 1);
+    first_seq = ld_const(meta_wg_seq(v, gridDim.x), wg);   // the plan's grid is the launch grid
   }
   const int rs = a.row_split;
   while (pos < end) {
     int b, g, blk_lo, blk_hi, slot;
     if (planned) {
-      // sequence holding global position pos: the largest b with rs * cu_blocks[b] <= pos
-      int lo = 0, hi = a.batch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (rs * ld_const(v.cu_blocks, mid) <= pos) lo = mid; else hi = mid - 1;
+      // sequence holding global position pos: the largest b with rs * cu_blocks[b] <= pos,
+      // given by the plan for the workgroup's first segment
+      if (first_seq >= 0) {
+        b = first_seq;
+        first_seq = -1;
+      } else {
+        int lo = 0, hi = a.batch - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (rs * ld_const(v.cu_blocks, mid) <= pos) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
       }
-      b = lo;
       const int cb = ld_const(v.cu_blocks, b);
       const int nb = ld_const(v.cu_blocks, b + 1) - cb;
       g = (pos - rs * cb) / nb;

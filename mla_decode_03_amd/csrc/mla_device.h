@@ -51,7 +51,9 @@ enum MetaHdr {
 // Partition rules of the planner (the split_rule option; the header's kHdrRule).
 enum PlanRule { kRuleAuto = 0, kRulePages = 1, kRuleCost = 2, kRuleFixed = 3 };
 // arrays follow the header: cu_blocks[B+1], num_splits[U], first_wg[U], part_off[U],
-// wg_begin[grid+1], with U = B * row_split units (unit u = b * row_split + g).
+// wg_begin[grid+1], wg_seq[grid], with U = B * row_split units (unit u = b * row_split + g).
+// wg_seq[w] is the sequence holding workgroup w's first block (0 past the workgroups with
+// work), so a decode workgroup finds its first segment without a search.
 struct MetaView {
   int32_t* hdr;
   int32_t* cu_blocks;
@@ -62,8 +64,10 @@ struct MetaView {
 };
 __host__ __device__ inline size_t meta_words(int batch, int row_split, int grid_wg) {
   const size_t units = (size_t)batch * row_split;
-  return kHdrWords + (size_t)(batch + 1) + 3 * units + (size_t)grid_wg + 1;
+  return kHdrWords + (size_t)(batch + 1) + 3 * units + 2 * (size_t)grid_wg + 1;
 }
+// wg_seq of a plan made for grid_wg workgroups (after wg_begin's grid_wg + 1 words)
+__host__ __device__ inline int32_t* meta_wg_seq(const MetaView& v, int grid_wg) { return v.wg_begin + grid_wg + 1; }
 __host__ __device__ inline MetaView meta_view(int32_t* base, int batch, int row_split) {
   MetaView v;
   const size_t units = (size_t)batch * row_split;

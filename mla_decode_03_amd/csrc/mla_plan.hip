@@ -75,6 +75,8 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
   MetaView v = meta_view(meta, batch, row_split);
   // Larger batches keep the non-empty prefix in first_wg (rewritten by the unit pass).
   int32_t* ne_glob = v.first_wg;
+  // wg_seq[w]: the sequence holding workgroup w's first block (0 past the workgroups with work)
+  int32_t* wg_seq = meta_wg_seq(v, grid_wg);
   int err = 0;
 
   // 1. blocks per sequence and their prefix sums; non-empty sequences before each; the
@@ -153,14 +155,20 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
         v.first_wg[u] = ns > 0 ? first : -1;
         v.part_off[u] = poff;
         for (int k = 0; k < ns; ++k)
-          if (first + k < grid_wg) v.wg_begin[first + k] = (int32_t)(ustart + (int64_t)k * fixed_blocks);
+          if (first + k < grid_wg) {
+            v.wg_begin[first + k] = (int32_t)(ustart + (int64_t)k * fixed_blocks);
+            wg_seq[first + k] = u / row_split;
+          }
       }
       ccarry += ctot;
       pcarry += ptot;
     }
     num_wg = ccarry;
     if (num_wg > grid_wg) err = 1;   // cannot happen when grid_wg covers max_blocks
-    for (int w = (int)min<int64_t>(num_wg, grid_wg) + t; w <= grid_wg; w += 256) v.wg_begin[w] = (int32_t)total;
+    for (int w = (int)min<int64_t>(num_wg, grid_wg) + t; w <= grid_wg; w += 256) {
+      v.wg_begin[w] = (int32_t)total;
+      if (w < grid_wg) wg_seq[w] = 0;
+    }
   } else {
     if (total > 0) {
       num_wg = (total + min_blocks - 1) / min_blocks;
@@ -252,10 +260,12 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const int32_t* __restrict
       v.hdr[kHdrCostBalanced] = (int32_t)min<int64_t>(worst_c, INT32_MAX);
     }
 
-    // 3. workgroup ranges
-    for (int w = t; w <= grid_wg; w += 256)
-      v.wg_begin[w] = (w <= num_wg && num_wg > 0) ? (int32_t)(use_cost ? cut_c(w) : cut_p(w))
-                                                  : (int32_t)total;
+    // 3. workgroup ranges, and the sequence holding each one's first block
+    for (int w = t; w <= grid_wg; w += 256) {
+      const int64_t begin = (w <= num_wg && num_wg > 0) ? (use_cost ? cut_c(w) : cut_p(w)) : total;
+      v.wg_begin[w] = (int32_t)begin;
+      if (w < grid_wg) wg_seq[w] = (w < num_wg && begin < total) ? seq_of_block(begin) : 0;
+    }
     // workgroup holding block p: the largest w < num_wg whose range starts at or before p.
     // Cost rule: a cut at cost x lands at or before p exactly when x < Y, Y = the cost
     // position just past block p, so the answer is the largest w with w*ctot < Y*num_wg.

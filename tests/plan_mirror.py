@@ -194,6 +194,19 @@ def segments(plan):
     return out
 
 
+def wg_seq(plan, grid_wg):
+    """The sequence holding each workgroup's first block (0 past the workgroups with work)."""
+    rs, cu, total = plan["row_split"], plan["cu_blocks"], plan["total"]
+    out = []
+    for w in range(grid_wg):
+        p = plan["wg_begin"][w]
+        seq = 0
+        if w < plan["num_wg"] and p < total:
+            seq = max(i for i in range(plan["batch"]) if rs * cu[i] <= p)
+        out.append(seq)
+    return out
+
+
 def to_words(plan, grid_wg, rows, max_partials, max_blocks, error=0):
     """The metadata buffer's int32 words as the device planner writes them."""
     B, rs = plan["batch"], plan["row_split"]
@@ -201,4 +214,4 @@ def to_words(plan, grid_wg, rows, max_partials, max_blocks, error=0):
            plan["num_partials"], error, max_partials, max_blocks, plan["rule"], plan["cost_pages"],
            plan["cost_balanced"], plan["seg_cost"]]
     return hdr, (plan["cu_blocks"] + plan["num_splits"] + plan["first_wg"] + plan["part_off"]
-                      + plan["wg_begin"])
+                      + plan["wg_begin"] + wg_seq(plan, grid_wg))

@@ -87,8 +87,8 @@ def test_plan_sizes_and_workspace_checks():
     p = _problem()
     mb = m.metadata_bytes(p, None, 256)
     wb = m.workspace_bytes(p, None, 256)
-    # header + cu_blocks[B+1] + 3 per unit + wg_begin[grid+1] int32 words
-    assert mb == 4 * (16 + 5 + 3 * 4 + 257)
+    # header + cu_blocks[B+1] + 3 per unit + wg_begin[grid+1] + wg_seq[grid] int32 words
+    assert mb == 4 * (16 + 5 + 3 * 4 + 257 + 256)
     # partial slots: grid + min(grid, units), each rows_per_wg rows of a compensated bf16
     # pair (hi and lo halves) and a float32 LSE, plus 16 words of low-half flags a slot
     def part(slots, rows):
@@ -100,7 +100,7 @@ def test_plan_sizes_and_workspace_checks():
     # batch-invariant plan: one workgroup and one partial slot per possible chunk
     fo = m.PlanOptions(fixed_split_blocks=5, row_split=2, num_workgroups=3)
     grid = 4 * 2 * 4                                       # units * ceil(16 / 5)
-    assert m.metadata_bytes(p, fo, 256) == 4 * (16 + 5 + 3 * 8 + grid + 1)
+    assert m.metadata_bytes(p, fo, 256) == 4 * (16 + 5 + 3 * 8 + 2 * grid + 1)
     assert m.workspace_bytes(p, fo, 256) == part(grid, 64)
     assert m.workspace_bytes(p, fo, 80) == m.workspace_bytes(p, fo, 256)   # no CU dependence
     # partition rule: 0 (cost model), 1 (pages) or 2 (cost); anything else is refused
@@ -161,7 +161,7 @@ def test_sparse_problem_checks():
     sp = _problem(q_len=2, num_heads=128, topk=100)           # 256 rows: fine for a sparse problem
     # planned as batch*q_len units of ceil(100/64) = 2 blocks, 128 rows each
     mb = m.metadata_bytes(sp, None, 256)
-    assert mb == 4 * (16 + 9 + 3 * 8 + 257)
+    assert mb == 4 * (16 + 9 + 3 * 8 + 257 + 256)
     # workspace: partials (256-byte aligned), then the row lists and the counts
     part = (256 + 8) * 128 * 2052 + (256 + 8) * 64
     rows = 8 * 128 * 4
