@@ -18,9 +18,11 @@ ahead or replaying a captured graph).  Each timed pass starts with --settle-ms o
 untimed whole steps, back to back with the timed ones: when the device goes from idle
 to this load, its power management first runs the shader clock about 10 percent
 below its sustained rate for some milliseconds, and the settle steps carry the timed
-ones past that into the sustained rate a serving loop runs at.  The planner and the
-combine are then timed in passes of their own (back to back, after settle steps), and
-the decode kernel's duration is the step's remainder.
+ones past that into the sustained rate a serving loop runs at.  The decode kernel's own
+duration comes from a second pass of whole steps whose decode launches carry events bound
+to the kernel's start and end (mla_decode_splits_timed: no timing packet between the
+launches); the planner and the combine are timed in passes of their own (back to back,
+after settle steps).
 
 Prints one JSON line: throughput in TFLOP/s (algorithmic FLOPs: 2*(576+512) per
 visible key per query row), KV GB/s, roofline fractions, the decode kernel's own
@@ -196,27 +198,17 @@ def main():
     pools = (kv_a, kv_b)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, dec_ev=None):
+        """One whole step; dec_ev: a (start, stop) event pair bound to the decode kernel's own
+        start and end (no timing packet between the step's launches)."""
         kv = pools[i & 1]
         if not split:
-            if ev is not None:
-                ev[1].record(stream)
             mla.decode(dec.problem, q, kv, bt, lens, case.scale, out, lse, None, None, stream, sinks)
-            if ev is not None:
-                ev[2].record(stream)
             return
-        if ev is not None:
-            ev[0].record(stream)
         plan = dec.plan_for(lens, stream)
-        if ev is not None:
-            ev[1].record(stream)
         mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace, stream,
-                          sinks, indices)
-        if ev is not None:
-            ev[2].record(stream)
+                          sinks, indices, events=dec_ev)
         mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks)
-        if ev is not None:
-            ev[3].record(stream)
 
     t_host = time.perf_counter()
     for i in range(args.warmup):
@@ -262,13 +254,14 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
 
-    # Per-kernel durations.  Events between the launches of a step would change them (each
-    # timing event is a stream packet that waits for and releases the work before it, and
-    # the kernel after it starts cold), so the planner and the combine are timed in passes
-    # of their own, `steps` launches back to back between two events, each pass after
-    # `settle` whole untimed steps; the decode's duration is the step's remainder:
-    # ms_per_step - plan - combine (launch gaps inside a held stream are under 1 us).
-    # A kernel trace of the same command agrees with it (the timed steps' dispatches).
+    # Per-kernel durations.  Events recorded between the launches of a step would change
+    # them (each is a stream packet that waits for and releases the work before it, and the
+    # kernel after it starts cold).  So the decode kernel is timed with events bound to its
+    # own start and end (mla_decode_splits_timed), over `steps` whole steps after `settle`
+    # untimed ones, and the planner and the combine in passes of their own, `steps`
+    # launches back to back between two events, each after `settle` whole steps.  A
+    # kernel trace of the same command agrees with the decode figure (the timed steps'
+    # dispatches).
 
     def timed_pass(fn):
         torch.cuda.synchronize()
@@ -284,13 +277,28 @@ def main():
         return p0.elapsed_time(p1) / args.steps
 
     if split:
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        for a_, b_ in dev_ev:             # creates the events
+            a_.record(stream)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        hold(settle + args.steps)
+        for i in range(settle):
+            step(i)
+        for i in range(args.steps):
+            step(i, dev_ev[i])
+        torch.cuda.synchronize()
+        dec_ms = sum(a_.elapsed_time(b_) for a_, b_ in dev_ev) / args.steps
         plan_ms = timed_pass(lambda i: dec.plan_for(lens, stream))
         plan = dec.plan_for(lens, stream)
         comb_ms = timed_pass(lambda i: mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks))
-        kernel_ms = ms_per_step - plan_ms - comb_ms
-        launches = {"method": "decode = step - plan - combine; plan and combine timed in passes of their own",
+        kernel_ms = dec_ms
+        launches = {"method": "decode: events bound to the kernel's own start and end, over whole steps; plan "
+                              "and combine: passes of their own",
                     "first_timed_step": args.warmup + 10 + settle,
                     "decode_us": round(kernel_ms * 1e3, 2), "plan_us": round(plan_ms * 1e3, 2),
+                    "step_minus_plan_combine_us": round((ms_per_step - plan_ms - comb_ms) * 1e3, 2),
                     "combine_us": round(comb_ms * 1e3, 2), "step_us": round(ms_per_step * 1e3, 2)}
     else:
         kernel_ms = ms_per_step

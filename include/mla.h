@@ -270,6 +270,20 @@ MLA_API int32_t mla_decode_splits(const mla_problem_t* problem, const mla_varian
                                   float scale, void* out, float* lse,
                                   const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
                                   void* stream);
+/*
+ * mla_decode_splits_timed: mla_decode_splits whose decode kernel launch also records
+ * two caller-created HIP events (hipEvent_t, timing enabled) bound to that kernel's own
+ * start and end, so hipEventElapsedTime(start, stop) is the kernel's duration.  The
+ * events add no packet of their own between launches (a sparse problem's list kernel
+ * runs before `start`).  For measurement; both events NULL is mla_decode_splits, one
+ * NULL is MLA_ERR_NULL.
+ */
+MLA_API int32_t mla_decode_splits_timed(const mla_problem_t* problem, const mla_variant_t* variant,
+                                        const void* q, const void* kv_cache,
+                                        const int32_t* block_table, const int32_t* cache_seqlens,
+                                        float scale, void* out, float* lse,
+                                        const mla_plan_t* plan, void* workspace, size_t workspace_bytes,
+                                        void* stream, void* start_event, void* stop_event);
 MLA_API int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant,
                             void* out, float* lse,
                             const mla_plan_t* plan, const void* workspace, size_t workspace_bytes,

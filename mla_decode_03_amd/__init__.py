@@ -132,15 +132,19 @@ def decode(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: flo
 
 
 def decode_splits(problem: Problem, q, kv_cache, block_table, cache_seqlens, scale: float, out, lse,
-                  plan: Plan, workspace, stream=None, sinks=None, indices=None) -> None:
-    """Enqueue only the split-KV decode kernel (partials for split sequences)."""
+                  plan: Plan, workspace, stream=None, sinks=None, indices=None, events=None) -> None:
+    """Enqueue only the split-KV decode kernel (partials for split sequences).  events: an
+    optional (start, stop) pair of timing torch.cuda.Event, bound to the kernel's own start
+    and end (mla_decode_splits_timed)."""
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = lib().mla_decode_splits(ctypes.byref(problem), _variant(sinks, indices), _ptr(q), _ptr(kv_cache),
-                                 _ptr(block_table),
-                                 _ptr(cache_seqlens), ctypes.c_float(scale), _ptr(out), _ptr(lse),
-                                 ctypes.byref(plan.c_plan), _ptr(workspace), ctypes.c_size_t(ws_bytes),
-                                 _stream_handle(stream))
-    _abi.check(rc, "mla_decode_splits")
+    args = (ctypes.byref(problem), _variant(sinks, indices), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+            _ptr(cache_seqlens), ctypes.c_float(scale), _ptr(out), _ptr(lse), ctypes.byref(plan.c_plan),
+            _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    if events is None:
+        _abi.check(lib().mla_decode_splits(*args), "mla_decode_splits")
+    else:
+        start, stop = (ctypes.c_void_p(e.cuda_event) for e in events)
+        _abi.check(lib().mla_decode_splits_timed(*args, start, stop), "mla_decode_splits_timed")
 
 
 def combine(problem: Problem, out, lse, plan: Plan, workspace, stream=None, sinks=None) -> None:

@@ -24,7 +24,7 @@ MLA_ERR_BAD_INPUT = 9
 
 # Exported functions, as declared in include/mla.h.
 EXPORTS = ("mla_status_string", "mla_device_num_cus", "mla_metadata_bytes", "mla_workspace_bytes",
-           "mla_get_metadata", "mla_decode", "mla_decode_ex", "mla_decode_splits", "mla_combine",
+           "mla_get_metadata", "mla_decode", "mla_decode_ex", "mla_decode_splits", "mla_decode_splits_timed", "mla_combine",
            "mla_plan_error", "mla_hbm_read_probe", "mla_decode_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +97,9 @@ def lib():
         L.mla_decode_splits.restype = i32
         L.mla_decode_splits.argtypes = [ctypes.POINTER(Problem), V, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                         ctypes.POINTER(CPlan), vp, sz, vp]
+        L.mla_decode_splits_timed.restype = i32
+        L.mla_decode_splits_timed.argtypes = [ctypes.POINTER(Problem), V, vp, vp, vp, vp, ctypes.c_float, vp,
+                                              vp, ctypes.POINTER(CPlan), vp, sz, vp, vp, vp]
         L.mla_combine.restype = i32
         L.mla_combine.argtypes = [ctypes.POINTER(Problem), V, vp, vp, ctypes.POINTER(CPlan), vp, sz, vp]
         L.mla_plan_error.restype = i32

@@ -359,12 +359,13 @@ int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
 // The bf16 decode launches of a planned problem: row lists (sparse), then the split-KV
 // kernel.
 int32_t launch_planned_decode(const mla_problem_t& orig, const int32_t* indices, const int32_t* block_table,
-                              const int32_t* cache_seqlens, const mla::DecodeArgs& a, int grid, hipStream_t st) {
+                              const int32_t* cache_seqlens, const mla::DecodeArgs& a, int grid, hipStream_t st,
+                              hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
   if (orig.topk > 0) {
     const int32_t rc = launch_sparse_rows(orig, indices, block_table, cache_seqlens, a, st);
     if (rc != MLA_OK) return rc;
   }
-  return mla_launch_decode_bf16(&a, grid, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  return mla_launch_decode_bf16(&a, grid, st, start, stop) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -421,7 +422,7 @@ int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t* variant
   }
   if (!plan) {
     if (problem->topk > 0) return MLA_ERR_UNSUPPORTED;   // the row lists live in the workspace
-    return mla_launch_decode_bf16(&a, a.batch, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+    return mla_launch_decode_bf16(&a, a.batch, st, nullptr, nullptr) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
   }
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
@@ -435,6 +436,15 @@ int32_t mla_decode_splits(const mla_problem_t* problem, const mla_variant_t* var
                           const int32_t* block_table, const int32_t* cache_seqlens, float scale,
                           void* out, float* lse, const mla_plan_t* plan, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  return mla_decode_splits_timed(problem, variant, q, kv_cache, block_table, cache_seqlens, scale, out, lse, plan,
+                                 workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int32_t mla_decode_splits_timed(const mla_problem_t* problem, const mla_variant_t* variant, const void* q,
+                                const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                                float scale, void* out, float* lse, const mla_plan_t* plan, void* workspace,
+                                size_t workspace_bytes, void* stream, void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return MLA_ERR_NULL;
   int32_t rc = check_problem(problem);
   if (rc != MLA_OK) return rc;
   if (problem->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
@@ -448,7 +458,8 @@ int32_t mla_decode_splits(const mla_problem_t* problem, const mla_variant_t* var
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
   return launch_planned_decode(*problem, indices, block_table, cache_seqlens, a, plan->grid_wg,
-                               static_cast<hipStream_t>(stream));
+                               static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                               static_cast<hipEvent_t>(stop_event));
 }
 
 int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant, void* out, float* lse,

@@ -75,7 +75,9 @@ extern "C" MLA_INTERNAL hipError_t mla_launch_plan(const int32_t* seqlens, int32
                                       int row_split, int grid_wg, int min_blocks, int max_blocks,
                                       int max_partials, int fixed_blocks, int split_rule, int seg_cost,
                                       int uniform_len, hipStream_t stream);
-extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream);
+// start/stop: events recorded at the kernel's own start and end (both null: a plain launch)
+extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream,
+                                                       hipEvent_t start, hipEvent_t stop);
 extern "C" MLA_INTERNAL hipError_t mla_launch_combine(const mla::CombineArgs* args, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_decode_f32(const mla::F32Args* args, hipStream_t stream);
 extern "C" MLA_INTERNAL hipError_t mla_launch_sparse_rows(const mla::SparseArgs* args, hipStream_t stream);

@@ -29,6 +29,8 @@
 // visible keys and accumulates exp2(x - m_ref) <= 2^kRefSlack; if a later page's sum
 // exceeds that, the segment is decoded again with m_ref at or above every score of the
 // row (exact: no term can overflow, and the row's largest term is at least 2^-kRefSlack).
+#include <hip/hip_ext.h>
+
 #include "mla_args.h"
 #include "mla_device.h"
 
@@ -1374,19 +1376,32 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
 
 }  // namespace mla
 
-extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream) {
+namespace {
+// One launch of the decode kernel: a plain launch, or with events bound to the kernel's own
+// start and end (hipExtLaunchKernelGGL), which adds no timing packet between launches.
+template <int NRT, bool SPARSE>
+void launch_decode(const mla::DecodeArgs& args, dim3 g, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop)
+    hipExtLaunchKernelGGL((mla::mla_decode_bf16_kernel<NRT, SPARSE>), g, dim3(256), 0, stream, start, stop, 0, args);
+  else
+    hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<NRT, SPARSE>), g, dim3(256), 0, stream, args);
+}
+}  // namespace
+
+extern "C" MLA_INTERNAL hipError_t mla_launch_decode_bf16(const mla::DecodeArgs* args, int grid, hipStream_t stream,
+                                                       hipEvent_t start, hipEvent_t stop) {
   const int rpw = args->rows_per_wg;
   const bool sp = args->sparse_rows != nullptr;
-  const dim3 g(grid), blk(256);
+  const dim3 g(grid);
   if (rpw > 64) {
-    if (sp) hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<4, true>), g, blk, 0, stream, *args);
-    else hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<4, false>), g, blk, 0, stream, *args);
+    if (sp) launch_decode<4, true>(*args, g, stream, start, stop);
+    else launch_decode<4, false>(*args, g, stream, start, stop);
   } else if (rpw > 32) {
-    if (sp) hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<2, true>), g, blk, 0, stream, *args);
-    else hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<2, false>), g, blk, 0, stream, *args);
+    if (sp) launch_decode<2, true>(*args, g, stream, start, stop);
+    else launch_decode<2, false>(*args, g, stream, start, stop);
   } else {
-    if (sp) hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<1, true>), g, blk, 0, stream, *args);
-    else hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<1, false>), g, blk, 0, stream, *args);
+    if (sp) launch_decode<1, true>(*args, g, stream, start, stop);
+    else launch_decode<1, false>(*args, g, stream, start, stop);
   }
   return hipGetLastError();
 }

@@ -335,6 +335,50 @@ def test_device_fixed_plan_matches_mirror():
         assert list(words[16:16 + len(arrays)]) == arrays
 
 
+@pytest.mark.parametrize("H, sparse", [(128, False), (16, False), (128, True)])
+def test_timed_decode_matches_untimed(H, sparse):
+    """mla_decode_splits_timed writes what mla_decode_splits writes, bit for bit, and its
+    events time the decode kernel (a positive duration, below the whole enqueue-to-sync time)."""
+    import time
+    import torch
+    import mla_decode_03_amd as mla
+    from mla_inputs import make_topk_indices
+    case = _case(3, 1, H, [300, 1000, 65], seed=61)
+    say("timed decode", H, sparse)
+    q, kv, bt, lens = to_device(case)
+    topk, ix = 0, None
+    if sparse:
+        idx = make_topk_indices(case.cache_seqlens, case.q_len, 64, seed=5)
+        topk, ix = 64, torch.from_numpy(idx).to(q.device)
+    dec = mla.Decoder(q, kv, bt, causal=case.causal, topk=topk)
+    plan = dec.plan_for(lens)
+    R = case.q_len * H
+    results = []
+    for timed in (False, True):
+        out = torch.zeros((case.batch, case.q_len, H, 512), dtype=torch.bfloat16, device=q.device)
+        lse = torch.zeros((case.batch, case.q_len, H), dtype=torch.float32, device=q.device)
+        dec.workspace.zero_()
+        ev = None
+        if timed:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for e in ev:
+                e.record()                   # creates the events
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        mla.decode_splits(dec.problem, q, kv, bt, lens, case.scale, out, lse, plan, dec.workspace,
+                          indices=ix, events=ev)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        if timed:
+            ms = ev[0].elapsed_time(ev[1])
+            say("  kernel %.4f ms, enqueue to sync %.4f ms" % (ms, wall_ms))
+            assert 0.0 < ms <= wall_ms
+        results.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy(), dec.workspace.cpu().numpy()))
+    (o0, l0, w0), (o1, l1, w1) = results
+    assert np.array_equal(o0, o1) and np.array_equal(l0.view(np.int32), l1.view(np.int32))
+    assert np.array_equal(w0, w1)
+
+
 def test_fixed_split_plan_is_batch_invariant():
     """With fixed-size splits a sequence's output bits do not depend on the rest of the
     batch (its position, its neighbours, the batch size) nor on the CU count; the balanced
