@@ -5,8 +5,11 @@ Workload (default): batch 64, 128 query heads, q_len 1, every sequence 4096 cach
 tokens, 576-wide bf16 latent rows (512 latent + 64 rope) in 64-token pages, block
 table a seeded page permutation, scale 192^-0.5; seeded N(0, 1) synthetic inputs.
 
-One step = the whole decode path on one batch: the split planner (mla_get_metadata),
-the split-KV decode kernel and the log-sum-exp combine.  Inputs are resident in HBM
+One step = the whole decode path on one batch: the split plan, the split-KV decode kernel
+and the log-sum-exp combine.  The plan is computed inside the decode launch from the
+step's lengths (plan_in_decode: one mla_get_metadata up front, then every decode launch
+re-plans, each workgroup taking its own share); --planner-kernel plans with a planner
+launch every step instead.  Inputs are resident in HBM
 before timing starts.  Two KV pools with identical contents are alternated step by
 step, so no step can be served from the 256 MB memory-side cache left warm by the
 step before it.
@@ -139,6 +142,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--min-blocks", type=int, default=0)
+    ap.add_argument("--planner-kernel", action="store_true",
+                    help="plan with a planner launch every step (mla_get_metadata), instead of inside the "
+                         "decode launch (plan_in_decode, the default here)")
     ap.add_argument("--row-split", type=int, default=0)
     ap.add_argument("--fixed-split-blocks", type=int, default=0,
                     help="batch-invariant plan: fixed chunks of this many 64-token blocks")
@@ -189,11 +195,13 @@ def main():
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     sinks = torch.from_numpy(make_sinks(H, seed=1)).to(dev) if args.sinks else None
     indices = torch.from_numpy(indices_np).to(dev) if indices_np is not None else None
-    opts = None
-    if args.num_workgroups or args.min_blocks or args.row_split or args.fixed_split_blocks:
-        opts = mla.PlanOptions(num_workgroups=args.num_workgroups, min_blocks_per_wg=args.min_blocks,
-                               row_split=args.row_split, fixed_split_blocks=args.fixed_split_blocks)
     split = case.dtype == "bf16"
+    # bf16 batches of at most 4095 (units of) sequences plan inside the decode launch: the plan
+    # is made once and every decode re-plans from the lengths it is given
+    in_decode = split and not args.planner_kernel and case.batch * (case.q_len if args.sparse_topk > 0 else 1) <= 4095
+    opts = mla.PlanOptions(num_workgroups=args.num_workgroups, min_blocks_per_wg=args.min_blocks,
+                           row_split=args.row_split, fixed_split_blocks=args.fixed_split_blocks,
+                           plan_in_decode=1 if in_decode else 0)
     dec = mla.Decoder(q, kv_a, bt, causal=case.causal, split=split, options=opts, topk=args.sparse_topk)
     pools = (kv_a, kv_b)
     stream = torch.cuda.current_stream()
@@ -290,12 +298,14 @@ def main():
             step(i, dev_ev[i])
         torch.cuda.synchronize()
         dec_ms = sum(a_.elapsed_time(b_) for a_, b_ in dev_ev) / args.steps
-        plan_ms = timed_pass(lambda i: dec.plan_for(lens, stream))
+        # (planning inside the decode: plan_for launches nothing after the first call)
+        plan_ms = timed_pass(lambda i: dec.plan_for(lens, stream)) if not in_decode else 0.0
         plan = dec.plan_for(lens, stream)
         comb_ms = timed_pass(lambda i: mla.combine(dec.problem, out, lse, plan, dec.workspace, stream, sinks))
         kernel_ms = dec_ms
         launches = {"method": "decode: events bound to the kernel's own start and end, over whole steps; plan "
                               "and combine: passes of their own",
+                    "plan_in_decode": bool(in_decode),
                     "first_timed_step": args.warmup + 10 + settle,
                     "decode_us": round(kernel_ms * 1e3, 2), "plan_us": round(plan_ms * 1e3, 2),
                     "step_minus_plan_combine_us": round((ms_per_step - plan_ms - comb_ms) * 1e3, 2),
@@ -358,7 +368,8 @@ def main():
                                                        ("sparse_top%d" % args.sparse_topk, args.sparse_topk > 0))
                                        if on) or "plain",
                    "plan": {"num_workgroups": dec.plan.grid_wg if dec.plan else None,
-                            "fixed_split_blocks": args.fixed_split_blocks or None}},
+                            "fixed_split_blocks": args.fixed_split_blocks or None,
+                            "in_decode": bool(in_decode)}},
         "kv_gb_per_s": round(kv_gbs, 1),
         "frac_hbm_total_bytes": round(frac_hbm, 4),
         "frac_mfma_bf16": round(frac_mfma, 4),

@@ -137,6 +137,8 @@ typedef struct {
                                   2: cost-balanced shares (see mla_get_metadata) */
   int32_t segment_cost;        /* cost model's per-segment overhead in quarter blocks
                                   (0: from the traffic of a segment's rows, see below) */
+  int32_t plan_in_decode;      /* 1: every decode launch re-plans from the lengths it is given
+                                  (see mla_get_metadata); 0: the plan is made once (default) */
 } mla_plan_options_t;
 
 /* Variants of the operation.  NULL (or every field NULL) = plain MLA decode. */
@@ -189,6 +191,8 @@ typedef struct {
   int32_t max_partials;        /* partial slots the workspace must hold (filled) */
   int32_t batch;               /* problem the plan was made for (filled) */
   int32_t rows;                /* q_len * num_heads of that problem (filled) */
+  int32_t plan_in_decode;      /* decode launches re-plan (filled; options->plan_in_decode) */
+  int32_t min_blocks, fixed_blocks, split_rule, segment_cost, topk;   /* the plan's settings (filled) */
 } mla_plan_t;
 
 /*
@@ -200,8 +204,9 @@ typedef struct {
  * candidate configurations by traffic over bandwidth, "Key design 2: tile
  * recommendation"): equal block shares, and equal shares of cost where every segment a
  * workgroup decodes (a sequence's rows, or its slice of them) adds the traffic of its
- * Q and output rows, segment_cost quarter blocks (default: the segment's rows times
- * 2180 B, over 73,728 B per block, rounded; 15 for 128 rows).  The plan keeps the cut whose busiest workgroup costs less,
+ * Q and output rows and its fixed costs, segment_cost quarter blocks (default: from a
+ * step-time model in roofline form fitted on MI355X, 11 for 128 rows per workgroup, 13
+ * for 64 or fewer).  The plan keeps the cut whose busiest workgroup costs less,
  * equal block shares on a tie; split_rule forces either.
  * With options->fixed_split_blocks = C > 0 the plan is batch-invariant instead: every
  * sequence (row slice) is cut into chunks of C blocks from its own start, one chunk per
@@ -212,6 +217,13 @@ typedef struct {
  * A sparse problem is planned as batch * q_len units of ceil(topk / 64) blocks each
  * (cache_seqlens is not read and may be NULL).
  * One single-workgroup kernel launch on `stream`; fills the host fields of *plan.
+ * With options->plan_in_decode = 1 (bf16 problems of at most 4095 sequences, or sparse
+ * units), the plan depends on the lengths only through the decode: every mla_decode /
+ * mla_decode_splits launch made with it recomputes the same cut from the cache_seqlens
+ * it is given, inside the decode kernel (each workgroup takes its own share, one writes
+ * the metadata the combine reads), so one mla_get_metadata serves every later step of
+ * the same problem shape and no planner launch runs per step.  The fault flag is then
+ * only ever raised by the decode; mla_plan_error reads and clears it.
  */
 MLA_API int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
                          const mla_plan_options_t* options, int32_t num_cus,

@@ -207,8 +207,12 @@ class Decoder:
         self.plan = None
 
     def plan_for(self, cache_seqlens, stream=None) -> Plan | None:
+        """The plan for these lengths.  With options.plan_in_decode the decode launches
+        re-plan from the lengths they are given, so the plan is made once and reused."""
         if not self.planned:
             return None
+        if self.plan is not None and self.options is not None and self.options.plan_in_decode:
+            return self.plan
         self.plan = get_metadata(self.problem, cache_seqlens, self.metadata, self.options,
                                  self.num_cus, stream)
         return self.plan

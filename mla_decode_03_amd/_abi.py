@@ -49,7 +49,8 @@ class Problem(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("num_workgroups", ctypes.c_int32), ("min_blocks_per_wg", ctypes.c_int32),
                 ("row_split", ctypes.c_int32), ("fixed_split_blocks", ctypes.c_int32),
-                ("split_rule", ctypes.c_int32), ("segment_cost", ctypes.c_int32)]
+                ("split_rule", ctypes.c_int32), ("segment_cost", ctypes.c_int32),
+                ("plan_in_decode", ctypes.c_int32)]
 
 
 class Variant(ctypes.Structure):
@@ -60,7 +61,10 @@ class CPlan(ctypes.Structure):
     _fields_ = [("metadata", ctypes.c_void_p), ("metadata_bytes", ctypes.c_size_t),
                 ("grid_wg", ctypes.c_int32), ("row_split", ctypes.c_int32),
                 ("rows_per_wg", ctypes.c_int32), ("max_partials", ctypes.c_int32),
-                ("batch", ctypes.c_int32), ("rows", ctypes.c_int32)]
+                ("batch", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("plan_in_decode", ctypes.c_int32), ("min_blocks", ctypes.c_int32),
+                ("fixed_blocks", ctypes.c_int32), ("split_rule", ctypes.c_int32),
+                ("segment_cost", ctypes.c_int32), ("topk", ctypes.c_int32)]
 
 
 def lib_path() -> str:

@@ -13,6 +13,7 @@
 #include "mla.h"
 #include "mla_args.h"
 #include "mla_device.h"
+#include "mla_plan_core.h"
 
 namespace {
 
@@ -91,7 +92,7 @@ int32_t resolve_cus(int32_t num_cus, int32_t* out) {
 }
 
 struct PlanShape {
-  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials, fixed_blocks, split_rule, seg_cost;
+  int grid_wg, row_split, rows_per_wg, min_blocks, max_partials, fixed_blocks, split_rule, seg_cost, in_decode;
 };
 
 // Cost-model overhead of one segment (a unit's rows decoded by one workgroup) besides
@@ -142,6 +143,10 @@ int32_t plan_shape(const mla_problem_t* problem, const mla_plan_options_t* o, in
   if (s->seg_cost > (1 << 20)) return MLA_ERR_SHAPE;
   // each workgroup range holds at most one partial segment at each end (fixed chunks: one)
   s->max_partials = fixed > 0 ? grid : (int)(grid + (units < grid ? units : grid));
+  // re-planning inside the decode keeps the lengths' prefix sums in LDS
+  s->in_decode = (o && o->plan_in_decode) ? 1 : 0;
+  if (o && (o->plan_in_decode < 0 || o->plan_in_decode > 1)) return MLA_ERR_UNSUPPORTED;
+  if (s->in_decode && (p->batch > mla::kPlanLdsBatch || p->dtype != MLA_DTYPE_BF16)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -210,6 +215,12 @@ int32_t mla_get_metadata(const mla_problem_t* problem, const int32_t* cache_seql
   plan->max_partials = s.max_partials;
   plan->batch = problem->batch;
   plan->rows = problem->q_len * problem->num_heads;
+  plan->plan_in_decode = s.in_decode;
+  plan->min_blocks = s.min_blocks;
+  plan->fixed_blocks = s.fixed_blocks;
+  plan->split_rule = s.split_rule;
+  plan->segment_cost = s.seg_cost;
+  plan->topk = topk;
   if (mla_launch_plan(cache_seqlens, static_cast<int32_t*>(plan->metadata), problem->batch,
                       plan->rows, s.row_split, s.grid_wg, s.min_blocks, problem->max_blocks_per_seq,
                       s.max_partials, s.fixed_blocks, s.split_rule, s.seg_cost,
@@ -257,6 +268,9 @@ int32_t prepare_decode(const mla_problem_t* problem, const void* q, const void* 
   a->ws_lo_mask = nullptr;
   a->rows_per_wg = a->rows;
   a->row_split = 1;
+  a->plan_in_decode = 0;
+  a->plan_min_blocks = a->plan_max_partials = a->plan_fixed_blocks = 0;
+  a->plan_split_rule = a->plan_seg_cost = a->plan_uniform_len = 0;
   a->sinks = nullptr;
   a->sparse_rows = nullptr;
   a->sparse_stride = 0;
@@ -310,6 +324,14 @@ int32_t attach_plan(const mla_problem_t& orig, const mla_plan_t* plan, const voi
   a->ws_lo = reinterpret_cast<uint16_t*>(p_mask + (size_t)plan->max_partials * mla::kLoMaskWords * sizeof(uint32_t));
   a->rows_per_wg = plan->rows_per_wg;
   a->row_split = plan->row_split;
+  a->plan_in_decode = plan->plan_in_decode;
+  a->plan_min_blocks = plan->min_blocks;
+  a->plan_max_partials = plan->max_partials;
+  a->plan_fixed_blocks = plan->fixed_blocks;
+  a->plan_split_rule = plan->split_rule;
+  a->plan_seg_cost = plan->segment_cost;
+  a->plan_uniform_len = plan->topk;
+  if (plan->plan_in_decode && (p.batch > mla::kPlanLdsBatch || p.dtype != MLA_DTYPE_BF16)) return MLA_ERR_UNSUPPORTED;
   if (orig.topk > 0) {
     a->sparse_rows = reinterpret_cast<const int32_t*>(ws + part);
     a->sparse_stride = p.max_blocks_per_seq * mla::kPage;

@@ -29,6 +29,9 @@ struct DecodeArgs {
   float scale_log2;            // scale * log2(e)
   int batch, rows, q_len, heads, causal, num_pages, bt_stride, max_blocks;
   int rows_per_wg, row_split;
+  // plan_in_decode: every workgroup re-plans from seqlens with the plan's settings
+  int plan_in_decode, plan_min_blocks, plan_max_partials, plan_fixed_blocks, plan_split_rule, plan_seg_cost,
+      plan_uniform_len;
 };
 
 struct CombineArgs {

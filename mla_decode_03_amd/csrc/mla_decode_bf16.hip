@@ -33,6 +33,7 @@
 
 #include "mla_args.h"
 #include "mla_device.h"
+#include "mla_plan_core.h"
 
 namespace mla {
 
@@ -1314,6 +1315,69 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
   if (part && tid_e < kLoMaskWords) a.ws_lo_mask[(size_t)slot * kLoMaskWords + tid_e] = lo_mask_word(amax, tid_e, row_end - row0);
 }
 
+// ===== a decode launch that plans for itself =============================================
+// Blocks of unit-holding sequence b, as the planner counts them.
+__device__ __forceinline__ int plan_blocks(const DecodeArgs& a, int b) {
+  int64_t L = a.plan_uniform_len > 0 ? a.plan_uniform_len : ld_const(a.seqlens, b);
+  if (L < 0) L = 0;
+  return (int)min<int64_t>((L + kPage - 1) / kPage, a.max_blocks);
+}
+// The whole planner computation on the lengths given to this launch, in LDS (idle until
+// the first segment starts); the workgroup numbered 0 also writes the plan, which the
+// combine reads.  Then this workgroup's share: its range, and the split units at its two
+// ends (units strictly inside the range are whole, so unsplit).  The units after the
+// first are walked in order, each starting where the previous one ended.
+template <int NRT, bool SPARSE>
+__device__ __forceinline__ void decode_replanned(const DecodeArgs& a, MLA_LDS uint8_t* lds, MetaView v, int wg) {
+  constexpr int kOffCu = 1024, kOffNe = kOffCu + 4 * (kPlanLdsBatch + 1), kOffRed = kOffNe + 4 * (kPlanLdsBatch + 1);
+  constexpr int kOffBp = kOffRed + 32, kOffBc = kOffBp + 4 * (kPlanLdsWg + 1), kOffErr = kOffBc + 4 * (kPlanLdsWg + 1);
+  constexpr int kOffShare = kOffErr + 4;
+  static_assert(kOffShare + 4 * kShareWords <= kRingScratch, "the planner's LDS fits the ring");
+  const PlanLds L{(int32_t*)(lds), (int32_t*)(lds + kOffCu), (int32_t*)(lds + kOffNe), (int64_t*)(lds + kOffRed),
+                  (int32_t*)(lds + kOffBp), (int32_t*)(lds + kOffBc), (int32_t*)(lds + kOffErr),
+                  (int32_t*)(lds + kOffShare)};
+  const PlanParams p{a.seqlens, a.batch, a.rows, a.row_split, (int)gridDim.x, a.plan_min_blocks, a.max_blocks,
+                     a.plan_max_partials, a.plan_fixed_blocks, a.plan_split_rule, a.plan_seg_cost, a.plan_uniform_len};
+  int sh[kShareWords];
+  if (!plan_share_wave(p, v, wg == 0, wg, sh)) {   // the general case: the block-wide computation
+    plan_core<true>(p, L, v, wg == 0, wg);
+#pragma unroll
+    for (int k = 0; k < kShareWords; ++k) sh[k] = L.share[k];
+    __syncthreads();   // every wave has its share before the segments reuse the LDS
+  }
+  // the share as scalars (uniform over the workgroup)
+  auto word = [&](int k) { return __builtin_amdgcn_readfirstlane(sh[k]); };
+  if (wg >= word(kShareNumWg)) return;
+  const int u_first = word(kShareUFirst), ns_first = word(kShareNsFirst);
+  const int fw_first = word(kShareFirstWgFirst), poff_first = word(kSharePoffFirst);
+  const int u_last = word(kShareULast), ns_last = word(kShareNsLast);
+  const int fw_last = word(kShareFirstWgLast), poff_last = word(kSharePoffLast);
+  const int rs = a.row_split;
+  const int end = word(kShareEnd);
+  int pos = word(kSharePos);
+  int u = u_first;
+  int unit_start = word(kShareStartFirst), nb = word(kShareNbFirst);
+  while (pos < end) {
+    const int b = u / rs, g = u - b * rs;
+    const int blk_lo = pos - unit_start, blk_hi = min(end - unit_start, nb);
+    int slot = -1;
+    if (u == u_first) {
+      if (ns_first > 1) slot = poff_first + (wg - fw_first);
+    } else if (u == u_last) {
+      if (ns_last > 1) slot = poff_last + (wg - fw_last);
+    }
+    if constexpr (NRT == 4 && !SPARSE) decode_segment_cols(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    else decode_segment_wide<NRT, SPARSE>(a, lds, b, g * a.rows_per_wg, blk_lo, blk_hi, slot);
+    pos = unit_start + blk_hi;
+    while (pos < end) {              // the next unit with blocks
+      ++u;
+      nb = plan_blocks(a, u / rs);
+      if (nb > 0) break;
+    }
+    unit_start = pos;
+  }
+}
+
 // ===== kernel ==========================================================================
 // NRT = 32-row tiles per workgroup (1, 2 or 4).
 template <int NRT, bool SPARSE>
@@ -1326,6 +1390,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   // neighbours (the splits of one sequence) are made to share an XCD and its L2.
   int wg = blockIdx.x;
   if (planned && (gridDim.x & 7) == 0) wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (planned && a.plan_in_decode) {
+    decode_replanned<NRT, SPARSE>(a, lds, v, wg);
+    return;
+  }
   int pos = 0, end = 1;                       // unsplit: one segment, the whole sequence
   int first_seq = -1;
   if (planned) {

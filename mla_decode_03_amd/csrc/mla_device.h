@@ -121,14 +121,22 @@ __device__ __forceinline__ void lds_barrier() {
 // Block-wide exclusive scan of one value per thread (256 threads = 4 waves): a scan
 // inside each wave, then the wave totals through LDS.  Returns the exclusive prefix and
 // writes the block total to *total.
+// Inclusive sum over a wave's 64 lanes with DPP moves (no LDS): shifts by 1, 2, 4 and 8
+// inside each 16-lane row, then the last lane of row 0 into row 1 and of row 2 into row 3,
+// then lane 31 into rows 2 and 3.  Lanes with no source add 0.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s, int32_t* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int32_t x = wave_inclusive_sum(v);
   if (lane == 63) s[wv] = x;
   lds_barrier();
   int32_t base = 0;

@@ -10,6 +10,24 @@ namespace mla {
 constexpr int kPlanLdsBatch = 4095;   // batches up to this size keep cu_blocks in LDS
 constexpr int kPlanLdsWg = 1024;      // plans up to this many workgroups keep both cuts in LDS
 
+// Block-wide maximum of one non-negative int32 per thread (256 threads); every thread gets
+// it.  The wave's maximum with DPP moves (an inclusive max-scan, lane 63 read), then the
+// four waves' through LDS.
+__device__ inline int32_t block_max_nonneg(int32_t x, int64_t* s) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));   // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));   // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));   // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));   // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  x = __builtin_amdgcn_readlane(x, 63);
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
+  lds_barrier();
+  const int64_t r = max(max(s[0], s[1]), max(s[2], s[3]));
+  lds_barrier();  // s is reused by the next call
+  return (int32_t)r;
+}
+
 // Block-wide maximum of one int64 per thread (256 threads); every thread gets it.
 __device__ inline int64_t block_max(int64_t x, int64_t* s) {
 #pragma unroll
@@ -27,6 +45,7 @@ __device__ inline int64_t block_max(int64_t x, int64_t* s) {
 // floor(n / d) for 0 <= n < 2^53, 0 < d < 2^31: a double quotient, corrected to the
 // exact integer (the rounded quotient is off by at most one).
 __device__ inline int64_t floor_div(int64_t n, int64_t d) {
+  if (((n | d) >> 31) == 0) return (int64_t)((uint32_t)n / (uint32_t)d);   // both under 2^31
   int64_t q = (int64_t)((double)n / (double)d);
   if (q * d > n) --q;
   else if ((q + 1) * d <= n) ++q;
@@ -208,7 +227,7 @@ __device__ inline void plan_core(const PlanParams& p, const PlanLds& L, MetaView
       }
   } else {
     if (total > 0) {
-      num_wg = (total + min_blocks - 1) / min_blocks;
+      num_wg = floor_div(total + min_blocks - 1, min_blocks);
       if (num_wg > grid_wg) num_wg = grid_wg;
       if (num_wg < 1) num_wg = 1;
     }
@@ -267,10 +286,10 @@ __device__ inline void plan_core(const PlanParams& p, const PlanLds& L, MetaView
     int64_t worst_p = 0, worst_c = 0;
     bool evaluate = split_rule == kRuleAuto && num_wg > 0;
     if (evaluate) {
-      const int64_t nbm = block_max(nb_max, s_red);
-      const int64_t share = total / num_wg;
+      const int64_t nbm = block_max_nonneg((int32_t)nb_max, s_red);   // nb_max <= max_blocks
+      const int64_t share = floor_div(total, num_wg);
       if ((int64_t)carry == nbm * ne_carry && share * num_wg == total && nbm > 0 &&
-          (share % nbm == 0 || nbm % share == 0))
+          (share == floor_div(share, nbm) * nbm || nbm == floor_div(nbm, share) * share))
         evaluate = false;
     }
     const bool cuts_in_lds = evaluate && num_wg <= kPlanLdsWg;
@@ -328,18 +347,26 @@ __device__ inline void plan_core(const PlanParams& p, const PlanLds& L, MetaView
     // my workgroup's range and the units of its first and last blocks (uniform values)
     int64_t my_pos = total, my_end = total;
     int u_first = -1, u_last = -1;
-    auto unit_of = [&](int64_t q) -> int {
-      const int b = seq_of_block(q);
-      const int64_t nb = cu_at(b + 1) - cu_at(b);
-      return b * rs + (rs == 1 ? 0 : (int)floor_div(q - rs * cu_at(b), nb));
-    };
     if (my_wg >= 0 && my_wg < num_wg) {
       my_pos = use_cost ? cut_c(my_wg) : cut_p(my_wg);
       my_end = use_cost ? cut_c(my_wg + 1) : cut_p(my_wg + 1);
-      if (my_pos < my_end) {
-        u_first = unit_of(my_pos);
-        u_last = unit_of(my_end - 1);
+    }
+    if (my_pos < my_end) {   // (uniform) the sequences of both ends counted over the block:
+      // the largest b with rs * cu[b] <= q is the count of such b, less one
+      int32_t cnt = 0;
+      for (int b = t; b < batch; b += 256) {
+        const int64_t cb = rs * cu_at(b);
+        cnt += (cb <= my_pos ? 1 : 0) + (cb <= my_end - 1 ? 1 << 16 : 0);
       }
+      int32_t tot;
+      block_exclusive_scan(cnt, s_scan, &tot);
+      const int bf = (tot & 0xffff) - 1, bl = (tot >> 16) - 1;
+      auto unit_in = [&](int b, int64_t q) -> int {
+        const int64_t nb = cu_at(b + 1) - cu_at(b);
+        return b * rs + (rs == 1 ? 0 : (int)floor_div(q - rs * cu_at(b), nb));
+      };
+      u_first = unit_in(bf, my_pos);
+      u_last = unit_in(bl, my_end - 1);
     }
     if (my_wg >= 0 && t == 0) {
       s_share[kSharePos] = (int32_t)my_pos;
@@ -442,6 +469,125 @@ __device__ inline void plan_core(const PlanParams& p, const PlanLds& L, MetaView
     if (refuse) v.hdr[kHdrNumWg] = 0;  // refuse to run a plan that overflows
   }
   lds_barrier();   // the share words are complete
+}
+
+
+// The common case of a re-planning decode, computed by each wave on its own with wave-wide
+// operations (no LDS, no barrier): at most 64 sequences, no row split, no fixed chunks,
+// and the equal-share cut (forced, or the cost model's choice when every non-empty
+// sequence holds the same number of blocks and the shares line up with them, where
+// plan_core keeps it without evaluating).  Lane b holds sequence b.  Gives the same plan
+// as plan_core; write: also store it into v (as plan_core does inside a decode launch).
+// Returns false, with nothing written, when the case does not apply.
+__device__ inline bool plan_share_wave(const PlanParams& p, MetaView v, bool write, int my_wg, int32_t* sh) {
+  const int lane = threadIdx.x & 63;
+  const int B = p.batch;
+  if (B > 64 || p.row_split != 1 || p.fixed_blocks > 0 || p.split_rule == kRuleCost) return false;
+  int err = 0;
+  int32_t n = 0;
+  if (lane < B) {
+    int64_t L = p.uniform_len > 0 ? p.uniform_len : p.seqlens[lane];
+    if (L < 0) { L = 0; err = 1; }
+    int64_t nn = (L + kPage - 1) / kPage;
+    if (nn > p.max_blocks) { nn = p.max_blocks; err = 1; }
+    n = (int32_t)nn;
+  }
+  const int32_t incl = wave_inclusive_sum(n), excl = incl - n;
+  const int32_t total = __builtin_amdgcn_readlane(incl, 63);
+  const int32_t ne_carry = __builtin_amdgcn_readlane(wave_inclusive_sum(n > 0 ? 1 : 0), 63);
+  int32_t mx = n;   // the largest sequence
+  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x111, 0xf, 0xf, true));
+  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x112, 0xf, 0xf, true));
+  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x114, 0xf, 0xf, true));
+  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x118, 0xf, 0xf, true));
+  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x142, 0xa, 0xf, false));
+  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x143, 0xc, 0xf, false));
+  const int32_t nbm = __builtin_amdgcn_readlane(mx, 63);
+  int32_t num_wg = 0;
+  if (total > 0) num_wg = max(1, min(p.grid_wg, (int32_t)floor_div((int64_t)total + p.min_blocks - 1, p.min_blocks)));
+  if (p.split_rule == kRuleAuto && num_wg > 0) {   // must be the even case plan_core skips
+    const int64_t share = floor_div(total, num_wg);
+    const bool even = (int64_t)total == (int64_t)nbm * ne_carry && share * num_wg == total && nbm > 0 &&
+                      (share == floor_div(share, nbm) * nbm || nbm == floor_div(nbm, share) * share);
+    if (!even) return false;
+  }
+  auto cut = [&](int64_t w) -> int64_t { return (w <= num_wg && num_wg > 0) ? floor_div(w * total, num_wg) : total; };
+  auto holder = [&](int64_t q) -> int32_t { return wg_of(q, total, num_wg); };
+  // lane u's unit: its workgroups and partial slots
+  int32_t ns = 0, first = -1;
+  if (n > 0) {
+    first = holder(excl);
+    ns = holder((int64_t)excl + n - 1) - first + 1;
+  }
+  const int32_t pincl = wave_inclusive_sum(ns > 1 ? ns : 0), poff = pincl - (ns > 1 ? ns : 0);
+  const int32_t num_partials = __builtin_amdgcn_readlane(pincl, 63);
+  const bool refuse = num_partials > p.max_partials;
+  const bool any_err = __builtin_amdgcn_ballot_w64(err != 0) != 0 || num_partials > p.max_partials;
+  // my range and the sequences of its two ends
+  const int64_t pos = my_wg < num_wg ? cut(my_wg) : total, end = my_wg < num_wg ? cut(my_wg + 1) : total;
+  int uf = -1, ul = -1;
+  if (pos < end) {
+    uf = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < B && excl <= pos)) - 1;
+    ul = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < B && excl <= end - 1)) - 1;
+  }
+  sh[kSharePos] = (int32_t)pos;
+  sh[kShareEnd] = (int32_t)end;
+  sh[kShareUFirst] = uf;
+  sh[kShareULast] = ul;
+  sh[kShareNumWg] = refuse ? 0 : num_wg;
+  sh[kShareErr] = any_err ? 1 : 0;
+  if (uf >= 0) {
+    sh[kShareNsFirst] = __builtin_amdgcn_readlane(ns, uf);
+    sh[kShareFirstWgFirst] = __builtin_amdgcn_readlane(first, uf);
+    sh[kSharePoffFirst] = __builtin_amdgcn_readlane(poff, uf);
+    sh[kShareStartFirst] = __builtin_amdgcn_readlane(excl, uf);
+    sh[kShareNbFirst] = __builtin_amdgcn_readlane(n, uf);
+    sh[kShareNsLast] = __builtin_amdgcn_readlane(ns, ul);
+    sh[kShareFirstWgLast] = __builtin_amdgcn_readlane(first, ul);
+    sh[kSharePoffLast] = __builtin_amdgcn_readlane(poff, ul);
+  }
+  if (write) {   // the plan, as plan_core stores it; the waves split the per-workgroup words
+    const int wv = threadIdx.x >> 6;
+    if (wv == 0) {
+      if (lane < B) {
+        v.cu_blocks[lane] = excl;
+        v.num_splits[lane] = ns;
+        v.first_wg[lane] = first;
+        v.part_off[lane] = poff;
+      }
+      if (lane == 0) {
+        v.cu_blocks[B] = total;
+        v.hdr[kHdrMagic] = kMetaMagic;
+        v.hdr[kHdrBatch] = B;
+        v.hdr[kHdrRows] = p.rows;
+        v.hdr[kHdrRowSplit] = 1;
+        v.hdr[kHdrRowsPerWg] = p.rows;
+        v.hdr[kHdrNumWg] = refuse ? 0 : num_wg;
+        v.hdr[kHdrGridWg] = p.grid_wg;
+        v.hdr[kHdrTotal] = total;
+        v.hdr[kHdrNumPartials] = num_partials;
+        if (any_err) v.hdr[kHdrError] = 1;   // other workgroups may already have raised it
+        v.hdr[kHdrMaxPartials] = p.max_partials;
+        v.hdr[kHdrMaxBlocks] = p.max_blocks;
+        v.hdr[kHdrRule] = kRulePages;
+        v.hdr[kHdrCostPages] = 0;
+        v.hdr[kHdrCostBalanced] = 0;
+        v.hdr[kHdrSegCost] = p.seg_cost;
+      }
+    }
+    int32_t* wg_seq = meta_wg_seq(v, p.grid_wg);
+    for (int w = threadIdx.x; w <= p.grid_wg; w += 256) {
+      const int64_t begin = cut(w);
+      v.wg_begin[w] = (int32_t)begin;
+      if (w < p.grid_wg) {
+        int seq = 0;
+        if (w < num_wg && begin < total)   // the largest b with cu[b] <= begin
+          for (int k = 1; k < B; ++k) seq += __builtin_amdgcn_readlane(excl, k) <= begin ? 1 : 0;
+        wg_seq[w] = seq;
+      }
+    }
+  }
+  return true;
 }
 
 }  // namespace mla

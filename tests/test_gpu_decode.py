@@ -280,6 +280,53 @@ def test_device_plan_matches_mirror():
         assert list(words[16:16 + len(arrays)]) == arrays
 
 
+@pytest.mark.parametrize("kind", ["auto", "pages", "cost", "row_split2", "fixed", "h16", "sparse", "even"])
+def test_plan_in_decode_matches_planner(kind):
+    """A plan made with plan_in_decode = 1 and reused: every decode launch re-plans from the
+    lengths it is given.  Its outputs equal the planner-kernel path's bit for bit, the
+    metadata it leaves for the combine equals the CPU mirror's words, and a later step
+    with other lengths (same plan object) equals a fresh plan for those lengths."""
+    import torch
+    import mla_decode_03_amd as mla
+    from mla_inputs import make_topk_indices
+    from plan_mirror import make_plan, to_words
+    rng = np.random.default_rng(71)
+    H = 16 if kind == "h16" else 128
+    lens = [int(x) for x in rng.integers(0, 3000, size=23)]
+    lens[3] = 0
+    if kind == "even":       # every sequence 16 blocks, shares of 4 blocks: the equal-share cut
+        lens = [1000] * 40
+    case = _case(len(lens), 1, H, lens, seed=72, extra_pages=40)
+    say("plan in decode", kind)
+    q, kv, bt, lt = to_device(case)
+    base = dict(num_workgroups=160 if kind == "even" else 96, min_blocks_per_wg=2)
+    base.update({"auto": {}, "pages": dict(split_rule=1), "cost": dict(split_rule=2), "row_split2": dict(row_split=2),
+                 "fixed": dict(fixed_split_blocks=5), "h16": {}, "sparse": {}, "even": {}}[kind])
+    topk, ix = 0, None
+    if kind == "sparse":
+        idx = make_topk_indices(case.cache_seqlens, case.q_len, 100, seed=3)
+        topk, ix = 100, torch.from_numpy(idx).to(q.device)
+    fused = mla.Decoder(q, kv, bt, options=mla.PlanOptions(plan_in_decode=1, **base), num_cus=256, topk=topk)
+    plain = mla.Decoder(q, kv, bt, options=mla.PlanOptions(**base), num_cus=256, topk=topk)
+    later = [max(0, x - 700) for x in lens] if kind != "even" else [x + 24 for x in lens]
+    for step, lv in enumerate((lens, later)):
+        lt2 = torch.tensor(lv, dtype=torch.int32, device=q.device)
+        o1, l1 = fused(q, kv, bt, lt2, case.scale, indices=ix)
+        o2, l2 = plain(q, kv, bt, lt2, case.scale, indices=ix)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), (kind, step)
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), (kind, step)
+        if kind != "sparse":
+            words = fused.metadata.view(torch.int32).cpu().numpy()
+            ref = make_plan(lv, row_split=base.get("row_split", 1), grid_wg=fused.plan.grid_wg,
+                            min_blocks=base["min_blocks_per_wg"], max_blocks=case.block_table.shape[1],
+                            rule={0: "auto", 1: "pages", 2: "cost"}[base.get("split_rule", 0)],
+                            fixed_blocks=base.get("fixed_split_blocks", 0), rows=H)
+            hdr, arrays = to_words(ref, fused.plan.grid_wg, H, fused.plan.max_partials, case.block_table.shape[1])
+            assert list(words[:16]) == hdr, (kind, step)
+            assert list(words[16:16 + len(arrays)]) == arrays, (kind, step)
+
+
 @pytest.mark.parametrize("rule", [0, 1, 2])
 def test_device_plan_rules_match_mirror(rule):
     """Both partition rules and the cost model's choice, bit for bit against the mirror:
