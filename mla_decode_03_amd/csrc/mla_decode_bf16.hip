@@ -1338,8 +1338,13 @@ __device__ __forceinline__ void decode_replanned(const DecodeArgs& a, MLA_LDS ui
                   (int32_t*)(lds + kOffShare)};
   const PlanParams p{a.seqlens, a.batch, a.rows, a.row_split, (int)gridDim.x, a.plan_min_blocks, a.max_blocks,
                      a.plan_max_partials, a.plan_fixed_blocks, a.plan_split_rule, a.plan_seg_cost, a.plan_uniform_len};
+  static_assert(4 * 4 * kScatterLdsWords <= kRingScratch, "four waves' scatter tables fit the ring");
   int sh[kShareWords];
-  if (!plan_share_wave(p, v, wg == 0, wg, sh)) {   // the general case: the block-wide computation
+  if (plan_share_wave(p, v, wg == 0, wg, sh)) {
+    // even batches of up to 64 sequences: registers only
+  } else if (plan_share_scatter(p, v, wg == 0, wg, sh, (MLA_LDS int32_t*)lds + (threadIdx.x >> 6) * kScatterLdsWords)) {
+    __syncthreads();   // ragged batches of up to 256: every wave is done with its tables before the ring
+  } else {   // the general case: the block-wide computation
     plan_core<true>(p, L, v, wg == 0, wg);
 #pragma unroll
     for (int k = 0; k < kShareWords; ++k) sh[k] = L.share[k];

@@ -10,17 +10,22 @@ namespace mla {
 constexpr int kPlanLdsBatch = 4095;   // batches up to this size keep cu_blocks in LDS
 constexpr int kPlanLdsWg = 1024;      // plans up to this many workgroups keep both cuts in LDS
 
-// Block-wide maximum of one non-negative int32 per thread (256 threads); every thread gets
-// it.  The wave's maximum with DPP moves (an inclusive max-scan, lane 63 read), then the
-// four waves' through LDS.
-__device__ inline int32_t block_max_nonneg(int32_t x, int64_t* s) {
+// Wave-wide maximum of one non-negative int32 per lane, in every lane: an inclusive
+// max-scan with DPP moves (lanes with no source take 0), lane 63 read.
+__device__ inline int32_t wave_max_nonneg(int32_t x) {
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));   // row_shr:1
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));   // row_shr:2
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));   // row_shr:4
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));   // row_shr:8
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
-  x = __builtin_amdgcn_readlane(x, 63);
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Block-wide maximum of one non-negative int32 per thread (256 threads); every thread gets
+// it: the wave's maximum, then the four waves' through LDS.
+__device__ inline int32_t block_max_nonneg(int32_t x, int64_t* s) {
+  x = wave_max_nonneg(x);
   if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
   lds_barrier();
   const int64_t r = max(max(s[0], s[1]), max(s[2], s[3]));
@@ -495,14 +500,7 @@ __device__ inline bool plan_share_wave(const PlanParams& p, MetaView v, bool wri
   const int32_t incl = wave_inclusive_sum(n), excl = incl - n;
   const int32_t total = __builtin_amdgcn_readlane(incl, 63);
   const int32_t ne_carry = __builtin_amdgcn_readlane(wave_inclusive_sum(n > 0 ? 1 : 0), 63);
-  int32_t mx = n;   // the largest sequence
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x111, 0xf, 0xf, true));
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x112, 0xf, 0xf, true));
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x114, 0xf, 0xf, true));
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x118, 0xf, 0xf, true));
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x142, 0xa, 0xf, false));
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x143, 0xc, 0xf, false));
-  const int32_t nbm = __builtin_amdgcn_readlane(mx, 63);
+  const int32_t nbm = wave_max_nonneg(n);   // the largest sequence
   int32_t num_wg = 0;
   if (total > 0) num_wg = max(1, min(p.grid_wg, (int32_t)floor_div((int64_t)total + p.min_blocks - 1, p.min_blocks)));
   if (p.split_rule == kRuleAuto && num_wg > 0) {   // must be the even case plan_core skips
@@ -585,6 +583,254 @@ __device__ inline bool plan_share_wave(const PlanParams& p, MetaView v, bool wri
           for (int k = 1; k < B; ++k) seq += __builtin_amdgcn_readlane(excl, k) <= begin ? 1 : 0;
         wg_seq[w] = seq;
       }
+    }
+  }
+  return true;
+}
+
+// Cuts one sequence may hold, under either rule, in plan_share_scatter's form.
+constexpr int kScatterMaxCuts = 64;
+// LDS words plan_share_scatter takes per wave: the cuts of each rule and the owner of each
+// cut (kPlanLdsWg + 1 words each), and the sequence of each non-empty rank (256 words).
+constexpr int kScatterLdsWords = 4 * (kPlanLdsWg + 1) + 256;
+
+// The re-planning decode's form for ragged batches: at most 256 sequences (lane l holds
+// sequences l, l + 64, l + 128, l + 192), no row split, no fixed chunks, either rule or the
+// cost model's choice between them.  Computed by each wave on its own, in its own LDS
+// (tab: kScatterLdsWords words, private to the wave; no barrier inside, the caller
+// barriers before the LDS is reused).  Instead of searching the sequences for the holder
+// of each cut, every sequence writes the cuts that land in it, in closed form: under the
+// equal-share rule the cuts w*total/num_wg inside its blocks, under the cost rule the cuts
+// w*ctot/num_wg inside its stretch of the cost axis (its c quarters of overhead, then 4 per
+// block).  Each cut is written with its owner's sequence, rank among the non-empty
+// sequences, and whether it falls on the owner's first block; a workgroup then touches
+// the units from its first cut's owner to the owner of its last block, which gives the
+// busiest workgroup of each rule with no search.  Same plan as plan_core.  Returns false,
+// with nothing written, when the case does not apply: more sequences, row split, fixed
+// chunks, more than kPlanLdsWg workgroups, a cost axis whose products with num_wg reach
+// 2^31, or a sequence holding more than kScatterMaxCuts cuts.
+__device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool write, int my_wg, int32_t* sh,
+                                          MLA_LDS int32_t* tab) {
+  const int lane = threadIdx.x & 63;
+  const int B = p.batch;
+  if (B > 256 || p.row_split != 1 || p.fixed_blocks > 0) return false;
+  const int nk = (B + 63) >> 6;   // sequences per lane
+  int err = 0;
+  int32_t n[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    n[k] = 0;
+    const int b = lane + 64 * k;
+    if (k < nk && b < B) {
+      int64_t L = p.uniform_len > 0 ? p.uniform_len : p.seqlens[b];
+      if (L < 0) { L = 0; err = 1; }
+      int64_t nn = (L + kPage - 1) / kPage;
+      if (nn > p.max_blocks) { nn = p.max_blocks; err = 1; }
+      n[k] = (int32_t)nn;
+    }
+  }
+  // first blocks (prefix sums) and ranks among the non-empty sequences, in sequence order
+  int32_t s[4], r[4];
+  int32_t total = 0, ne = 0, mx = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    s[k] = total;
+    r[k] = ne;
+    if (k < nk) {
+      const int32_t incl = wave_inclusive_sum(n[k]);
+      s[k] = total + incl - n[k];
+      total += __builtin_amdgcn_readlane(incl, 63);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(n[k] > 0);
+      r[k] = ne + (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      ne += (int32_t)__builtin_popcountll(m);
+      mx = max(mx, n[k]);
+    }
+  }
+  const int32_t nbm = wave_max_nonneg(mx);
+  int32_t num_wg = 0;
+  if (total > 0) num_wg = max(1, min(p.grid_wg, (int32_t)floor_div((int64_t)total + p.min_blocks - 1, p.min_blocks)));
+  const int32_t c = p.seg_cost;
+  const int64_t ctot64 = 4 * (int64_t)total + (int64_t)c * ne;   // length of the cost axis
+  if (num_wg > kPlanLdsWg || ctot64 * num_wg >= ((int64_t)1 << 31) || c < 0) return false;
+  // below, every product with num_wg stays under 2^31: 32-bit unsigned arithmetic
+  const uint32_t T = (uint32_t)total, C = (uint32_t)ctot64, W = (uint32_t)num_wg, uc = (uint32_t)c;
+  bool evaluate = p.split_rule == kRuleAuto && num_wg > 0;
+  if (evaluate) {   // the even case plan_core keeps without evaluating
+    const uint32_t share = T / W;
+    if (T == (uint32_t)nbm * (uint32_t)ne && share * W == T && nbm > 0 &&
+        (share % (uint32_t)nbm == 0 || (uint32_t)nbm % share == 0))
+      evaluate = false;
+  }
+  const bool need_p = num_wg > 0 && p.split_rule != kRuleCost;
+  const bool need_c = num_wg > 0 && (p.split_rule == kRuleCost || evaluate);
+  // the cuts landing in each sequence: [pw0, pw1) equal-share, [cw0, cw1) cost
+  uint32_t pw0[4], pw1[4], cw0[4], cw1[4], cs[4];
+  int32_t most = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pw0[k] = pw1[k] = cw0[k] = cw1[k] = 0;
+    cs[k] = 4 * (uint32_t)s[k] + uc * (uint32_t)r[k];
+    if (k < nk && n[k] > 0) {
+      if (need_p) {
+        pw0[k] = ((uint32_t)s[k] * W + T - 1) / T;
+        pw1[k] = ((uint32_t)(s[k] + n[k]) * W + T - 1) / T;
+      }
+      if (need_c) {
+        cw0[k] = (cs[k] * W + C - 1) / C;
+        cw1[k] = ((cs[k] + uc + 4 * (uint32_t)n[k]) * W + C - 1) / C;
+      }
+      most = max(most, (int32_t)max(pw1[k] - pw0[k], cw1[k] - cw0[k]));
+    }
+  }
+  if (wave_max_nonneg(most) > kScatterMaxCuts) return false;
+
+  constexpr int kW = kPlanLdsWg + 1;
+  MLA_LDS int32_t* cut_p = tab;
+  MLA_LDS int32_t* own_p = tab + kW;
+  MLA_LDS int32_t* cut_c = tab + 2 * kW;
+  MLA_LDS int32_t* own_c = tab + 3 * kW;
+  MLA_LDS int32_t* seq_of_rank = tab + 4 * kW;
+  // owner word: sequence (bits 0-11), rank (12-23), cut on the owner's first block (24)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k < nk && n[k] > 0) {
+      const int b = lane + 64 * k;
+      seq_of_rank[r[k]] = b;
+      const int32_t own = b | (r[k] << 12);
+      for (uint32_t w = pw0[k]; w < pw1[k]; ++w) {
+        const uint32_t cut = w * T / W;
+        cut_p[w] = (int32_t)cut;
+        own_p[w] = own | ((cut == (uint32_t)s[k]) << 24);
+      }
+      for (uint32_t w = cw0[k]; w < cw1[k]; ++w) {
+        const uint32_t off = w * C / W - cs[k];
+        const uint32_t cut = (uint32_t)s[k] + (off < uc ? 0 : (off - uc) >> 2);
+        cut_c[w] = (int32_t)cut;
+        own_c[w] = own | ((cut == (uint32_t)s[k]) << 24);
+      }
+    }
+  }
+  if (lane == 0 && num_wg > 0) {   // the end: past the last non-empty rank
+    cut_p[num_wg] = cut_c[num_wg] = total;
+    own_p[num_wg] = own_c[num_wg] = B | (ne << 12) | (1 << 24);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // lanes read each other's words below
+  // the busiest workgroup of each rule: 4 per block plus c per unit touched
+  auto range_cost = [&](MLA_LDS const int32_t* cut, MLA_LDS const int32_t* own, int w) -> int32_t {
+    const int32_t lo = cut[w], hi = cut[w + 1];
+    if (hi <= lo) return 0;
+    const int32_t o0 = own[w], o1 = own[w + 1];
+    const int32_t first = (o0 >> 12) & 0xfff, last = ((o1 >> 12) & 0xfff) - ((o1 >> 24) & 1);
+    return 4 * (hi - lo) + c * (last - first + 1);
+  };
+  int32_t worst_p = 0, worst_c = 0;
+  if (evaluate) {
+    for (int w = lane; w < num_wg; w += 64) {
+      worst_p = max(worst_p, range_cost(cut_p, own_p, w));
+      worst_c = max(worst_c, range_cost(cut_c, own_c, w));
+    }
+    worst_p = wave_max_nonneg(worst_p);
+    worst_c = wave_max_nonneg(worst_c);
+  }
+  const bool use_cost = p.split_rule == kRuleCost || (evaluate && worst_c < worst_p);
+  MLA_LDS const int32_t* cut = use_cost ? cut_c : cut_p;
+  MLA_LDS const int32_t* own = use_cost ? own_c : own_p;
+  // each sequence's workgroups (the holders of its first and last blocks) and partial slots
+  int32_t ns[4], fw[4], po[4];
+  int32_t num_partials = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ns[k] = 0;
+    fw[k] = -1;
+    po[k] = num_partials;
+    if (k < nk) {
+      if (n[k] > 0) {
+        auto holder = [&](uint32_t q) -> int32_t {   // the workgroup holding block q of this sequence
+          if (!use_cost) return (int32_t)(((q + 1) * W - 1) / T);
+          const uint32_t y = cs[k] + uc + 4 * (q - (uint32_t)s[k]) + 4;   // cost position just past block q
+          return (int32_t)min((y * W - 1) / C, W - 1);
+        };
+        fw[k] = holder((uint32_t)s[k]);
+        ns[k] = holder((uint32_t)(s[k] + n[k] - 1)) - fw[k] + 1;
+      }
+      const int32_t x = ns[k] > 1 ? ns[k] : 0;
+      const int32_t incl = wave_inclusive_sum(x);
+      po[k] = num_partials + incl - x;
+      num_partials += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  const bool refuse = num_partials > p.max_partials;
+  const bool any_err = __builtin_amdgcn_ballot_w64(err != 0) != 0 || refuse;
+  // my range, its first block's sequence and its last block's
+  int32_t pos = total, end = total, uf = -1, ul = -1;
+  if (my_wg < num_wg) {
+    pos = __builtin_amdgcn_readfirstlane(cut[my_wg]);
+    end = __builtin_amdgcn_readfirstlane(cut[my_wg + 1]);
+  }
+  if (pos < end) {
+    const int32_t o0 = __builtin_amdgcn_readfirstlane(own[my_wg]);
+    const int32_t o1 = __builtin_amdgcn_readfirstlane(own[my_wg + 1]);
+    uf = o0 & 0xfff;
+    ul = ((o1 >> 24) & 1) ? __builtin_amdgcn_readfirstlane(seq_of_rank[((o1 >> 12) & 0xfff) - 1]) : (o1 & 0xfff);
+  }
+  auto pick = [&](const int32_t (&x)[4], int u) -> int32_t {   // sequence u's word (u uniform)
+    const int k = u >> 6;
+    const int32_t y = k == 0 ? x[0] : k == 1 ? x[1] : k == 2 ? x[2] : x[3];
+    return __builtin_amdgcn_readlane(y, u & 63);
+  };
+  sh[kSharePos] = pos;
+  sh[kShareEnd] = end;
+  sh[kShareUFirst] = uf;
+  sh[kShareULast] = ul;
+  sh[kShareNumWg] = refuse ? 0 : num_wg;
+  sh[kShareErr] = any_err ? 1 : 0;
+  if (uf >= 0) {
+    sh[kShareNsFirst] = pick(ns, uf);
+    sh[kShareFirstWgFirst] = pick(fw, uf);
+    sh[kSharePoffFirst] = pick(po, uf);
+    sh[kShareStartFirst] = pick(s, uf);
+    sh[kShareNbFirst] = pick(n, uf);
+    sh[kShareNsLast] = pick(ns, ul);
+    sh[kShareFirstWgLast] = pick(fw, ul);
+    sh[kSharePoffLast] = pick(po, ul);
+  }
+  if (write) {   // the plan, as plan_core stores it: wave k the words of sequences 64k + lane
+    const int wv = threadIdx.x >> 6;
+    const int b = lane + 64 * wv;
+    if (b < B) {
+      const int32_t bs = wv == 0 ? s[0] : wv == 1 ? s[1] : wv == 2 ? s[2] : s[3];
+      const int32_t bns = wv == 0 ? ns[0] : wv == 1 ? ns[1] : wv == 2 ? ns[2] : ns[3];
+      const int32_t bfw = wv == 0 ? fw[0] : wv == 1 ? fw[1] : wv == 2 ? fw[2] : fw[3];
+      const int32_t bpo = wv == 0 ? po[0] : wv == 1 ? po[1] : wv == 2 ? po[2] : po[3];
+      v.cu_blocks[b] = bs;
+      v.num_splits[b] = bns;
+      v.first_wg[b] = bfw;
+      v.part_off[b] = bpo;
+    }
+    if (threadIdx.x == 0) {
+      v.cu_blocks[B] = total;
+      v.hdr[kHdrMagic] = kMetaMagic;
+      v.hdr[kHdrBatch] = B;
+      v.hdr[kHdrRows] = p.rows;
+      v.hdr[kHdrRowSplit] = 1;
+      v.hdr[kHdrRowsPerWg] = p.rows;
+      v.hdr[kHdrNumWg] = refuse ? 0 : num_wg;
+      v.hdr[kHdrGridWg] = p.grid_wg;
+      v.hdr[kHdrTotal] = total;
+      v.hdr[kHdrNumPartials] = num_partials;
+      if (any_err) v.hdr[kHdrError] = 1;   // other workgroups may already have raised it
+      v.hdr[kHdrMaxPartials] = p.max_partials;
+      v.hdr[kHdrMaxBlocks] = p.max_blocks;
+      v.hdr[kHdrRule] = use_cost ? kRuleCost : kRulePages;
+      v.hdr[kHdrCostPages] = worst_p;
+      v.hdr[kHdrCostBalanced] = worst_c;
+      v.hdr[kHdrSegCost] = p.seg_cost;
+    }
+    int32_t* wg_seq = meta_wg_seq(v, p.grid_wg);
+    for (int w = threadIdx.x; w <= p.grid_wg; w += 256) {   // each wave reads its own tables
+      const int32_t begin = (w <= num_wg && num_wg > 0) ? cut[w] : total;
+      v.wg_begin[w] = begin;
+      if (w < p.grid_wg) wg_seq[w] = (w < num_wg && begin < total) ? (own[w] & 0xfff) : 0;
     }
   }
   return true;
