@@ -830,18 +830,32 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
   const int myrow = row0 + 32 * w + lr;
   const float c = a.scale_log2;
 
+  // The sequence's length and the page of half pages 0 and 1 (scalar loads) go out
+  // together, and Q's loads are issued while they are in flight: no vector load waits for
+  // a scalar round trip, and the two round trips overlap.  blk_lo < blk_hi <= max_blocks,
+  // so the entry is inside the block table's row.
+  const int* bt_row = a.block_table + (size_t)b * a.bt_stride;
   const int L = ld_const(a.seqlens, b);
+  const int pg01 = blk_lo < blk_hi ? ld_const(bt_row, blk_lo) : 0;
+  // ---- Q: each lane loads its row's fragments straight into registers (dims 16kk + 8g .. +8
+  // of row myrow: the B operand of S^T = K . Q^T).  A row past the workgroup's reads row
+  // row0; it is scored but never stored.
+  bf16x8 qf[36];
+  {
+    int tq = threadIdx.x;   // opaque: the address is formed here, not kept across the kernel
+    asm volatile("" : "+v"(tq));
+    // a scalar base for the workgroup's rows and a 32-bit lane offset (under 148 KB)
+    const uint8_t* qb = a.q + ((size_t)b * R + row0) * kRowBytes;
+    const int rq = 32 * w + (tq & 31);
+    const uint32_t qo = (uint32_t)((row0 + rq < row_end ? rq : 0) * kRowBytes + 16 * ((tq >> 5) & 1));
+#pragma unroll
+    for (int kk = 0; kk < 36; ++kk) qf[kk] = *(const bf16x8*)(qb + qo + 32 * kk);
+  }
   // more keys than the block table's row can hold: ceil(L / kPage) > max_blocks, in 32 bits
   const bool bad_len = (L < 0) || (L > 0 && (L - 1) / kPage >= a.max_blocks);
   const int Lc = bad_len ? 0 : L;
-  int nvis = Lc;
-  if (a.causal && a.q_len > 1) nvis = Lc - a.q_len + 1 + min(myrow, R - 1) / a.heads;
-  nvis = max(nvis, 0);
-  int nmin = Lc;   // fewest visible keys over the wave's rows: masking starts there
-  if (a.causal && a.q_len > 1) nmin = max(Lc - a.q_len + 1 + min(row0 + 32 * w, R - 1) / a.heads, 0);
   const int hp0 = 2 * blk_lo;                                                   // first half page
   const int H = max(0, (min(blk_hi * kPage, Lc) + kHalf - 1) / kHalf - hp0);   // half pages with keys
-  const int* bt_row = a.block_table + (size_t)b * a.bt_stride;
   bool bad_page = false;
   // P of two half pages after the ring: [half page & 1][row tile][K step][lane] x 16 B.
   // After the page loop the same bytes hold the workgroup-OR words and the row statistics.
@@ -857,30 +871,26 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     if (n < H) {
       int tl = threadIdx.x;
       asm volatile("" : "+v"(tl));
-      const HalfPage h = half_page(a, ld_const(bt_row, (hp0 + n) >> 1), hp0 + n, Lc, bad_page);
+      const HalfPage h = half_page(a, pg01, hp0 + n, Lc, bad_page);
 #pragma unroll
       for (int i = 0; i < 9; ++i) half_copy(h, lds + n * kSlotBytes, i, w, tl & 63);
     }
   };
-  // Half page 0 goes out first, then Q, then half page 1: the first score loop starts once
-  // half page 0 is in (every wave's copies), and each of its steps waits only for its own
-  // Q fragment.  At most 54 loads are in flight per wave, under the 63 the counter holds.
+  // Q's 36 loads, then half pages 0 and 1: the first score loop starts once Q and half page
+  // 0 are in.  At most 54 loads are in flight per wave, under the 63 the counter holds.
   first_copy(0);
-  // ---- Q: each lane loads its row's fragments straight into registers (dims 16kk + 8g .. +8
-  // of row myrow: the B operand of S^T = K . Q^T).  A row past the workgroup's reads row
-  // row0; it is scored but never stored.
-  bf16x8 qf[36];
-  {
-    int tq = threadIdx.x;   // opaque: the address is formed here, not kept across the kernel
-    asm volatile("" : "+v"(tq));
-    // a scalar base for the workgroup's rows and a 32-bit lane offset (under 148 KB)
-    const uint8_t* qb = a.q + ((size_t)b * R + row0) * kRowBytes;
-    const int rq = 32 * w + (tq & 31);
-    const uint32_t qo = (uint32_t)((row0 + rq < row_end ? rq : 0) * kRowBytes + 16 * ((tq >> 5) & 1));
-#pragma unroll
-    for (int kk = 0; kk < 36; ++kk) qf[kk] = *(const bf16x8*)(qb + qo + 32 * kk);
-  }
   first_copy(1);
+  // Causal rows' visible keys, formed here from an opaque copy of the flag (a flag the
+  // compiler kept from the kernel's start was reloaded from scratch right after the copies,
+  // and that reload waited for all of them).
+  int causal = a.causal, qlen = a.q_len;
+  asm volatile("" : "+s"(causal), "+s"(qlen));
+  causal = causal && qlen > 1;
+  int nvis = Lc;
+  if (causal) nvis = Lc - a.q_len + 1 + min(myrow, R - 1) / a.heads;
+  nvis = max(nvis, 0);
+  int nmin = Lc;   // fewest visible keys over the wave's rows: masking starts there
+  if (causal) nmin = max(Lc - a.q_len + 1 + min(row0 + 32 * w, R - 1) / a.heads, 0);
   // lane terms of the K reads (token lr, dims 16kk + 8g) and the transposing V reads
   int ky[4];
 #pragma unroll
@@ -928,14 +938,9 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
       __syncthreads();
     };
-    // The first pass's wait for half page 0: Q's 36 loads, and half page 1's copies, may
-    // still be in flight behind it.
-    auto wait_first = [&]() {
-      if (pass == 1) wait_half(0);
-      else if (1 < H) asm volatile("s_waitcnt vmcnt(45)" : : : "memory");
-      else asm volatile("s_waitcnt vmcnt(36)" : : : "memory");
-      if (pass == 0) __syncthreads();
-    };
+    // The wait for half page 0 (and, in the first pass, Q's loads issued before it): only
+    // half page 1's copies may still be in flight behind it.
+    auto wait_first = [&]() { wait_half(0); };
 
     f32x16 sc;                    // the score chain, then the softmax's terms in place
     u32x4 pn0, pn1;               // the wave's own P (bf16 B operands of the two K steps)
