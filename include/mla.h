@@ -166,13 +166,15 @@ MLA_API size_t mla_metadata_bytes(const mla_problem_t* problem, const mla_plan_o
  * problem/options/num_cus: room for the split partials, and for a sparse problem the
  * lists turned into pool rows (4 bytes per entry, padded to 64 per (b, t), plus a
  * count).  Host-only arithmetic.
- * A split partial row (one row of one split) takes 2052 bytes, and each partial slot
- * 64 more: the row's normalised float32 output o as a compensated pair of bf16 halves,
- * hi = bf16(o) and lo = bf16(o - hi) (2 x 1024 B), its float32 natural-log LSE, and per
- * slot 4 flag bits per row.  The decode always writes hi, and writes lo only for a
- * quarter of a row (128 values) whose largest |o| exceeds 1, setting that quarter's
- * bit; so a partial enters the merge within 2^-8 (hi alone, |o| <= 1) or 2^-16 |o|
- * (hi + lo) of its float32 value, however much a row's partials cancel.
+ * A split partial row (one row of one split) takes 2056 bytes, and each partial slot
+ * 64 more: the row's float32 output before normalisation, u = o / f (f = 1 / the row's
+ * sum of exponentials over the split), as a compensated pair of bf16 halves,
+ * hi = bf16(u) and lo = bf16(u - hi) (2 x 1024 B), its float32 natural-log LSE and f, and
+ * per slot 4 flag bits per row.  The decode always writes hi, and writes lo only for a
+ * quarter of a row (128 values) whose largest normalised |o| exceeds 1, setting that
+ * quarter's bit; the merge scales by f, so a partial enters it within 2^-8 (hi alone,
+ * |o| <= 1) or 2^-16 |o| (hi + lo) of its float32 value, however much a row's partials
+ * cancel.
  */
 MLA_API size_t mla_workspace_bytes(const mla_problem_t* problem, const mla_plan_options_t* options,
                            int32_t num_cus);
@@ -310,7 +312,7 @@ MLA_API int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* v
  * every device the library runs on holds until the process ends.  The caller passes the
  * inputs and outputs only; the call allocates nothing and never synchronises.
  *   - A problem whose default plan needs more metadata or workspace than that (for
- *     128-row problems, more than 544 partial slots, i.e. far more sequences than CUs)
+ *     128-row problems, more than 541 partial slots, i.e. far more sequences than CUs)
  *     returns MLA_ERR_WORKSPACE before anything is enqueued; a sparse problem
  *     (topk > 0) returns MLA_ERR_UNSUPPORTED (its row lists need a caller workspace).
  *   - Every call on a device shares that device's scratch, which keeps the last call's

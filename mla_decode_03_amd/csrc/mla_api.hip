@@ -21,10 +21,11 @@ constexpr int kDefaultMinBlocks = 4;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Split partials, over prow = slots * rows partial rows: the normalised output's bf16
-// high halves [prow, 512]; the fp32 LSEs [prow], padded to 16 bytes; the low-half flags
-// [slots, kLoMaskWords]; the low halves [prow, 512].  The combine reads the first three.
-size_t lse_bytes(size_t prow) { return (prow * sizeof(float) + 15) / 16 * 16; }
+// Split partials, over prow = slots * rows partial rows: the unnormalised output's bf16
+// high halves [prow, 512]; the fp32 (LSE, normalising factor) pairs [prow, 2], padded to
+// 16 bytes; the low-half flags [slots, kLoMaskWords]; the low halves [prow, 512].  The
+// combine reads the first three.
+size_t lse_bytes(size_t prow) { return (prow * 2 * sizeof(float) + 15) / 16 * 16; }
 size_t partial_bytes(int64_t slots, int64_t rows_per_wg) {
   const size_t prow = (size_t)slots * rows_per_wg;
   return 2 * prow * mla::kDv * sizeof(uint16_t) + lse_bytes(prow) + (size_t)slots * mla::kLoMaskWords * sizeof(uint32_t);

@@ -21,7 +21,7 @@ struct DecodeArgs {
   int32_t* meta;               // plan, or nullptr (one workgroup per sequence)
   uint16_t* ws_hi;             // split partials: normalised output rounded to bf16 [slots, rows_per_wg, 512]
   uint16_t* ws_lo;             // bf16(output - hi) [slots, rows_per_wg, 512], written for flagged quarters only
-  float* ws_lse;               // partial log-sum-exp [slots, rows_per_wg]
+  float* ws_lse;               // partial (log-sum-exp, 1 / row sum) [slots, rows_per_wg, 2]
   uint32_t* ws_lo_mask;        // low-half flags [slots, kLoMaskWords]
   const float* sinks;          // attention-sink logits [heads], or nullptr
   const int32_t* sparse_rows;  // sparse: pool rows per unit [units, row_stride], or nullptr

@@ -2,13 +2,13 @@
 //
 // A unit (rows of one sequence) cut across k > 1 workgroups left k partial results
 // (o_s = normalised output over its key range, lse_s = natural-log sum of exp over
-// it).  o_s is stored as its bf16 rounding hi_s, plus lo_s = bf16(o_s - hi_s) for the
+// it).  o_s is stored unnormalised, u_s = o_s / f_s with its factor f_s (1 / row sum)
+// beside lse_s, as the bf16 rounding hi_s of u_s, plus lo_s = bf16(u_s - hi_s) for the
 // quarters of a row (128 values each) whose flag bit says the decode wrote it (quarters
-// with a large |o_s|), so each partial reaches the merge within 0.0039 + 2^-16 |o_s| of
-// its fp32 value.  Over the union of
-// the disjoint ranges:
+// with a large |o_s|), so each f_s * (hi_s + lo_s) reaches the merge within
+// 0.0039 + 2^-16 |o_s| of o_s.  Over the union of the disjoint ranges:
 //     lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s
-//     out = sum_s exp(lse_s - lse) * o_s
+//     out = sum_s exp(lse_s - lse) * f_s * u_s
 // A partial with lse_s = -inf weighs 0; a NaN partial (a poisoned segment) makes the row NaN.  Units with no blocks at all get out = 0,
 // lse = -inf.  Units decoded by one workgroup were written directly and are skipped.
 // With attention sinks the merged row takes its head's sink here (one more softmax term
@@ -60,17 +60,19 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       mw[k] = base + k < ns ? a.ws_lo_mask[(size_t)(s0 + base + k) * kLoMaskWords + (rl0 >> 3)] : 0u;
-    float ls[4];
+    float ls[4], fs[4];
     u32x4 x[4][2], y[4][2];
+    // Past the last split the group reads that split again (no branch around the loads,
+    // whose results would otherwise be waited for where the branches join) and gives it
+    // no weight.
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      ls[k] = -INFINITY;
-      if (base + k < ns) {
-        const size_t pr = prow(base + k);
-        ls[k] = a.ws_lse[pr];
-        x[k][0] = *(const u32x4*)(a.ws_hi + pr * kDv + 8 * t);
-        x[k][1] = *(const u32x4*)(a.ws_hi + pr * kDv + kDv / 2 + 8 * t);
-      }
+      const size_t pr = prow(min(base + k, ns - 1));
+      const float2 lf = *(const float2*)(a.ws_lse + 2 * pr);   // (lse_s, f_s)
+      ls[k] = base + k < ns ? lf.x : -INFINITY;
+      fs[k] = base + k < ns ? lf.y : 0.f;
+      x[k][0] = *(const u32x4*)(a.ws_hi + pr * kDv + 8 * t);
+      x[k][1] = *(const u32x4*)(a.ws_hi + pr * kDv + kDv / 2 + 8 * t);
     }
     // this thread's values 8t .. 8t+7 lie in quarter t/16 of its row, 256+8t .. in 2 + t/16
 #pragma unroll
@@ -101,8 +103,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (base + k < ns) {
-        const float wgt = expf(ls[k] - Ms);
-        tot += wgt;
+        const float e = expf(ls[k] - Ms);
+        tot += e;
+        const float wgt = e * fs[k];   // a poisoned partial's NaN factor makes the row NaN
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll

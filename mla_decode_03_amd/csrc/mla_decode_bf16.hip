@@ -48,18 +48,29 @@ constexpr float kRefSlack = 16.0f;  // scores may exceed the reference max by 2^
 constexpr float kSumCap = 65536.0f; // 2^kRefSlack: a half-row page sum above it flags
 constexpr int kPrefK = 2;           // K-fragment prefetch distance (32-dim steps)
 constexpr int kPrefV = 4;           // V-fragment prefetch distance (16-wide value tiles)
-// A split partial row is stored as its bf16 rounding (hi), which is within 2^-8 |o| of the
-// fp32 value o; each quarter of the row (128 values) whose largest |o| exceeds kLoCut also
-// stores lo = bf16(o - hi), and hi + lo is within 2^-16 |o|.  So a partial the merge reads is never off by more than
-// 2^-8 * kLoCut = 0.0039 plus 2^-16 of its own size, however much the partials of a row
-// cancel in the merge.
+// A split partial row is stored unnormalised, u = o / so (so = 1 / row sum, stored beside
+// its LSE), as its bf16 rounding hi, within 2^-8 |u| of the fp32 value; each quarter of the
+// row (128 values) whose largest normalised |o| exceeds kLoCut also stores lo = bf16(u - hi),
+// and hi + lo is within 2^-16 |u|.  Scaled by so in the merge, a partial is never off by
+// more than 2^-8 * kLoCut = 0.0039 plus 2^-16 of its own size, however much the partials
+// of a row cancel in the merge.
 constexpr float kLoCut = 1.0f;
-// The low half of one row's quarter (the wave's 128 value columns), straight from the
-// accumulators: lane (l/32) of the row's pair holds values 32 t + 8 i + 4 (l/32) .. +3 of
-// tile t, so `dst` points at the quarter's first value plus 4 (l/32), and each 4-value
-// piece is one 8-byte store.  tile(t) gives the accumulator of value tile t (0..3).
+// Compile-time flags and counts passed as tag arguments (one code copy per value).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+// The low half of one row's quarter (the wave's 128 value columns) of an unnormalised split
+// partial, straight from the accumulators: lane (l/32) of the row's pair holds values
+// 32 t + 8 i + 4 (l/32) .. +3 of tile t, so `dst` points at the quarter's first value plus
+// 4 (l/32), and each 4-value piece is one 8-byte store.  tile(t) gives the accumulator of
+// value tile t (0..3).
 template <class Tile>
-__device__ __forceinline__ void store_lo_quarter(uint16_t* dst, float so, Tile tile) {
+__device__ __forceinline__ void store_lo_quarter(uint16_t* dst, Tile tile) {
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
@@ -68,7 +79,7 @@ __device__ __forceinline__ void store_lo_quarter(uint16_t* dst, float so, Tile t
       uint32_t lw[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float x0 = t[4 * i + 2 * h] * so, x1 = t[4 * i + 2 * h + 1] * so;
+        const float x0 = t[4 * i + 2 * h], x1 = t[4 * i + 2 * h + 1];
         const uint32_t hi2 = pack_bf16x2(x0, x1);
         lw[h] = pack_bf16x2(x0 - __uint_as_float(hi2 << 16), x1 - __uint_as_float(hi2 & 0xffff0000u));
       }
@@ -691,38 +702,50 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
     stats[2 * rr + 1] = lse_v;
   }
   __syncthreads();
-  // O (normalised, bf16) goes through LDS so that every store writes a whole 1 KB row:
-  // row rr of the workgroup at rr*1024, 16-byte chunk c (values 8c .. 8c+7) at
-  // (c ^ (rr & 15))*16.  The page buffers are idle now.  For a split partial the same
-  // pass takes each row's largest |o| over the wave's columns (NaN is ignored here; the
-  // row's high half carries it).
+  // O goes through LDS as bf16 so that every store writes a whole 1 KB row: row rr of the
+  // workgroup at rr*1024, 16-byte chunk c (values 8c .. 8c+7) at (c ^ (rr & 15))*16.  The
+  // page buffers are idle now.  An unsplit row is normalised here; a split partial stays
+  // unnormalised (the merge applies the factor, stored beside its LSE), and the same pass
+  // takes each row's largest |o| over the wave's columns, in normalised units (NaN is
+  // ignored here; the row's factor carries it).
   MLA_LDS uint8_t* ob = lds;
   const bool part = slot >= 0;
   const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
+  auto stage = [&](auto norm_tag) {
+    constexpr bool kNorm = decltype(norm_tag)::value;
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int rr = 32 * rt + lr_e;
-    const float scale_o = stats[2 * rr];
-    float mx = 0.f;
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int rr = 32 * rt + lr_e;
+      const float scale_o = stats[2 * rr];
+      float mx = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x16& t = o[dt][rt];
-        const float x0 = t[4 * i] * scale_o, x1 = t[4 * i + 1] * scale_o;
-        const float x2 = t[4 * i + 2] * scale_o, x3 = t[4 * i + 3] * scale_o;
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
-        const int c = 16 * w + 4 * dt + i;
-        *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) =
-            u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& t = o[dt][rt];
+          float x0 = t[4 * i], x1 = t[4 * i + 1], x2 = t[4 * i + 2], x3 = t[4 * i + 3];
+          if constexpr (kNorm) {
+            x0 *= scale_o;
+            x1 *= scale_o;
+            x2 *= scale_o;
+            x3 *= scale_o;
+          } else {
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+          }
+          const int c = 16 * w + 4 * dt + i;
+          *(MLA_LDS u32x2*)(ob + rr * 1024 + ((c ^ (rr & 15)) << 4) + 8 * g_e) =
+              u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      if constexpr (!kNorm) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_o;   // over the wave's 128 columns of the row
+        if (g_e == 0) amax[w * 128 + rr] = mx;
+        if (mx > kLoCut && row0 + rr < row_end)            // this quarter of the row keeps its low half
+          store_lo_quarter(a.ws_lo + (prow + rr) * kDv + 128 * w + 4 * g_e, [&](int dt) -> const f32x16& { return o[dt][rt]; });
       }
-    if (part) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));      // over the wave's 128 columns of the row
-      if (g_e == 0) amax[w * 128 + rr] = mx;
-      if (mx > kLoCut && row0 + rr < row_end)      // this quarter of the row keeps its low half
-        store_lo_quarter(a.ws_lo + (prow + rr) * kDv + 128 * w + 4 * g_e, scale_o, [&](int dt) -> const f32x16& { return o[dt][rt]; });
     }
-  }
+  };
+  if (part) stage(BoolC<false>{});
+  else stage(BoolC<true>{});
   __syncthreads();
   for (int k = 0; k < 32; ++k) {                  // the wave's rows 32w .. 32w+31
     const int rr = 32 * w + k;
@@ -737,7 +760,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
     if (!part) {
       a.lse[(size_t)b * R + row0 + rr] = lse_v;
     } else {
-      a.ws_lse[prow + rr] = lse_v;
+      *(float2*)(a.ws_lse + 2 * (prow + rr)) = float2{lse_v, stats[2 * rr]};
     }
   }
   if (part && tid_e < kLoMaskWords) a.ws_lo_mask[(size_t)slot * kLoMaskWords + tid_e] = lo_mask_word(amax, tid_e, row_end - row0);
@@ -798,14 +821,6 @@ __device__ __forceinline__ uint32_t half_copy_lane(const HalfPage& h, int k, int
   const int te = tp < h.valid ? tp : 0;
   return __umul24((uint32_t)te, (uint32_t)kRowBytes) + (uint32_t)(((l & 7) ^ cswz(t)) << 4);
 }
-template <bool B>
-struct BoolC {
-  static constexpr bool value = B;
-};
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
 // P.V MFMA with no wait states ahead: for operands that no vector instruction has just
 // written (LDS reads, or registers written many instructions earlier).
 __device__ __forceinline__ void mfma_pv_ds(f32x16& o, const bf16x8& v, const bf16x8& p) {
@@ -1271,35 +1286,48 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     stats[2 * rr + 1] = lse_v;
   }
   __syncthreads();
-  // O (normalised, bf16) goes through the idle ring so that every store writes a whole 1 KB
-  // row: row rr at rr*1024, 16-byte chunk cc (values 8cc .. 8cc+7) at (cc ^ (rr & 15))*16.
-  // For a split partial the same pass takes each row's largest |o| over the wave's columns.
+  // O goes through the idle ring as bf16 so that every store writes a whole 1 KB row: row rr
+  // at rr*1024, 16-byte chunk cc (values 8cc .. 8cc+7) at (cc ^ (rr & 15))*16.  An unsplit
+  // row is normalised here.  A split partial stays unnormalised (the merge applies the
+  // factor, stored beside its LSE: one multiply per row there instead of 512 here), and
+  // the same pass takes each row's largest |o| over the wave's columns, in normalised units.
   const bool part = slot >= 0;
   const size_t prow = (size_t)slot * a.rows_per_wg;   // the partial slot's first row
+  auto stage = [&](auto norm_tag) {
+    constexpr bool kNorm = decltype(norm_tag)::value;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int rr = 32 * ((w + r) & 3) + lr_e;
-    const float so = stats[2 * rr];
-    float mx = 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int rr = 32 * ((w + r) & 3) + lr_e;
+      const float so = stats[2 * rr];
+      float mx = 0.f;
 #pragma unroll
-    for (int vt = 0; vt < 4; ++vt)
+      for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x16& t = o[4 * vt + r];
-        const float x0 = t[4 * i] * so, x1 = t[4 * i + 1] * so;
-        const float x2 = t[4 * i + 2] * so, x3 = t[4 * i + 3] * so;
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
-        const int cc = 16 * w + 4 * vt + i;
-        *(MLA_LDS u32x2*)(lds + rr * 1024 + ((cc ^ (rr & 15)) << 4) + 8 * g_e) =
-            u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& t = o[4 * vt + r];
+          float x0 = t[4 * i], x1 = t[4 * i + 1], x2 = t[4 * i + 2], x3 = t[4 * i + 3];
+          if constexpr (kNorm) {
+            x0 *= so;
+            x1 *= so;
+            x2 *= so;
+            x3 *= so;
+          } else {
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+          }
+          const int cc = 16 * w + 4 * vt + i;
+          *(MLA_LDS u32x2*)(lds + rr * 1024 + ((cc ^ (rr & 15)) << 4) + 8 * g_e) =
+              u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      if constexpr (!kNorm) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * so;   // over the wave's 128 columns of the row
+        if (g_e == 0) amax[w * 128 + rr] = mx;
+        if (mx > kLoCut && row0 + rr < row_end)        // this quarter of the row keeps its low half
+          store_lo_quarter(a.ws_lo + (prow + rr) * kDv + 128 * w + 4 * g_e, [&](int vt) -> const f32x16& { return o[4 * vt + r]; });
       }
-    if (part) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));      // over the wave's 128 columns of the row
-      if (g_e == 0) amax[w * 128 + rr] = mx;
-      if (mx > kLoCut && row0 + rr < row_end)      // this quarter of the row keeps its low half
-        store_lo_quarter(a.ws_lo + (prow + rr) * kDv + 128 * w + 4 * g_e, so, [&](int vt) -> const f32x16& { return o[4 * vt + r]; });
     }
-  }
+  };
+  if (part) stage(BoolC<false>{});
+  else stage(BoolC<true>{});
   __syncthreads();
   for (int k = 0; k < 32; ++k) {                      // the wave's rows 32w .. 32w+31
     const int rr = 32 * w + k;
@@ -1314,7 +1342,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     if (!part) {
       a.lse[(size_t)b * R + row0 + rr] = lse_v;
     } else {
-      a.ws_lse[prow + rr] = lse_v;
+      *(float2*)(a.ws_lse + 2 * (prow + rr)) = float2{lse_v, stats[2 * rr]};
     }
   }
   if (part && tid_e < kLoMaskWords) a.ws_lo_mask[(size_t)slot * kLoMaskWords + tid_e] = lo_mask_word(amax, tid_e, row_end - row0);

@@ -90,9 +90,10 @@ def test_plan_sizes_and_workspace_checks():
     # header + cu_blocks[B+1] + 3 per unit + wg_begin[grid+1] + wg_seq[grid] int32 words
     assert mb == 4 * (16 + 5 + 3 * 4 + 257 + 256)
     # partial slots: grid + min(grid, units), each rows_per_wg rows of a compensated bf16
-    # pair (hi and lo halves) and a float32 LSE, plus 16 words of low-half flags a slot
+    # pair (hi and lo halves) and a float32 (LSE, normalising factor) pair, plus 16 words
+    # of low-half flags a slot
     def part(slots, rows):
-        return slots * rows * 512 * 4 + (slots * rows * 4 + 15) // 16 * 16 + slots * 64
+        return slots * rows * 512 * 4 + (slots * rows * 8 + 15) // 16 * 16 + slots * 64
     assert wb == part(256 + 4, 128)
     opts = m.PlanOptions(num_workgroups=8, min_blocks_per_wg=1, row_split=2)
     assert m.workspace_bytes(p, opts, 256) == part(8 + 8, 64)
@@ -163,7 +164,7 @@ def test_sparse_problem_checks():
     mb = m.metadata_bytes(sp, None, 256)
     assert mb == 4 * (16 + 9 + 3 * 8 + 257 + 256)
     # workspace: partials (256-byte aligned), then the row lists and the counts
-    part = (256 + 8) * 128 * 2052 + (256 + 8) * 64
+    part = (256 + 8) * 128 * 2056 + (256 + 8) * 64
     rows = 8 * 128 * 4
     assert m.workspace_bytes(sp, None, 256) == ((part + 255) // 256 * 256) + rows + 256
     assert m.metadata_bytes(_problem(q_len=2, num_heads=128), None, 256) == 0   # dense: too many rows

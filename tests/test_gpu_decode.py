@@ -174,9 +174,9 @@ def test_merge_of_large_cancelling_partials():
     o, l, dec = run(case, options=mla.PlanOptions(fixed_split_blocks=1))
     torch.cuda.synchronize()
     rows = dec.plan.max_partials * 128                 # partial rows of the workspace
-    # after the high halves and the LSEs (padded to 16 bytes): 16 flag words per slot,
-    # 4 bits per row
-    off = rows * 1024 + (rows * 4 + 15) // 16 * 16
+    # after the high halves and the (LSE, factor) pairs (padded to 16 bytes): 16 flag words
+    # per slot, 4 bits per row
+    off = rows * 1024 + (rows * 8 + 15) // 16 * 16
     words = dec.workspace[off: off + dec.plan.max_partials * 64].view(torch.int32).cpu().numpy().view(np.uint32)
     flags = np.stack([(words >> (4 * j)) & 15 for j in range(8)], axis=1).reshape(-1)
     # only the slots the plan uses were written; the rest of the region is uninitialised
