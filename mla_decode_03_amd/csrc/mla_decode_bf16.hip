@@ -155,16 +155,17 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
   return r;
 }
 
-// Workgroup-wide OR through 4 words of caller-provided LDS (the decode uses every byte
-// of LDS, so the OR cannot reserve its own).  The first barrier lets every wave finish
-// its earlier reads of those words before any wave overwrites them.
-__device__ __forceinline__ bool wg_or(bool f, MLA_LDS int* scratch) {
+// Workgroup-wide OR of two flag bits (bit 0, bit 1 of `bits`) through 4 words of
+// caller-provided LDS (the decode uses every byte of LDS, so the OR cannot reserve its
+// own).  The first barrier lets every wave finish its earlier reads of those words before
+// any wave overwrites them.
+__device__ __forceinline__ int wg_or_bits(int bits, MLA_LDS int* scratch) {
   const int w = wave_id();
-  const int wf = __builtin_amdgcn_ballot_w64(f) != 0;
+  const int wf = (__builtin_amdgcn_ballot_w64(bits & 1) != 0 ? 1 : 0) | (__builtin_amdgcn_ballot_w64(bits & 2) != 0 ? 2 : 0);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) scratch[w] = wf;
   __syncthreads();
-  const bool r = (scratch[0] | scratch[1] | scratch[2] | scratch[3]) != 0;
+  const int r = scratch[0] | scratch[1] | scratch[2] | scratch[3];
   __syncthreads();  // every wave has read before the words are reused
   return r;
 }
@@ -488,7 +489,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
 
   f32x16 o[4][NRT];
   float m_ref = -INFINITY, mtrue = -INFINITY, lsum = 0.f;
-  bool over = false;
+  bool over = false, bad_wg = false;   // bad_wg: some wave read a bad page
   float mref_init = -INFINITY;
   for (int pass = 0; pass < 2; ++pass) {
     m_ref = mref_init;
@@ -657,8 +658,12 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the page buffers and P buffer are idle until the next pass starts
-    if (!wg_or(over, (MLA_LDS int*)pbuf)) break;
+    // the page buffers and P buffer are idle until the next pass starts.  One OR gives
+    // both the second-pass flag and the bad-page flag (the second pass streams the same
+    // pages, so it gives the same bad-page flag).
+    const int flags = wg_or_bits((over ? 1 : 0) | (bad_page ? 2 : 0), (MLA_LDS int*)pbuf);
+    bad_wg = (flags & 2) != 0;
+    if (!(flags & 1)) break;
     // Second pass from an upper bound of every score of the row: pages that did not flag
     // stayed within m_ref + kRefSlack, the flagged ones gave their maxima.
     {
@@ -668,7 +673,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
   }
 
   // ---- epilogue: every wave needs the row statistics of all 128 rows ---------------------
-  const bool poison = bad_len || wg_or(bad_page, (MLA_LDS int*)pbuf);
+  const bool poison = bad_len || bad_wg;
   if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
   // Per row, once: the factor that normalises O and the natural-log LSE.  The attention
   // sink enters a row once, where its final result is formed: here for an unsplit range,
@@ -921,7 +926,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
 
   f32x16 o[16];   // O^T: value tile 4w + vt (values 128w + 32vt ..), row tile (w + r) % 4 at o[4 vt + r]
   float m_ref = -INFINITY, mtrue = -INFINITY, lsum = 0.f;
-  bool over = false;
+  bool over = false, bad_wg = false;   // bad_wg: some wave read a bad page
   float mref_init = -INFINITY;
   for (int pass = 0; pass < 2; ++pass) {
     m_ref = mref_init;
@@ -1249,7 +1254,11 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
       }
     }
     mfma_drain();
-    if (!wg_or(over, or_words)) break;
+    // One OR (its barriers: every slot is idle) gives both the second-pass flag and the
+    // bad-page flag (the second pass streams the same pages, so it gives the same one).
+    const int flags = wg_or_bits((over ? 1 : 0) | (bad_page ? 2 : 0), or_words);
+    bad_wg = (flags & 2) != 0;
+    if (!(flags & 1)) break;
     // Second pass from an upper bound of every score of the row: half pages that did not
     // flag stayed within m_ref + kRefSlack, the flagged ones gave their maxima.
     {
@@ -1259,7 +1268,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
   }
 
   // ---- epilogue: every wave needs the row statistics of all 128 rows ---------------------
-  const bool poison = bad_len || wg_or(bad_page, or_words);   // (its barriers: every slot is idle)
+  const bool poison = bad_len || bad_wg;
   if (poison && a.meta && threadIdx.x == 0) a.meta[kHdrError] = 1;
   MLA_LDS float* stats = (MLA_LDS float*)pbuf + 16;   // [row][scale_o, lse], after the OR words
   MLA_LDS float* amax = stats + 2 * 128;              // [wave][row]: largest |o| over the wave's columns
