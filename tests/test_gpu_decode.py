@@ -87,13 +87,16 @@ def test_small_parity(B, T, H, lens, causal, mode):
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
 def test_full_config_every_row(idx):
-    """Full-size workloads, default plan (the launch configuration the benchmark times),
-    every row against the oracle."""
+    """Full-size workloads, default plan, every row against the oracle: in the launch
+    configuration the benchmark times (the plan computed inside the decode launch), and
+    with a planner launch before the decode."""
+    import mla_decode_03_amd as mla
     case = make_config(idx)
     say("config", idx, case.name, "pages", case.num_pages)
-    o, l, _ = run(case)
     ref_o, ref_l = oracle_rows(case)
-    compare(o, l, ref_o, ref_l, "config%d, all %d rows" % (idx, o.shape[0]))
+    for in_decode in (1, 0):
+        o, l, _ = run(case, options=mla.PlanOptions(plan_in_decode=in_decode))
+        compare(o, l, ref_o, ref_l, "config%d, all %d rows, plan_in_decode=%d" % (idx, o.shape[0], in_decode))
 
 
 def test_split_counts_agree():
@@ -577,11 +580,13 @@ def test_sink_minus_inf_is_bit_identical_to_plain():
 
 
 def test_sink_full_headline_every_row():
-    """The benchmark's workload and default plan, with sinks, every row."""
+    """The benchmark's workload and launch configuration (default plan, computed inside the
+    decode launch), with sinks, every row."""
+    import mla_decode_03_amd as mla
     from mla_inputs import make_sinks
     case = make_config(1)
     sinks = make_sinks(case.num_heads, seed=1)
-    o, l, _ = run(case, sinks=sinks)
+    o, l, _ = run(case, sinks=sinks, options=mla.PlanOptions(plan_in_decode=1))
     ref_o, ref_l = oracle_rows(case, sinks=sinks)
     compare(o, l, ref_o, ref_l, "config1 sinks, all %d rows" % o.shape[0])
 
