@@ -1380,12 +1380,16 @@ __device__ __forceinline__ void decode_replanned(const DecodeArgs& a, MLA_LDS ui
                   (int32_t*)(lds + kOffShare)};
   const PlanParams p{a.seqlens, a.batch, a.rows, a.row_split, (int)gridDim.x, a.plan_min_blocks, a.max_blocks,
                      a.plan_max_partials, a.plan_fixed_blocks, a.plan_split_rule, a.plan_seg_cost, a.plan_uniform_len};
-  static_assert(4 * 4 * kScatterLdsWords <= kRingScratch, "four waves' scatter tables fit the ring");
+  // The table form's LDS lies in ring slots 2 and 3, apart from plan_core's (which it
+  // leaves to when it does not apply) and from the first two half pages' copies; the
+  // segment's first barrier comes before any copy into it.
+  static_assert(4 * kTablesLdsWords <= 2 * kSlotBytes && kOffShare + 4 * kShareWords <= 2 * kSlotBytes,
+                "the planners' LDS fits");
   int sh[kShareWords];
   if (plan_share_wave(p, v, wg == 0, wg, sh)) {
     // even batches of up to 64 sequences: registers only
-  } else if (plan_share_scatter(p, v, wg == 0, wg, sh, (MLA_LDS int32_t*)lds + (threadIdx.x >> 6) * kScatterLdsWords)) {
-    __syncthreads();   // ragged batches of up to 256: every wave is done with its tables before the ring
+  } else if (plan_share_tables(p, v, wg == 0, wg, sh, (MLA_LDS int32_t*)(lds + 2 * kSlotBytes))) {
+    // ragged batches of up to 256 sequences: tables in LDS
   } else {   // the general case: the block-wide computation
     plan_core<true>(p, L, v, wg == 0, wg);
 #pragma unroll

@@ -588,65 +588,87 @@ __device__ inline bool plan_share_wave(const PlanParams& p, MetaView v, bool wri
   return true;
 }
 
-// Cuts one sequence may hold, under either rule, in plan_share_scatter's form.
-constexpr int kScatterMaxCuts = 64;
-// LDS words plan_share_scatter takes per wave: the cuts of each rule and the owner of each
-// cut (kPlanLdsWg + 1 words each), and the sequence of each non-empty rank (256 words).
-constexpr int kScatterLdsWords = 4 * (kPlanLdsWg + 1) + 256;
+// Cuts one sequence may hold, under either rule, in plan_share_tables' form.
+constexpr int kTablesMaxCuts = 64;
+// LDS words plan_share_tables takes: the cuts of each rule and the owner of each cut
+// (kPlanLdsWg + 1 words each); per sequence its rank's sequence, first block, block count,
+// split count, first workgroup and partial-slot offset (256 words each, first blocks 257);
+// 16 words of per-wave totals.
+constexpr int kTablesLdsWords = 4 * (kPlanLdsWg + 1) + 6 * 256 + 1 + 16;
 
-// The re-planning decode's form for ragged batches: at most 256 sequences (lane l holds
-// sequences l, l + 64, l + 128, l + 192), no row split, no fixed chunks, either rule or the
-// cost model's choice between them.  Computed by each wave on its own, in its own LDS
-// (tab: kScatterLdsWords words, private to the wave; no barrier inside, the caller
-// barriers before the LDS is reused).  Instead of searching the sequences for the holder
-// of each cut, every sequence writes the cuts that land in it, in closed form: under the
-// equal-share rule the cuts w*total/num_wg inside its blocks, under the cost rule the cuts
-// w*ctot/num_wg inside its stretch of the cost axis (its c quarters of overhead, then 4 per
-// block).  Each cut is written with its owner's sequence, rank among the non-empty
-// sequences, and whether it falls on the owner's first block; a workgroup then touches
-// the units from its first cut's owner to the owner of its last block, which gives the
-// busiest workgroup of each rule with no search.  Same plan as plan_core.  Returns false,
-// with nothing written, when the case does not apply: more sequences, row split, fixed
-// chunks, more than kPlanLdsWg workgroups, a cost axis whose products with num_wg reach
-// 2^31, or a sequence holding more than kScatterMaxCuts cuts.
-__device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool write, int my_wg, int32_t* sh,
-                                          MLA_LDS int32_t* tab) {
-  const int lane = threadIdx.x & 63;
+// The re-planning decode's form for ragged batches: at most 256 sequences (thread t holds
+// sequence t), no row split, no fixed chunks, either rule or the cost model's choice
+// between them, computed by the whole workgroup in LDS (tab: kTablesLdsWords words) with
+// four barriers.  Instead of searching the sequences for the holder of each cut, every
+// sequence writes the cuts that land in it, in closed form: under the equal-share rule the
+// cuts w*total/num_wg inside its blocks, under the cost rule the cuts w*ctot/num_wg inside
+// its stretch of the cost axis (its c quarters of overhead, then 4 per block).  Each cut is
+// written with its owner's sequence, rank among the non-empty sequences, and whether it
+// falls on the owner's first block; a workgroup then touches the units from its first cut's
+// owner to the owner of its last block, so thread w prices workgroup w under each rule with
+// no search.  Same plan as plan_core.  Returns false (every thread alike, before any
+// table is written) when the case does not apply: more sequences, row split, fixed chunks,
+// more than kPlanLdsWg workgroups, a cost axis whose products with num_wg reach 2^31, or a
+// sequence that could hold more than kTablesMaxCuts cuts.  The LDS may be reused after the
+// caller's next barrier.
+__device__ inline bool plan_share_tables(const PlanParams& p, MetaView v, bool write, int my_wg, int32_t* sh,
+                                         MLA_LDS int32_t* tab) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int B = p.batch;
   if (B > 256 || p.row_split != 1 || p.fixed_blocks > 0) return false;
-  const int nk = (B + 63) >> 6;   // sequences per lane
+  constexpr int kW = kPlanLdsWg + 1;
+  MLA_LDS int32_t* cut_p = tab;
+  MLA_LDS int32_t* own_p = tab + kW;
+  MLA_LDS int32_t* cut_c = tab + 2 * kW;
+  MLA_LDS int32_t* own_c = tab + 3 * kW;
+  MLA_LDS int32_t* seq_of_rank = tab + 4 * kW;
+  MLA_LDS int32_t* seq_s = seq_of_rank + 256;   // [257]: first block of each sequence, then the total
+  MLA_LDS int32_t* seq_n = seq_s + 257;
+  MLA_LDS int32_t* seq_ns = seq_n + 256;
+  MLA_LDS int32_t* seq_fw = seq_ns + 256;
+  MLA_LDS int32_t* seq_po = seq_fw + 256;
+  MLA_LDS int32_t* wsum = seq_po + 256;          // [16]: per-wave totals
+
+  // 1. blocks of sequence t; prefix sums and ranks over the workgroup (one barrier)
   int err = 0;
-  int32_t n[4];
+  int32_t n = 0;
+  if (t < B) {
+    int64_t L = p.uniform_len > 0 ? p.uniform_len : p.seqlens[t];
+    if (L < 0) { L = 0; err = 1; }
+    int64_t nn = (L + kPage - 1) / kPage;
+    if (nn > p.max_blocks) { nn = p.max_blocks; err = 1; }
+    n = (int32_t)nn;
+  }
+  const int32_t incl = wave_inclusive_sum(n);
+  const uint64_t nzm = __builtin_amdgcn_ballot_w64(n > 0);
+  const int32_t rw = (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(nzm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)nzm, 0));
+  const int32_t wmax = wave_max_nonneg(n);
+  const bool werr = __builtin_amdgcn_ballot_w64(err != 0) != 0;
+  if (lane == 63) {
+    wsum[4 * wv] = incl;
+    wsum[4 * wv + 1] = (int32_t)__builtin_popcountll(nzm);
+    wsum[4 * wv + 2] = wmax;
+    wsum[4 * wv + 3] = werr ? 1 : 0;
+  }
+  lds_barrier();
+  int32_t total = 0, ne = 0, nbm = 0, s = 0, r = 0;
+  bool any_err = false;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    n[k] = 0;
-    const int b = lane + 64 * k;
-    if (k < nk && b < B) {
-      int64_t L = p.uniform_len > 0 ? p.uniform_len : p.seqlens[b];
-      if (L < 0) { L = 0; err = 1; }
-      int64_t nn = (L + kPage - 1) / kPage;
-      if (nn > p.max_blocks) { nn = p.max_blocks; err = 1; }
-      n[k] = (int32_t)nn;
+    const int32_t ws = wsum[4 * k], wc = wsum[4 * k + 1];
+    if (k < wv) {
+      s += ws;
+      r += wc;
     }
+    total += ws;
+    ne += wc;
+    nbm = max(nbm, wsum[4 * k + 2]);
+    any_err |= wsum[4 * k + 3] != 0;
   }
-  // first blocks (prefix sums) and ranks among the non-empty sequences, in sequence order
-  int32_t s[4], r[4];
-  int32_t total = 0, ne = 0, mx = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    s[k] = total;
-    r[k] = ne;
-    if (k < nk) {
-      const int32_t incl = wave_inclusive_sum(n[k]);
-      s[k] = total + incl - n[k];
-      total += __builtin_amdgcn_readlane(incl, 63);
-      const uint64_t m = __builtin_amdgcn_ballot_w64(n[k] > 0);
-      r[k] = ne + (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      ne += (int32_t)__builtin_popcountll(m);
-      mx = max(mx, n[k]);
-    }
-  }
-  const int32_t nbm = wave_max_nonneg(mx);
+  s += incl - n;
+  r += rw;
+
+  // 2. the workgroups, the cost axis, which rules to form; every check before any table write
   int32_t num_wg = 0;
   if (total > 0) num_wg = max(1, min(p.grid_wg, (int32_t)floor_div((int64_t)total + p.min_blocks - 1, p.min_blocks)));
   const int32_t c = p.seg_cost;
@@ -663,59 +685,49 @@ __device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool 
   }
   const bool need_p = num_wg > 0 && p.split_rule != kRuleCost;
   const bool need_c = num_wg > 0 && (p.split_rule == kRuleCost || evaluate);
-  // the cuts landing in each sequence: [pw0, pw1) equal-share, [cw0, cw1) cost
-  uint32_t pw0[4], pw1[4], cw0[4], cw1[4], cs[4];
-  int32_t most = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    pw0[k] = pw1[k] = cw0[k] = cw1[k] = 0;
-    cs[k] = 4 * (uint32_t)s[k] + uc * (uint32_t)r[k];
-    if (k < nk && n[k] > 0) {
+  // cuts inside one sequence of nb blocks: at most ceil(nb W / T), or ceil((c + 4 nb) W / C)
+  if (need_p && ((uint32_t)nbm * W + T - 1) / T > (uint32_t)kTablesMaxCuts) return false;
+  if (need_c && ((uc + 4 * (uint32_t)nbm) * W + C - 1) / C > (uint32_t)kTablesMaxCuts) return false;
+
+  // 3. the cuts landing in sequence t, with their owner word: sequence (bits 0-11), rank
+  // (12-23), cut on the owner's first block (24) (one barrier)
+  const uint32_t cs = 4 * (uint32_t)s + uc * (uint32_t)r;   // the sequence's start on the cost axis
+  if (t < B) {
+    seq_s[t] = s;
+    seq_n[t] = n;
+    if (n > 0) {
+      seq_of_rank[r] = t;
+      const int32_t own = t | (r << 12);
       if (need_p) {
-        pw0[k] = ((uint32_t)s[k] * W + T - 1) / T;
-        pw1[k] = ((uint32_t)(s[k] + n[k]) * W + T - 1) / T;
+        const uint32_t w1 = ((uint32_t)(s + n) * W + T - 1) / T;
+        for (uint32_t w = ((uint32_t)s * W + T - 1) / T; w < w1; ++w) {
+          const uint32_t cut = w * T / W;
+          cut_p[w] = (int32_t)cut;
+          own_p[w] = own | ((cut == (uint32_t)s) << 24);
+        }
       }
       if (need_c) {
-        cw0[k] = (cs[k] * W + C - 1) / C;
-        cw1[k] = ((cs[k] + uc + 4 * (uint32_t)n[k]) * W + C - 1) / C;
+        const uint32_t w1 = ((cs + uc + 4 * (uint32_t)n) * W + C - 1) / C;
+        for (uint32_t w = (cs * W + C - 1) / C; w < w1; ++w) {
+          const uint32_t off = w * C / W - cs;
+          const uint32_t cut = (uint32_t)s + (off < uc ? 0 : (off - uc) >> 2);
+          cut_c[w] = (int32_t)cut;
+          own_c[w] = own | ((cut == (uint32_t)s) << 24);
+        }
       }
-      most = max(most, (int32_t)max(pw1[k] - pw0[k], cw1[k] - cw0[k]));
     }
   }
-  if (wave_max_nonneg(most) > kScatterMaxCuts) return false;
+  if (t == 0) {
+    seq_s[B] = total;
+    if (num_wg > 0) {   // the end: past the last non-empty rank
+      cut_p[num_wg] = cut_c[num_wg] = total;
+      own_p[num_wg] = own_c[num_wg] = B | (ne << 12) | (1 << 24);
+    }
+  }
+  lds_barrier();
 
-  constexpr int kW = kPlanLdsWg + 1;
-  MLA_LDS int32_t* cut_p = tab;
-  MLA_LDS int32_t* own_p = tab + kW;
-  MLA_LDS int32_t* cut_c = tab + 2 * kW;
-  MLA_LDS int32_t* own_c = tab + 3 * kW;
-  MLA_LDS int32_t* seq_of_rank = tab + 4 * kW;
-  // owner word: sequence (bits 0-11), rank (12-23), cut on the owner's first block (24)
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (k < nk && n[k] > 0) {
-      const int b = lane + 64 * k;
-      seq_of_rank[r[k]] = b;
-      const int32_t own = b | (r[k] << 12);
-      for (uint32_t w = pw0[k]; w < pw1[k]; ++w) {
-        const uint32_t cut = w * T / W;
-        cut_p[w] = (int32_t)cut;
-        own_p[w] = own | ((cut == (uint32_t)s[k]) << 24);
-      }
-      for (uint32_t w = cw0[k]; w < cw1[k]; ++w) {
-        const uint32_t off = w * C / W - cs[k];
-        const uint32_t cut = (uint32_t)s[k] + (off < uc ? 0 : (off - uc) >> 2);
-        cut_c[w] = (int32_t)cut;
-        own_c[w] = own | ((cut == (uint32_t)s[k]) << 24);
-      }
-    }
-  }
-  if (lane == 0 && num_wg > 0) {   // the end: past the last non-empty rank
-    cut_p[num_wg] = cut_c[num_wg] = total;
-    own_p[num_wg] = own_c[num_wg] = B | (ne << 12) | (1 << 24);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // lanes read each other's words below
-  // the busiest workgroup of each rule: 4 per block plus c per unit touched
+  // 4. the busiest workgroup of each rule (4 per block plus c per unit touched), and each
+  // sequence's workgroups and partial slots under both rules (one barrier)
   auto range_cost = [&](MLA_LDS const int32_t* cut, MLA_LDS const int32_t* own, int w) -> int32_t {
     const int32_t lo = cut[w], hi = cut[w + 1];
     if (hi <= lo) return 0;
@@ -725,43 +737,65 @@ __device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool 
   };
   int32_t worst_p = 0, worst_c = 0;
   if (evaluate) {
-    for (int w = lane; w < num_wg; w += 64) {
+    for (int w = t; w < num_wg; w += 256) {
       worst_p = max(worst_p, range_cost(cut_p, own_p, w));
       worst_c = max(worst_c, range_cost(cut_c, own_c, w));
     }
     worst_p = wave_max_nonneg(worst_p);
     worst_c = wave_max_nonneg(worst_c);
   }
-  const bool use_cost = p.split_rule == kRuleCost || (evaluate && worst_c < worst_p);
-  MLA_LDS const int32_t* cut = use_cost ? cut_c : cut_p;
-  MLA_LDS const int32_t* own = use_cost ? own_c : own_p;
-  // each sequence's workgroups (the holders of its first and last blocks) and partial slots
-  int32_t ns[4], fw[4], po[4];
-  int32_t num_partials = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    ns[k] = 0;
-    fw[k] = -1;
-    po[k] = num_partials;
-    if (k < nk) {
-      if (n[k] > 0) {
-        auto holder = [&](uint32_t q) -> int32_t {   // the workgroup holding block q of this sequence
-          if (!use_cost) return (int32_t)(((q + 1) * W - 1) / T);
-          const uint32_t y = cs[k] + uc + 4 * (q - (uint32_t)s[k]) + 4;   // cost position just past block q
-          return (int32_t)min((y * W - 1) / C, W - 1);
-        };
-        fw[k] = holder((uint32_t)s[k]);
-        ns[k] = holder((uint32_t)(s[k] + n[k] - 1)) - fw[k] + 1;
-      }
-      const int32_t x = ns[k] > 1 ? ns[k] : 0;
-      const int32_t incl = wave_inclusive_sum(x);
-      po[k] = num_partials + incl - x;
-      num_partials += __builtin_amdgcn_readlane(incl, 63);
+  // the workgroup holding block q of this sequence, under each rule
+  auto holder_p = [&](uint32_t q) -> int32_t { return (int32_t)(((q + 1) * W - 1) / T); };
+  auto holder_c = [&](uint32_t q) -> int32_t {
+    const uint32_t y = cs + uc + 4 * (q - (uint32_t)s) + 4;   // cost position just past block q
+    return (int32_t)min((y * W - 1) / C, W - 1);
+  };
+  int32_t ns_p = 0, fw_p = -1, ns_c = 0, fw_c = -1;
+  if (n > 0) {
+    if (need_p) {
+      fw_p = holder_p((uint32_t)s);
+      ns_p = holder_p((uint32_t)(s + n - 1)) - fw_p + 1;
+    }
+    if (need_c) {
+      fw_c = holder_c((uint32_t)s);
+      ns_c = holder_c((uint32_t)(s + n - 1)) - fw_c + 1;
     }
   }
+  // partial slots of both rules in one scan: at most num_wg + B < 2^16 each
+  const int32_t xp = ns_p > 1 ? ns_p : 0, xc = ns_c > 1 ? ns_c : 0;
+  const int32_t xincl = wave_inclusive_sum(xp | (xc << 16));
+  if (lane == 63) {
+    wsum[4 * wv] = xincl;
+    wsum[4 * wv + 1] = worst_p;
+    wsum[4 * wv + 2] = worst_c;
+  }
+  lds_barrier();
+  int32_t xbase = 0, xtot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int32_t x = wsum[4 * k];
+    if (k < wv) xbase += x;
+    xtot += x;
+    worst_p = max(worst_p, wsum[4 * k + 1]);
+    worst_c = max(worst_c, wsum[4 * k + 2]);
+  }
+  const bool use_cost = p.split_rule == kRuleCost || (evaluate && worst_c < worst_p);
+  const int sh16 = use_cost ? 16 : 0;
+  const int32_t ns = use_cost ? ns_c : ns_p, fw = use_cost ? fw_c : fw_p;
+  const int32_t po = ((xbase + xincl) >> sh16 & 0xffff) - (use_cost ? xc : xp);
+  const int32_t num_partials = (xtot >> sh16) & 0xffff;
   const bool refuse = num_partials > p.max_partials;
-  const bool any_err = __builtin_amdgcn_ballot_w64(err != 0) != 0 || refuse;
-  // my range, its first block's sequence and its last block's
+  any_err |= refuse;
+
+  // 5. this workgroup's share (one barrier: the per-sequence words of its two end units)
+  if (t < B) {
+    seq_ns[t] = ns;
+    seq_fw[t] = fw;
+    seq_po[t] = po;
+  }
+  lds_barrier();
+  MLA_LDS const int32_t* cut = use_cost ? cut_c : cut_p;
+  MLA_LDS const int32_t* own = use_cost ? own_c : own_p;
   int32_t pos = total, end = total, uf = -1, ul = -1;
   if (my_wg < num_wg) {
     pos = __builtin_amdgcn_readfirstlane(cut[my_wg]);
@@ -773,11 +807,6 @@ __device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool 
     uf = o0 & 0xfff;
     ul = ((o1 >> 24) & 1) ? __builtin_amdgcn_readfirstlane(seq_of_rank[((o1 >> 12) & 0xfff) - 1]) : (o1 & 0xfff);
   }
-  auto pick = [&](const int32_t (&x)[4], int u) -> int32_t {   // sequence u's word (u uniform)
-    const int k = u >> 6;
-    const int32_t y = k == 0 ? x[0] : k == 1 ? x[1] : k == 2 ? x[2] : x[3];
-    return __builtin_amdgcn_readlane(y, u & 63);
-  };
   sh[kSharePos] = pos;
   sh[kShareEnd] = end;
   sh[kShareUFirst] = uf;
@@ -785,29 +814,23 @@ __device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool 
   sh[kShareNumWg] = refuse ? 0 : num_wg;
   sh[kShareErr] = any_err ? 1 : 0;
   if (uf >= 0) {
-    sh[kShareNsFirst] = pick(ns, uf);
-    sh[kShareFirstWgFirst] = pick(fw, uf);
-    sh[kSharePoffFirst] = pick(po, uf);
-    sh[kShareStartFirst] = pick(s, uf);
-    sh[kShareNbFirst] = pick(n, uf);
-    sh[kShareNsLast] = pick(ns, ul);
-    sh[kShareFirstWgLast] = pick(fw, ul);
-    sh[kSharePoffLast] = pick(po, ul);
+    sh[kShareNsFirst] = __builtin_amdgcn_readfirstlane(seq_ns[uf]);
+    sh[kShareFirstWgFirst] = __builtin_amdgcn_readfirstlane(seq_fw[uf]);
+    sh[kSharePoffFirst] = __builtin_amdgcn_readfirstlane(seq_po[uf]);
+    sh[kShareStartFirst] = __builtin_amdgcn_readfirstlane(seq_s[uf]);
+    sh[kShareNbFirst] = __builtin_amdgcn_readfirstlane(seq_n[uf]);
+    sh[kShareNsLast] = __builtin_amdgcn_readfirstlane(seq_ns[ul]);
+    sh[kShareFirstWgLast] = __builtin_amdgcn_readfirstlane(seq_fw[ul]);
+    sh[kSharePoffLast] = __builtin_amdgcn_readfirstlane(seq_po[ul]);
   }
-  if (write) {   // the plan, as plan_core stores it: wave k the words of sequences 64k + lane
-    const int wv = threadIdx.x >> 6;
-    const int b = lane + 64 * wv;
-    if (b < B) {
-      const int32_t bs = wv == 0 ? s[0] : wv == 1 ? s[1] : wv == 2 ? s[2] : s[3];
-      const int32_t bns = wv == 0 ? ns[0] : wv == 1 ? ns[1] : wv == 2 ? ns[2] : ns[3];
-      const int32_t bfw = wv == 0 ? fw[0] : wv == 1 ? fw[1] : wv == 2 ? fw[2] : fw[3];
-      const int32_t bpo = wv == 0 ? po[0] : wv == 1 ? po[1] : wv == 2 ? po[2] : po[3];
-      v.cu_blocks[b] = bs;
-      v.num_splits[b] = bns;
-      v.first_wg[b] = bfw;
-      v.part_off[b] = bpo;
+  if (write) {   // the plan, as plan_core stores it
+    if (t < B) {
+      v.cu_blocks[t] = s;
+      v.num_splits[t] = ns;
+      v.first_wg[t] = fw;
+      v.part_off[t] = po;
     }
-    if (threadIdx.x == 0) {
+    if (t == 0) {
       v.cu_blocks[B] = total;
       v.hdr[kHdrMagic] = kMetaMagic;
       v.hdr[kHdrBatch] = B;
@@ -827,7 +850,7 @@ __device__ inline bool plan_share_scatter(const PlanParams& p, MetaView v, bool 
       v.hdr[kHdrSegCost] = p.seg_cost;
     }
     int32_t* wg_seq = meta_wg_seq(v, p.grid_wg);
-    for (int w = threadIdx.x; w <= p.grid_wg; w += 256) {   // each wave reads its own tables
+    for (int w = t; w <= p.grid_wg; w += 256) {
       const int32_t begin = (w <= num_wg && num_wg > 0) ? cut[w] : total;
       v.wg_begin[w] = begin;
       if (w < p.grid_wg) wg_seq[w] = (w < num_wg && begin < total) ? (own[w] & 0xfff) : 0;
