@@ -1430,8 +1430,10 @@ __device__ __forceinline__ void decode_replanned(const DecodeArgs& a, MLA_LDS ui
 }
 
 // ===== kernel ==========================================================================
-// NRT = 32-row tiles per workgroup (1, 2 or 4).
-template <int NRT, bool SPARSE>
+// NRT = 32-row tiles per workgroup (1, 2 or 4).  REPLAN: the launch plans for itself (a
+// plan made with plan_in_decode); each form is its own kernel, so that neither carries the
+// other's code (a smaller binary to fetch at the start of every workgroup).
+template <int NRT, bool SPARSE, bool REPLAN>
 __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)lds_raw;
@@ -1441,7 +1443,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   // neighbours (the splits of one sequence) are made to share an XCD and its L2.
   int wg = blockIdx.x;
   if (planned && (gridDim.x & 7) == 0) wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  if (planned && a.plan_in_decode) {
+  if constexpr (REPLAN) {   // the host launches this form only with a plan (meta set)
     decode_replanned<NRT, SPARSE>(a, lds, v, wg);
     return;
   }
@@ -1498,12 +1500,18 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
 namespace {
 // One launch of the decode kernel: a plain launch, or with events bound to the kernel's own
 // start and end (hipExtLaunchKernelGGL), which adds no timing packet between launches.
+template <int NRT, bool SPARSE, bool REPLAN>
+void launch_decode_form(const mla::DecodeArgs& args, dim3 g, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop)
+    hipExtLaunchKernelGGL((mla::mla_decode_bf16_kernel<NRT, SPARSE, REPLAN>), g, dim3(256), 0, stream, start, stop, 0,
+                          args);
+  else
+    hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<NRT, SPARSE, REPLAN>), g, dim3(256), 0, stream, args);
+}
 template <int NRT, bool SPARSE>
 void launch_decode(const mla::DecodeArgs& args, dim3 g, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (start || stop)
-    hipExtLaunchKernelGGL((mla::mla_decode_bf16_kernel<NRT, SPARSE>), g, dim3(256), 0, stream, start, stop, 0, args);
-  else
-    hipLaunchKernelGGL((mla::mla_decode_bf16_kernel<NRT, SPARSE>), g, dim3(256), 0, stream, args);
+  if (args.meta && args.plan_in_decode) launch_decode_form<NRT, SPARSE, true>(args, g, stream, start, stop);
+  else launch_decode_form<NRT, SPARSE, false>(args, g, stream, start, stop);
 }
 }  // namespace
 
