@@ -361,8 +361,13 @@ int32_t launch_sparse_rows(const mla_problem_t& orig, const int32_t* indices, co
   return mla_launch_sparse_rows(&sp, st) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
-int32_t launch_combine(const mla::DecodeArgs& a, hipStream_t st) {
+// The merge of a plan's partials.  The grouped form (4 thread groups per row) where the
+// plan's units average 8 or more partials (grid_wg >= 8 units); chosen from the plan's
+// shape, never from the lengths, and never for fixed chunks, whose results must not depend
+// on the batch around a sequence.
+int32_t launch_combine(const mla::DecodeArgs& a, int grid_wg, hipStream_t st) {
   mla::CombineArgs c;
+  c.grouped = a.plan_fixed_blocks == 0 && grid_wg >= 8 * a.batch * a.row_split;
   c.meta = a.meta;
   c.ws_hi = a.ws_hi;
   c.ws_lo = a.ws_lo;
@@ -451,7 +456,7 @@ int32_t mla_decode_ex(const mla_problem_t* problem, const mla_variant_t* variant
   if (rc != MLA_OK) return rc;
   rc = launch_planned_decode(*problem, indices, block_table, cache_seqlens, a, plan->grid_wg, st);
   if (rc != MLA_OK) return rc;
-  return launch_combine(a, st);
+  return launch_combine(a, plan->grid_wg, st);
 }
 
 int32_t mla_decode_splits(const mla_problem_t* problem, const mla_variant_t* variant, const void* q,
@@ -504,7 +509,7 @@ int32_t mla_combine(const mla_problem_t* problem, const mla_variant_t* variant, 
   if (rc != MLA_OK) return rc;
   rc = attach_plan(*problem, plan, workspace, workspace_bytes, &a);
   if (rc != MLA_OK) return rc;
-  return launch_combine(a, static_cast<hipStream_t>(stream));
+  return launch_combine(a, plan->grid_wg, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -44,6 +44,7 @@ struct CombineArgs {
   float* lse;       // [B, R]
   const float* sinks;  // attention-sink logits [heads], or nullptr
   int batch, rows, rows_per_wg, row_split, heads;
+  int grouped;         // 1: the grouped form (units of 8 or more partials)
 };
 
 // Sparse lists -> pool rows (one workgroup per (b, t) unit).
