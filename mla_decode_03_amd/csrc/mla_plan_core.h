@@ -57,6 +57,17 @@ __device__ inline int64_t floor_div(int64_t n, int64_t d) {
   return q;
 }
 
+// floor(n / d) of wave-uniform operands, divided by the vector unit: for uniform values the
+// compiler divides on the scalar unit, whose sequence takes several times the cycles (one
+// scalar unit serves the workgroup's four waves).  Operands of 2^31 or more go through
+// floor_div.
+__device__ inline int64_t floor_div_uniform(int64_t n, int64_t d) {
+  if (((n | d) >> 31) != 0) return floor_div(n, d);
+  uint32_t nv = (uint32_t)n, dv = (uint32_t)d;
+  asm volatile("" : "+v"(nv), "+v"(dv));
+  return (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(nv / dv));
+}
+
 // Workgroup holding global block position x (0 <= x < total): the largest w < num_wg
 // with floor(w*total/num_wg) <= x.
 __device__ inline int32_t wg_of(int64_t x, int64_t total, int64_t num_wg) {
@@ -502,14 +513,18 @@ __device__ inline bool plan_share_wave(const PlanParams& p, MetaView v, bool wri
   const int32_t ne_carry = __builtin_amdgcn_readlane(wave_inclusive_sum(n > 0 ? 1 : 0), 63);
   const int32_t nbm = wave_max_nonneg(n);   // the largest sequence
   int32_t num_wg = 0;
-  if (total > 0) num_wg = max(1, min(p.grid_wg, (int32_t)floor_div((int64_t)total + p.min_blocks - 1, p.min_blocks)));
+  if (total > 0)
+    num_wg = max(1, min(p.grid_wg, (int32_t)floor_div_uniform((int64_t)total + p.min_blocks - 1, p.min_blocks)));
   if (p.split_rule == kRuleAuto && num_wg > 0) {   // must be the even case plan_core skips
-    const int64_t share = floor_div(total, num_wg);
+    const int64_t share = floor_div_uniform(total, num_wg);
     const bool even = (int64_t)total == (int64_t)nbm * ne_carry && share * num_wg == total && nbm > 0 &&
-                      (share == floor_div(share, nbm) * nbm || nbm == floor_div(nbm, share) * share);
+                      (share == floor_div_uniform(share, nbm) * nbm || nbm == floor_div_uniform(nbm, share) * share);
     if (!even) return false;
   }
   auto cut = [&](int64_t w) -> int64_t { return (w <= num_wg && num_wg > 0) ? floor_div(w * total, num_wg) : total; };
+  auto cut_uniform = [&](int64_t w) -> int64_t {   // (w uniform)
+    return (w <= num_wg && num_wg > 0) ? floor_div_uniform(w * total, num_wg) : total;
+  };
   auto holder = [&](int64_t q) -> int32_t { return wg_of(q, total, num_wg); };
   // lane u's unit: its workgroups and partial slots
   int32_t ns = 0, first = -1;
@@ -522,7 +537,7 @@ __device__ inline bool plan_share_wave(const PlanParams& p, MetaView v, bool wri
   const bool refuse = num_partials > p.max_partials;
   const bool any_err = __builtin_amdgcn_ballot_w64(err != 0) != 0 || num_partials > p.max_partials;
   // my range and the sequences of its two ends
-  const int64_t pos = my_wg < num_wg ? cut(my_wg) : total, end = my_wg < num_wg ? cut(my_wg + 1) : total;
+  const int64_t pos = my_wg < num_wg ? cut_uniform(my_wg) : total, end = my_wg < num_wg ? cut_uniform(my_wg + 1) : total;
   int uf = -1, ul = -1;
   if (pos < end) {
     uf = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < B && excl <= pos)) - 1;
@@ -670,7 +685,8 @@ __device__ inline bool plan_share_tables(const PlanParams& p, MetaView v, bool w
 
   // 2. the workgroups, the cost axis, which rules to form; every check before any table write
   int32_t num_wg = 0;
-  if (total > 0) num_wg = max(1, min(p.grid_wg, (int32_t)floor_div((int64_t)total + p.min_blocks - 1, p.min_blocks)));
+  if (total > 0)
+    num_wg = max(1, min(p.grid_wg, (int32_t)floor_div_uniform((int64_t)total + p.min_blocks - 1, p.min_blocks)));
   const int32_t c = p.seg_cost;
   const int64_t ctot64 = 4 * (int64_t)total + (int64_t)c * ne;   // length of the cost axis
   if (num_wg > kPlanLdsWg || ctot64 * num_wg >= ((int64_t)1 << 31) || c < 0) return false;
@@ -678,16 +694,16 @@ __device__ inline bool plan_share_tables(const PlanParams& p, MetaView v, bool w
   const uint32_t T = (uint32_t)total, C = (uint32_t)ctot64, W = (uint32_t)num_wg, uc = (uint32_t)c;
   bool evaluate = p.split_rule == kRuleAuto && num_wg > 0;
   if (evaluate) {   // the even case plan_core keeps without evaluating
-    const uint32_t share = T / W;
+    const int64_t share = floor_div_uniform(T, W);
     if (T == (uint32_t)nbm * (uint32_t)ne && share * W == T && nbm > 0 &&
-        (share % (uint32_t)nbm == 0 || (uint32_t)nbm % share == 0))
+        (share == floor_div_uniform(share, nbm) * nbm || nbm == floor_div_uniform(nbm, share) * share))
       evaluate = false;
   }
   const bool need_p = num_wg > 0 && p.split_rule != kRuleCost;
   const bool need_c = num_wg > 0 && (p.split_rule == kRuleCost || evaluate);
   // cuts inside one sequence of nb blocks: at most ceil(nb W / T), or ceil((c + 4 nb) W / C)
-  if (need_p && ((uint32_t)nbm * W + T - 1) / T > (uint32_t)kTablesMaxCuts) return false;
-  if (need_c && ((uc + 4 * (uint32_t)nbm) * W + C - 1) / C > (uint32_t)kTablesMaxCuts) return false;
+  if (need_p && floor_div_uniform((uint32_t)nbm * W + T - 1, T) > kTablesMaxCuts) return false;
+  if (need_c && floor_div_uniform((uc + 4 * (uint32_t)nbm) * W + C - 1, C) > kTablesMaxCuts) return false;
 
   // 3. the cuts landing in sequence t, with their owner word: sequence (bits 0-11), rank
   // (12-23), cut on the owner's first block (24) (one barrier)
