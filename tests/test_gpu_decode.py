@@ -123,6 +123,24 @@ def test_split_counts_agree():
         assert np.linalg.norm(o - o0) / np.linalg.norm(o0) < 5e-3
 
 
+@pytest.mark.parametrize("H,nwg,with_sinks", [(128, 8, False), (33, 12, True), (16, 40, False)])
+def test_grouped_merge(H, nwg, with_sinks):
+    """Plans that average 8 or more partials per unit take the grouped merge (4 thread
+    groups per row, then one LDS exchange): 8 partials (each group's 2 in one batch), 12
+    (groups of 3 in batches of 4, one split read again with no weight), 40 with 16 heads
+    (several batches); 33 heads leave the last workgroup's second row empty; with sinks
+    too.  Every row meets the oracle."""
+    import mla_decode_03_amd as mla
+    from mla_inputs import make_sinks
+    case = _case(1, 1, H, [3000], seed=80 + nwg)
+    sinks = make_sinks(H, seed=6) if with_sinks else None
+    say("grouped merge", H, nwg, with_sinks)
+    ref_o, ref_l = oracle_rows(case, sinks=sinks)
+    o, l, dec = run(case, options=mla.PlanOptions(num_workgroups=nwg, min_blocks_per_wg=1), sinks=sinks)
+    assert dec.plan.grid_wg == nwg
+    compare(o, l, ref_o, ref_l, "grouped merge H=%d nwg=%d" % (H, nwg))
+
+
 def _scale_blocks(case, factor, rope_only):
     """Multiply block j of every sequence by factor(j): its rope dims only, or whole rows
     (keys and values alike), re-rounded to bf16."""
