@@ -308,10 +308,10 @@ def test_plan_in_decode_matches_planner(kind):
     lengths it is given.  Its outputs equal the planner-kernel path's bit for bit, the
     metadata it leaves for the combine equals the CPU mirror's words, and a later step
     with other lengths (same plan object) equals a fresh plan for those lengths.  The kinds
-    reach each form of the in-launch planning: registers only (even), per-wave cut tables
-    (ragged batches up to 256 sequences: auto, pages, cost, h16, wide) and the block-wide
-    computation (row split, fixed chunks, 300 sequences, and few_cost, whose sequences each
-    hold more cuts than the per-wave tables take)."""
+    reach each form of the in-launch planning: registers only (even), the cut tables
+    (ragged batches up to 256 sequences: auto, pages, cost, h16, wide) and the general
+    block-wide computation (row split, fixed chunks, 300 sequences, and few_cost, whose
+    sequences could each hold more cuts than the tables take)."""
     import torch
     import mla_decode_03_amd as mla
     from mla_inputs import make_topk_indices
