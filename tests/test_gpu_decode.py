@@ -302,14 +302,15 @@ def test_device_plan_matches_mirror():
 
 
 @pytest.mark.parametrize("kind", ["auto", "pages", "cost", "row_split2", "fixed", "h16", "sparse", "even",
-                                  "wide", "b300", "few_cost"])
+                                  "wide", "wide512", "b300", "few_cost"])
 def test_plan_in_decode_matches_planner(kind):
     """A plan made with plan_in_decode = 1 and reused: every decode launch re-plans from the
     lengths it is given.  Its outputs equal the planner-kernel path's bit for bit, the
     metadata it leaves for the combine equals the CPU mirror's words, and a later step
     with other lengths (same plan object) equals a fresh plan for those lengths.  The kinds
     reach each form of the in-launch planning: registers only (even), the cut tables
-    (ragged batches up to 256 sequences: auto, pages, cost, h16, wide) and the general
+    (ragged batches up to 256 sequences: auto, pages, cost, h16, wide, and wide512, whose
+    512 workgroups take each thread's pricing loop twice) and the general
     block-wide computation (row split, fixed chunks, 300 sequences, and few_cost, whose
     sequences could each hold more cuts than the tables take)."""
     import torch
@@ -322,8 +323,8 @@ def test_plan_in_decode_matches_planner(kind):
     lens[3] = 0
     if kind == "even":       # every sequence 16 blocks, shares of 4 blocks: the equal-share cut
         lens = [1000] * 40
-    elif kind in ("wide", "b300"):
-        lens = [int(x) for x in rng.integers(0, 1200, size=200 if kind == "wide" else 300)]
+    elif kind in ("wide", "wide512", "b300"):
+        lens = [int(x) for x in rng.integers(0, 1200, size=300 if kind == "b300" else 200)]
         lens[5] = lens[77] = 0
     elif kind == "few_cost":  # three sequences of up to 313 blocks over 512 workgroups
         lens = [20000, 7, 19000]
@@ -334,6 +335,7 @@ def test_plan_in_decode_matches_planner(kind):
     base.update({"auto": {}, "pages": dict(split_rule=1), "cost": dict(split_rule=2), "row_split2": dict(row_split=2),
                  "fixed": dict(fixed_split_blocks=5), "h16": {}, "sparse": {}, "even": {},
                  "wide": dict(num_workgroups=256), "b300": dict(num_workgroups=256),
+                 "wide512": dict(num_workgroups=512, min_blocks_per_wg=1),
                  "few_cost": dict(num_workgroups=512, min_blocks_per_wg=1, split_rule=2)}[kind])
     topk, ix = 0, None
     if kind == "sparse":
