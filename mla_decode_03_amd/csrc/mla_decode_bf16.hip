@@ -757,7 +757,7 @@ __device__ __forceinline__ void decode_segment_wide(const DecodeArgs& a, MLA_LDS
     if (row0 + rr >= row_end) break;              // uniform
     const u32x4 v = *(const MLA_LDS u32x4*)(ob + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
     uint16_t* dst = part ? a.ws_hi + (prow + rr) * kDv : a.out + ((size_t)b * R + row0 + rr) * kDv;
-    *(u32x4*)(dst + 8 * l_e) = v;
+    __builtin_nontemporal_store(v, (u32x4*)(dst + 8 * l_e));   // streamed: this launch never reads it
   }
   if (tid_e < 128 && row0 + tid_e < row_end) {
     const int rr = tid_e;
@@ -1343,7 +1343,7 @@ __device__ __forceinline__ void decode_segment_cols(const DecodeArgs& a, MLA_LDS
     if (row0 + rr >= row_end) break;                  // uniform
     const u32x4 v = *(const MLA_LDS u32x4*)(lds + rr * 1024 + ((l_e ^ (rr & 15)) << 4));
     uint16_t* dst = part ? a.ws_hi + (prow + rr) * kDv : a.out + ((size_t)b * R + row0 + rr) * kDv;
-    *(u32x4*)(dst + 8 * l_e) = v;
+    __builtin_nontemporal_store(v, (u32x4*)(dst + 8 * l_e));   // streamed: this launch never reads it
   }
   if (tid_e < 128 && row0 + tid_e < row_end) {
     const int rr = tid_e;
