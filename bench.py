@@ -322,10 +322,14 @@ def main():
     frac_mfma = tflops / MFMA_BF16_PEAK_TFLOPS
 
     roofline = None
+    # The committed counter profiles were taken on the plain decode with the default plan;
+    # any other launch (a variant or a plan override) has no traffic figure.
+    profiled = not (args.sinks or args.sparse_topk or args.num_workgroups or args.min_blocks or args.row_split
+                    or args.fixed_split_blocks or args.planner_kernel)
     if kernel_ms is not None:
         achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(CONFIGS[args.config]["name"]),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(CONFIGS[args.config]["name"]) if profiled else None,
                     "kernel": DECODE_KERNEL if split else "mla_decode_f32_kernel", "kernel_ms": round(kernel_ms, 5),
                     "algorithmic_bytes_per_launch": total_bytes}
 

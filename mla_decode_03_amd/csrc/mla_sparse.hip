@@ -25,6 +25,8 @@ __global__ __launch_bounds__(256) void mla_sparse_rows_kernel(SparseArgs a) {
   const int32_t* list = a.indices + (size_t)u * a.topk;
   int32_t* rows = a.rows + (size_t)u * a.row_stride;
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  // 16-byte accesses where both lists and both row arrays are 16-byte aligned
+  const bool vec = ((reinterpret_cast<uintptr_t>(list) | reinterpret_cast<uintptr_t>(rows)) & 15) == 0;
   // 8 consecutive entries per thread and round, every load of a round in flight at once
   // (index, then its block-table entry), then one scan of the per-thread counts keeps
   // the list order.
@@ -32,10 +34,14 @@ __global__ __launch_bounds__(256) void mla_sparse_rows_kernel(SparseArgs a) {
   int32_t carry = 0;
   for (int base = 0; base < a.topk; base += 256 * kPer) {
     int32_t p[kPer], row[kPer];
+    const int k0 = base + kPer * t;
+    if (vec && k0 + kPer <= a.topk) {   // two 16-byte loads; a wave reads 2 KB in a row
+      const int4 v0 = *(const int4*)(list + k0), v1 = *(const int4*)(list + k0 + 4);
+      p[0] = v0.x; p[1] = v0.y; p[2] = v0.z; p[3] = v0.w;
+      p[4] = v1.x; p[5] = v1.y; p[6] = v1.z; p[7] = v1.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int k = base + kPer * t + e;
-      p[e] = (k < a.topk) ? list[k] : -1;
+      for (int e = 0; e < kPer; ++e) p[e] = (k0 + e < a.topk) ? list[k0 + e] : -1;
     }
     int32_t cnt = 0;
 #pragma unroll
@@ -53,9 +59,14 @@ __global__ __launch_bounds__(256) void mla_sparse_rows_kernel(SparseArgs a) {
     }
     int32_t tot;
     int32_t pos = carry + block_exclusive_scan(cnt, s_scan, &tot);
+    if (vec && cnt == kPer && (pos & 3) == 0) {   // a full run of kept entries, aligned
+      *(int4*)(rows + pos) = int4{row[0], row[1], row[2], row[3]};
+      *(int4*)(rows + pos + 4) = int4{row[4], row[5], row[6], row[7]};
+    } else {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (p[e] != -1) rows[pos++] = row[e];
+      for (int e = 0; e < kPer; ++e)
+        if (p[e] != -1) rows[pos++] = row[e];
+    }
     carry += tot;
   }
   for (int k = carry + t; k < a.row_stride; k += 256) rows[k] = 0;   // whole blocks
